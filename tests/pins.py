@@ -1,0 +1,309 @@
+"""Pins of the oracle: each raises AssertionError when the oracle disagrees with something
+other than itself (a textbook formula written with loops, a closed form, a library routine,
+a hand-worked example or an invariant the mathematics fixes).
+
+They take no arguments and call the oracle through its modules' attributes, so that
+``test_oracle_mutants`` can plant a mistake in the oracle and check that some pin catches it.
+"""
+
+import math
+
+import numpy as np
+import scipy.special
+
+import brute
+import oracle.compact as OC
+import oracle.sals as OS
+
+TOL = 1e-11
+
+
+def _rand(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _orthogonal(seed, n, m=None):
+    m = n if m is None else m
+    q, r = np.linalg.qr(_rand(seed, n, m))
+    return q * np.sign(np.diag(r))[None, :]
+
+
+def _run_decode(q, Lk, Lv, Pk, Pv, T, k, w, G, H_kv, base=10000.0):
+    return OS.decode_step(q[None], Lk[None], Lv[None], Pk, Pv, ctx=T, k=k, w=w, G=G, H_kv=H_kv,
+                          base=base, dtype="f64")
+
+
+# ---------------------------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------------------------
+
+def pin_rope_d2_closed_form():
+    """d = 2: theta_0 = 1, so RoPE([1, 0], p) = [cos p, sin p] and RoPE([0, 1], p) = [-sin p, cos p]."""
+    for p in [0, 1, 2, 7, 1000, 131071]:
+        a = OS.rope(np.array([[1.0, 0.0]]), p, 10000.0)[0]
+        b = OS.rope(np.array([[0.0, 1.0]]), p, 10000.0)[0]
+        assert np.allclose(a, [math.cos(p), math.sin(p)], atol=1e-12, rtol=0), (p, a)
+        assert np.allclose(b, [-math.sin(p), math.cos(p)], atol=1e-12, rtol=0), (p, b)
+
+
+def pin_rope_complex_form():
+    """Agrees with (x_i + i x_{i+d/2}) e^{i p theta_i}, theta_i = base^(-2i/d)."""
+    for d, base in [(8, 10000.0), (16, 500000.0), (64, 10000.0)]:
+        x = _rand(d, 5, d)
+        pos = [0, 3, 511, 4095, 131071]
+        got = OS.rope(x, pos, base)
+        for j in range(5):
+            ref = brute.rope_complex(list(x[j]), pos[j], base)
+            assert np.allclose(got[j], ref, atol=1e-9, rtol=0), (d, pos[j])
+
+
+def pin_rope_invariants():
+    """Norm preserved; position 0 is the identity; q.k depends only on the position difference."""
+    d = 16
+    x = _rand(1, 4, d)
+    y = OS.rope(x, [5, 17, 1000, 99999], 10000.0)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), atol=1e-12)
+    assert np.array_equal(OS.rope(x, 0, 10000.0), x)
+    q, k = _rand(2, d), _rand(3, d)
+    for (a, b, c) in [(10, 3, 100), (4095, 0, 12345), (7, 7, 1)]:
+        l1 = OS.rope(q[None], a, 10000.0)[0] @ OS.rope(k[None], b, 10000.0)[0]
+        l2 = OS.rope(q[None], a + c, 10000.0)[0] @ OS.rope(k[None], b + c, 10000.0)[0]
+        assert abs(l1 - l2) < 1e-9, (a, b, c)
+
+
+# ---------------------------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------------------------
+
+def pin_select_hand_examples():
+    """Hand-worked: candidates [0.5, 2.0, -1.0, 2.0, 0.3, 2.0, 1.5, 0.0], T=10, w=2, k=2:
+    three 2.0 ties -> the lowest two indices 1, 3; window 8, 9."""
+    S = np.array([0.5, 2.0, -1.0, 2.0, 0.3, 2.0, 1.5, 0.0])
+    assert list(OS.select_tokens(S, 10, 2, 2)) == [1, 3, 8, 9]
+    assert list(OS.select_tokens(S, 10, 4, 2)) == [1, 3, 5, 6, 8, 9]
+    assert list(OS.select_tokens(np.array([0.0, -0.0]), 2, 1, 0)) == [0]
+    assert list(OS.select_tokens(np.array([-0.0, 0.0]), 2, 1, 0)) == [0]
+    assert list(OS.select_tokens(np.array([-0.0, 0.0, 1e-300]), 3, 1, 0)) == [2]
+    # k = 0: window only; w >= T: everything; k + w >= T: everything
+    assert list(OS.select_tokens(S, 10, 0, 2)) == [8, 9]
+    assert list(OS.select_tokens(S[:0], 5, 3, 7)) == [0, 1, 2, 3, 4]
+    assert list(OS.select_tokens(S, 10, 8, 2)) == list(range(10))
+    assert list(OS.select_tokens(S, 10, 100, 2)) == list(range(10))
+
+
+def pin_select_bruteforce():
+    """Against Python's sorted() on (-score, index) keys, with heavy ties and signed zeros."""
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        n = int(rng.integers(1, 40))
+        vals = rng.integers(-3, 4, size=n).astype(np.float64)
+        vals[rng.random(n) < 0.2] = -0.0
+        T = n + int(rng.integers(0, 6))
+        w = T - n
+        k = int(rng.integers(0, n + 3))
+        S = np.concatenate([vals, np.zeros(w)])
+        got = list(OS.select_tokens(S, T, k, w))
+        assert got == brute.select(list(S), T, k, w), (trial, vals, k, w)
+
+
+# ---------------------------------------------------------------------------------------------
+# projection
+# ---------------------------------------------------------------------------------------------
+
+def pin_project_identity_orthogonal():
+    X = _rand(11, 3, 5, 12)
+    assert np.array_equal(OS.project_kv(X, np.eye(12)), X)
+    P = _orthogonal(12, 12)
+    assert np.allclose(OS.project_kv(X, P) @ P.T, X, atol=1e-12)
+    Pr = _orthogonal(13, 12, 4)  # orthonormal columns: projecting rows already in span(P) is lossless
+    Y = _rand(14, 6, 4)
+    assert np.allclose(OS.project_kv(Y @ Pr.T, Pr), Y, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# decode: scores, selection and attention against dense RoPE attention
+# ---------------------------------------------------------------------------------------------
+
+SHAPES = [  # (H_q, H_kv, G, d)
+    (2, 2, 1, 8),
+    (4, 2, 2, 8),
+    (4, 4, 2, 4),
+    (6, 3, 3, 4),
+    (4, 1, 1, 8),
+]
+
+
+def pin_decode_dense_special_case():
+    """P = I (r = H_kv*d) and k + w >= T: SALS equals dense RoPE attention over the whole cache."""
+    for i, (H_q, H_kv, G, d) in enumerate(SHAPES):
+        D = H_kv * d
+        for T, k, w in [(1, 0, 1), (9, 4, 5), (20, 15, 5), (24, 30, 0), (17, 0, 17)]:
+            rs = np.random.default_rng(100 + i * 10 + T)
+            K = rs.standard_normal((T, D))
+            V = rs.standard_normal((T, D))
+            q = rs.standard_normal((H_q, d))
+            res = _run_decode(q, K, V, np.eye(D), np.eye(D), T, k, w, G, H_kv)
+            ref = brute.dense_rope_attention(q.tolist(), K.tolist(), V.tolist(), range(T), T,
+                                             10000.0, H_q, H_kv, d)
+            assert np.allclose(res["out"][0], ref, atol=TOL, rtol=0), (H_q, H_kv, G, d, T, k, w)
+            assert all(list(res["sel"][0, s]) == list(range(T)) for s in range(G))
+
+
+def _selection_case(seed, H_q, H_kv, G, d, T, lowrank):
+    D = H_kv * d
+    rs = np.random.default_rng(seed)
+    if lowrank:  # rows in span(P) with orthonormal columns: the latent is lossless
+        r = max(2, D // 2)
+        P = _orthogonal(seed + 1, D, r)
+        Yk, Yv = rs.standard_normal((T, r)), rs.standard_normal((T, r))
+        Kpre, Vpre, Lk, Lv = Yk @ P.T, Yv @ P.T, Yk, Yv
+    else:  # square orthogonal P
+        P = _orthogonal(seed + 1, D)
+        Kpre, Vpre = rs.standard_normal((T, D)), rs.standard_normal((T, D))
+        Lk, Lv = Kpre @ P, Vpre @ P
+    q = rs.standard_normal((H_q, d))
+    return q, Kpre, Vpre, Lk, Lv, P
+
+
+def pin_decode_selected_matches_masked_dense():
+    """With a lossless projection, the latent score of group s at t is the RoPE-free logit sum
+    over its heads; the selected set is its top-k (ties low) plus the window; and the output is
+    dense RoPE attention restricted to that set."""
+    for i, (H_q, H_kv, G, d) in enumerate(SHAPES):
+        for lowrank in (False, True):
+            for T, k, w in [(30, 6, 4), (41, 10, 7), (25, 1, 0), (12, 0, 3)]:
+                q, Kpre, Vpre, Lk, Lv, P = _selection_case(500 + 7 * i + T, H_q, H_kv, G, d, T, lowrank)
+                res = _run_decode(q, Lk, Lv, P, P, T, k, w, G, H_kv)
+                T_c = max(0, T - w)
+                Sb = brute.ropefree_group_scores(q.tolist(), Kpre.tolist(), T_c, H_q, H_kv, G, d)
+                assert np.allclose(res["S"][0], np.array(Sb).reshape(G, T_c), atol=1e-10, rtol=0)
+                for s in range(G):
+                    assert list(res["sel"][0, s]) == brute.select(Sb[s], T, k, w), (i, lowrank, T, s)
+                for h in range(H_q):
+                    s = brute.grp_of(brute.kv_of(h, H_q, H_kv), H_kv, G)
+                    pos = brute.select(Sb[s], T, k, w)
+                    ref = brute.dense_rope_attention(q.tolist(), Kpre.tolist(), Vpre.tolist(), pos, T,
+                                                     10000.0, H_q, H_kv, d)
+                    assert np.allclose(res["out"][0, h], ref[h], atol=1e-10, rtol=0), (i, lowrank, T, h)
+
+
+def pin_decode_uniform_and_single():
+    """q = 0: every score and logit is 0, so the top-k is the lowest k' positions and the output
+    is the plain mean of the rebuilt value rows over the selected set. ctx = 1: the output is
+    the single rebuilt value row."""
+    H_q, H_kv, G, d = 4, 2, 1, 8
+    D = H_kv * d
+    T, k, w = 20, 5, 3
+    rs = np.random.default_rng(3)
+    Lk, Lv = rs.standard_normal((T, 6)), rs.standard_normal((T, 6))
+    Pk, Pv = rs.standard_normal((D, 6)), rs.standard_normal((D, 6))
+    res = _run_decode(np.zeros((H_q, d)), Lk, Lv, Pk, Pv, T, k, w, G, H_kv)
+    sel = list(range(5)) + [17, 18, 19]
+    assert list(res["sel"][0, 0]) == sel
+    for h in range(H_q):
+        g = brute.kv_of(h, H_q, H_kv)
+        Vh = np.array([[sum(Lv[t, j] * Pv[g * d + c, j] for j in range(6)) for c in range(d)] for t in sel])
+        assert np.allclose(res["out"][0, h], Vh.mean(axis=0), atol=1e-12, rtol=0)
+    res1 = _run_decode(rs.standard_normal((H_q, d)), Lk[:1], Lv[:1], Pk, Pv, 1, 4, 2, G, H_kv)
+    for h in range(H_q):
+        g = brute.kv_of(h, H_q, H_kv)
+        assert np.allclose(res1["out"][0, h], Pv[g * d:(g + 1) * d] @ Lv[0], atol=1e-12, rtol=0)
+
+
+def pin_decode_softmax_and_permutation():
+    """Attention weights sum to 1; permuting the latent rows among unselected candidate positions
+    changes neither the selected set nor the output (scores are position-free)."""
+    H_q, H_kv, G, d = 4, 2, 2, 8
+    D, r, T, k, w = H_kv * d, 6, 40, 8, 4
+    rs = np.random.default_rng(21)
+    Lk, Lv = rs.standard_normal((T, r)), rs.standard_normal((T, r))
+    Pk, Pv = rs.standard_normal((D, r)), rs.standard_normal((D, r))
+    q = rs.standard_normal((H_q, d))
+    res = _run_decode(q, Lk, Lv, Pk, Pv, T, k, w, G, H_kv)
+    sets = [res["sel"][0, s] for s in range(G)]
+    _, weights = OS.attend_selected(q, Lk, Lv, Pk, Pv, sets, T, 10000.0, H_kv, G)
+    for pi in weights:
+        assert abs(pi.sum() - 1.0) < 1e-14 and (pi >= 0).all()
+    chosen = set(np.concatenate(sets).tolist())
+    free = [t for t in range(T - w) if t not in chosen]
+    perm = np.array(free)[rs.permutation(len(free))]
+    idx = np.arange(T)
+    idx[free] = perm
+    res2 = _run_decode(q, Lk[idx], Lv[idx], Pk, Pv, T, k, w, G, H_kv)
+    assert np.array_equal(res2["sel"], res["sel"])
+    assert np.array_equal(res2["out"], res["out"])
+
+
+# ---------------------------------------------------------------------------------------------
+# compaction
+# ---------------------------------------------------------------------------------------------
+
+def pin_importance_bruteforce_and_mass():
+    """Causal importance against explicit loops; it is non-negative and sums to w per query head."""
+    rs = np.random.default_rng(31)
+    for T, w, d in [(1, 1, 4), (9, 3, 4), (23, 8, 8), (16, 16, 2)]:
+        Q, K = rs.standard_normal((w, d)), rs.standard_normal((T, d))
+        I = OC.importance(Q, K, T)
+        assert np.allclose(I, brute.causal_importance(Q.tolist(), K.tolist(), T), atol=1e-13, rtol=0)
+        assert (I >= 0).all() and abs(I.sum() - w) < 1e-12
+
+
+def pin_importance_closed_forms():
+    """Zero queries: every allowed key gets 1/(p_i+1), so I[t] = sum_{i: p_i >= t} 1/(p_i + 1).
+    One query (w = 1) at T-1 sees every key: I equals scipy's softmax of K q / sqrt(d)."""
+    T, w, d = 12, 5, 4
+    I = OC.importance(np.zeros((w, d)), np.random.default_rng(0).standard_normal((T, d)), T)
+    ref = [sum(1.0 / (p + 1) for p in range(T - w, T) if p >= t) for t in range(T)]
+    assert np.allclose(I, ref, atol=1e-14, rtol=0)
+    rs = np.random.default_rng(1)
+    K, q = rs.standard_normal((T, d)), rs.standard_normal((1, d))
+    assert np.allclose(OC.importance(q, K, T), scipy.special.softmax(K @ q[0] / math.sqrt(d)), atol=1e-14)
+
+
+def pin_compact_identity_and_masked():
+    """k_keep = T keeps every row unchanged; a dense decode over the compact cache equals
+    masked attention over the full cache with the evicted positions at -inf; the dense decode
+    itself equals scipy's softmax times V."""
+    rs = np.random.default_rng(41)
+    B, H_q, H_kv, T, w, d = 2, 4, 2, 14, 3, 4
+    K, V = rs.standard_normal((B, H_kv, T, d)), rs.standard_normal((B, H_kv, T, d))
+    Q = rs.standard_normal((B, H_q, w, d))
+    full = OC.kv_compact(K, V, Q, ctx=T, k_keep=T, H_kv=H_kv, dtype="f64")
+    assert np.array_equal(full["Kc"], K) and np.array_equal(full["Vc"], V)
+    assert (full["kept"] == np.arange(T)).all()
+    # importance per KV head sums over its query heads: total mass w * (H_q / H_kv)
+    assert np.allclose(full["importance"].sum(axis=-1), w * H_q / H_kv, atol=1e-12)
+    c = OC.kv_compact(K, V, Q, ctx=T, k_keep=5, H_kv=H_kv, dtype="f64")
+    q = rs.standard_normal((B, H_q, d))
+    out = OC.dense_decode(q, c["Kc"], c["Vc"], n=5, H_kv=H_kv, dtype="f64")
+    for b in range(B):
+        for h in range(H_q):
+            g = brute.kv_of(h, H_q, H_kv)
+            keep = set(c["kept"][b, g].tolist())
+            ref = brute.masked_attention(q[b, h].tolist(), K[b, g].tolist(), V[b, g].tolist(), keep)
+            assert np.allclose(out[b, h], ref, atol=1e-12, rtol=0)
+            lib = scipy.special.softmax(K[b, g] @ q[b, h] / math.sqrt(d)) @ V[b, g]
+            assert np.allclose(OC.dense_decode(q, K, V, n=T, H_kv=H_kv, dtype="f64")[b, h], lib, atol=1e-12)
+            # the kept set is the top-5 of the importance (ties low), ascending
+            Ib = c["importance"][b, g]
+            assert sorted(c["kept"][b, g].tolist()) == sorted(sorted(range(T), key=lambda t: (-Ib[t], t))[:5])
+            ref_I = np.sum([brute.causal_importance(Q[b, hh].tolist(), K[b, g].tolist(), T)
+                            for hh in range(H_q) if brute.kv_of(hh, H_q, H_kv) == g], axis=0)
+            assert np.allclose(Ib, ref_I, atol=1e-12)
+
+
+PINS = [
+    pin_rope_d2_closed_form,
+    pin_rope_complex_form,
+    pin_rope_invariants,
+    pin_select_hand_examples,
+    pin_select_bruteforce,
+    pin_project_identity_orthogonal,
+    pin_decode_dense_special_case,
+    pin_decode_selected_matches_masked_dense,
+    pin_decode_uniform_and_single,
+    pin_decode_softmax_and_permutation,
+    pin_importance_bruteforce_and_mass,
+    pin_importance_closed_forms,
+    pin_compact_identity_and_masked,
+]

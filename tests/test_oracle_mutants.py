@@ -1,0 +1,101 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that some pin fails.
+
+Each mutant rewrites one snippet of an oracle source file, loads the result as a fresh module
+and swaps its functions into ``oracle.sals`` / ``oracle.compact`` for the duration of one test.
+A pin "catches" a mutant when it raises (an AssertionError, or any error the mistake causes).
+"""
+
+import os
+import types
+
+import pytest
+
+import oracle.compact as OC
+import oracle.sals as OS
+from pins import PINS
+
+ORACLE_DIR = os.path.dirname(OS.__file__)
+
+MUTANTS = [
+    # (file, original snippet, mutated snippet, what the mistake is)
+    ("sals.py", "return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=1)",
+     "return np.concatenate([x1 * c + x2 * s, x2 * c - x1 * s], axis=1)", "RoPE rotates the wrong way"),
+    ("sals.py", "** (-(2.0 * i) / d)", "** (-(1.0 * i) / d)", "RoPE frequency exponent"),
+    ("sals.py", "x1, x2 = x[:, :half], x[:, half:]", "x1, x2 = x[:, 0::2], x[:, 1::2]",
+     "RoPE pairs interleaved instead of halves"),
+    ("sals.py", "return (h * H_kv) // H_q", "return h % H_kv", "query-head to KV-head map"),
+    ("sals.py", "return (g * G) // H_kv", "return g % G", "KV-head to group map"),
+    ("sals.py", "qt[s] += q[h] @ Pk[g * d:(g + 1) * d, :]",
+     "qt[s] += q[h] @ Pk[((g + 1) % H_kv) * d:((g + 1) % H_kv + 1) * d, :]", "latent query uses another head's P"),
+    ("sals.py", "order = np.lexsort((np.arange(n), -np.asarray(", "order = np.lexsort((-np.arange(n), -np.asarray(",
+     "ties go to the highest index"),
+    ("sals.py", "top = topk_lowest_index(S_row[:T_c], min(k, T_c))",
+     "top = topk_lowest_index(S_row[:T_c], min(k + 1, T_c))", "one token too many"),
+    ("sals.py", "top = topk_lowest_index(S_row[:T_c], min(k, T_c))",
+     "top = topk_lowest_index(S_row[:T], min(k, T))[:min(k, T_c)]", "top-k also ranks window positions"),
+    ("sals.py", "pi = _softmax(Kh @ qh / np.sqrt(d))", "pi = _softmax(Kh @ qh)", "attention scale dropped"),
+    ("sals.py", "qh = rope(q[h][None, :], T - 1, base)[0]", "qh = rope(q[h][None, :], T, base)[0]",
+     "query rotated at T instead of T-1"),
+    ("sals.py", "Kh = rope(reconstruct(Lk[idx], Pk[g * d:(g + 1) * d]), idx, base)",
+     "Kh = rope(reconstruct(Lk[idx], Pk[g * d:(g + 1) * d]), np.arange(len(idx)), base)",
+     "keys rotated at their slot, not their position"),
+    ("sals.py", "Kh = rope(reconstruct(Lk[idx], Pk[g * d:(g + 1) * d]), idx, base)",
+     "Kh = reconstruct(Lk[idx], Pk[g * d:(g + 1) * d])", "keys not rotated"),
+    ("sals.py", "Vh = reconstruct(Lv[idx], Pv[g * d:(g + 1) * d])",
+     "Vh = reconstruct(Lv[idx], Pk[g * d:(g + 1) * d])", "values rebuilt with P_k"),
+    ("sals.py", "return np.asarray(X, dtype=np.float64) @ np.asarray(P, dtype=np.float64)",
+     "return np.asarray(X, dtype=np.float64) @ np.asarray(P, dtype=np.float64).T", "projection transposed"),
+    ("sals.py", "    e = np.exp(logits - m)\n    return e / e.sum()", "    e = np.exp(logits - m)\n    return e",
+     "softmax not normalised"),
+    ("compact.py", "a = _softmax(K[: p + 1] @ Qobs[i] / np.sqrt(d))\n        I[: p + 1] += a",
+     "a = _softmax(K[:T] @ Qobs[i] / np.sqrt(d))\n        I[:T] += a", "causal mask dropped"),
+    ("compact.py", "p = T - w + i", "p = T - w + i + 1 if i < w - 1 else T - 1", "observation positions shifted"),
+    ("compact.py", "a = _softmax(K[: p + 1] @ Qobs[i] / np.sqrt(d))", "a = _softmax(K[: p + 1] @ Qobs[i])",
+     "importance scale dropped"),
+    ("compact.py", "out[b, h] = _softmax(Kf @ qf[b, h] / np.sqrt(d)) @ Vf", "out[b, h] = _softmax(Kf @ qf[b, h]) @ Vf",
+     "dense decode scale dropped"),
+    ("compact.py", "if kv_head_of(h, H_q, H_kv) == g:", "if h == g:", "importance ignores grouped heads"),
+    ("compact.py", "Vc[b, g] = V[b, g, kept[b, g]]", "Vc[b, g] = K[b, g, kept[b, g]]", "values gathered from K"),
+    ("compact.py", "    e = np.exp(logits - m)\n    return e / e.sum()", "    e = np.exp(logits - m)\n    return e / e.max()",
+     "importance softmax normalised by the max"),
+]
+
+
+def _load(fname, old, new):
+    path = os.path.join(ORACLE_DIR, fname)
+    src = open(path).read()
+    assert src.count(old) == 1, (fname, old)
+    src = src.replace(old, new).replace("from .sals import", "from oracle.sals import")
+    mod = types.ModuleType("oracle_mutant_" + fname[:-3])
+    exec(compile(src, path + " (mutant)", "exec"), mod.__dict__)
+    return mod
+
+
+def _patch(monkeypatch, mod, target):
+    for name, obj in vars(mod).items():
+        if isinstance(obj, types.FunctionType) and obj.__module__ == mod.__name__ and hasattr(target, name):
+            monkeypatch.setattr(target, name, obj)
+            if target is OS and hasattr(OC, name):
+                monkeypatch.setattr(OC, name, obj)
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[3] for m in MUTANTS])
+def test_some_pin_catches(mutant, monkeypatch):
+    fname, old, new, what = mutant
+    mod = _load(fname, old, new)
+    _patch(monkeypatch, mod, OS if fname == "sals.py" else OC)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except Exception:  # noqa: BLE001 - any failure of a pin counts as catching the mutant
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches: {what}"
+
+
+def test_unmutated_copy_passes(monkeypatch):
+    """Loading the sources through the same path without a change passes every pin."""
+    for fname, target in (("sals.py", OS), ("compact.py", OC)):
+        _patch(monkeypatch, _load(fname, "import numpy as np", "import numpy as np"), target)
+    for pin in PINS:
+        pin()
