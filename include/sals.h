@@ -1,0 +1,217 @@
+/*
+ * sals.h - C ABI of the SALS decode path and post-prefill KV compaction for MI355X (gfx950).
+ *
+ * The method (sources cited by page title and section):
+ *   "SALS: Sparse Attention in Latent Space for KV cache Compression" (arXiv 2510.24273),
+ *   section 方法详解 -> 技术框架, stages 1-4: keys (before RoPE) and values are projected into a
+ *   compact latent space, L = X . P; each decode query selects tokens through a RoPE-free
+ *   query-key interaction in that space; only the selected tokens are rebuilt, L_sel . P^T, with
+ *   RoPE applied at their true positions; standard attention runs over them. 关键设计 items 1-4:
+ *   P from SVD or random, sparsity set by the number of selected tokens, top-k selection.
+ *   "VL-Cache" author responses (reviewers KiPr W1/W2/W6, XVzL W2/W3, X8F2 Q2): importance from
+ *   the softmax attention A = softmax(Q K^T / sqrt(d)) of the queries that follow the prompt's
+ *   visual tokens, top-k of that importance, eviction once after prefill.
+ *
+ * Conventions shared by every entry point
+ *   - Arrays are device pointers, row-major and contiguous, in the layout stated per argument.
+ *     "dtype" arrays hold SALS_F32 (IEEE fp32) or SALS_BF16 (bfloat16) elements.
+ *   - Every pointer must be 16-byte aligned (SALS_ERR_ALIGN otherwise).
+ *   - The caller owns every buffer, workspaces included. The library never allocates, frees or
+ *     synchronises; all work is enqueued on `stream` (NULL = the null stream) and returns
+ *     asynchronously. Buffers must stay valid until that work completes.
+ *   - Inputs are never written. Outputs are fully overwritten. Inputs, outputs and workspace
+ *     must not overlap.
+ *   - All argument checks run before any HIP call, so they cost nothing on the GPU and can be
+ *     exercised on a host with no GPU. A failed HIP call returns SALS_ERR_HIP; the raw hipError_t
+ *     is available from sals_last_hip_error() on the calling thread.
+ *   - Inputs must be finite. Results are deterministic: the same inputs give the same bits.
+ *   - Nothing is printed and no C++ exception crosses this interface. All calls are reentrant.
+ */
+#ifndef SALS_H
+#define SALS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SALS_ABI_VERSION 1
+
+/* A hipStream_t (same underlying type); NULL selects the null stream. */
+typedef struct ihipStream_t* sals_stream_t;
+
+typedef enum {
+    SALS_OK = 0,
+    SALS_ERR_NULL = 1,      /* a required pointer is NULL */
+    SALS_ERR_SHAPE = 2,     /* unsupported or inconsistent shape */
+    SALS_ERR_DTYPE = 3,     /* unknown element type */
+    SALS_ERR_RANGE = 4,     /* a length or index argument is out of range */
+    SALS_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the size query returned */
+    SALS_ERR_ALIGN = 6,     /* a pointer is not 16-byte aligned */
+    SALS_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed */
+} sals_status;
+
+typedef enum { SALS_F32 = 0, SALS_BF16 = 1 } sals_dtype;
+
+/* Shape of one attention layer with a latent cache.
+ *   B      sequences (one new token each per decode step)
+ *   H_q    query heads; H_kv KV heads, H_q % H_kv == 0, H_q / H_kv <= 8
+ *   d      head dimension, 64 or 128
+ *   r      latent rank: 32 or a multiple of 64 up to 512, with d * r * elemsize <= 128 KiB
+ *   dtype  element type of q, X, P and L (fp32 accumulation throughout) */
+typedef struct {
+    int32_t B, H_q, H_kv, d, r;
+    int32_t dtype; /* sals_dtype */
+} sals_shape;
+
+/* Token selection knobs (SALS 关键设计 items 2 and 4).
+ *   k  top-k over the non-window positions [0, ctx - w)
+ *   w  recent window [ctx - w, ctx), always selected
+ *   G  selection groups per sequence, H_kv % G == 0: KV head g belongs to group g*G/H_kv and all
+ *      KV heads of a group use one token set; a group's score is the sum over its query heads
+ *      of the raw latent dot products (G = 1: one set per sequence; G = H_kv: one per KV head). */
+typedef struct {
+    int32_t k, w, G;
+} sals_select;
+
+/* Shape of a plain (post-RoPE) KV cache for compaction and dense decode.
+ * H_q % H_kv == 0, H_q / H_kv <= 8, d in {64, 128}, dtype SALS_BF16 or SALS_F32. */
+typedef struct {
+    int32_t B, H_q, H_kv, d;
+    int32_t dtype; /* sals_dtype */
+} kvc_shape;
+
+/* Version of this interface (SALS_ABI_VERSION). */
+int32_t sals_abi_version(void);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* sals_status_string(sals_status status);
+
+/* Raw hipError_t of the last failed HIP call on this thread (0 if none). */
+int32_t sals_last_hip_error(void);
+
+/*
+ * sals_project_kv - latent projection of new cache rows (SALS 技术框架 stage 1).
+ *   L[b, t0 + t, :] = X[b, t, :] . P for t in [0, T), for K and, when given, for V.
+ *   X  = pre-RoPE rows of all KV heads side by side (D = H_kv * d), P = the layer's projection.
+ * Args
+ *   s            shape (B, H_kv, d, r, dtype used; H_q ignored)
+ *   Xk, Xv       [B, T, D] dtype, read. Xv may be NULL (then Pv and Lv must be NULL too).
+ *   Pk, Pv       [D, r] dtype, read.
+ *   Lk, Lv       [B, ctx_cap, r] dtype; rows [t0, t0 + T) written, other rows untouched.
+ *   ctx_cap      rows per sequence in L; 0 <= t0, 1 <= T, t0 + T <= ctx_cap.
+ * Arithmetic: fp32 products and sums, one rounding to dtype (nearest even) at the end.
+ * Errors: NULL/ALIGN/SHAPE/DTYPE/RANGE as stated above, HIP on launch failure.
+ */
+sals_status sals_project_kv(const sals_shape* s, const void* Xk, const void* Xv, const void* Pk,
+                            const void* Pv, void* Lk, void* Lv, int32_t ctx_cap, int32_t t0,
+                            int32_t T, sals_stream_t stream);
+
+/*
+ * sals_decode_workspace_bytes - exact workspace size of sals_decode_step for (s, sel, ctx).
+ * Writes *bytes; returns the same argument errors sals_decode_step would.
+ */
+sals_status sals_decode_workspace_bytes(const sals_shape* s, const sals_select* sel, int32_t ctx,
+                                        size_t* bytes);
+
+/*
+ * sals_decode_step - one decode step of one layer over a latent cache (SALS 技术框架 stages 2-4).
+ *   For every sequence b and group g_s:
+ *     q~      = sum over the group's query heads h of q[b, h] . P_k[kv(h)]          (fp32)
+ *     S[t]    = q~ . L_k[b, t] for t in [0, T_c), T_c = max(0, ctx - w)              (fp32)
+ *     Sel     = the min(k, T_c) largest S (ties to the lowest index) plus [T_c, ctx), ascending
+ *   and for every query head h (KV head g = h * H_kv / H_q, group of g):
+ *     K_hat   = RoPE(L_k[b, Sel] . P_k[g]^T, Sel),  V_hat = L_v[b, Sel] . P_v[g]^T
+ *     out[b,h]= softmax(RoPE(q[b,h], ctx - 1) . K_hat^T / sqrt(d)) . V_hat
+ *   P_x[g] = rows [g*d, (g+1)*d) of P_x. RoPE is rotate-half on pairs (i, i + d/2) with angle
+ *   p * rope_base^(-2i/d); angles are reduced in fp64 before fp32 sin/cos.
+ * Args
+ *   s, sel        shapes and knobs as documented on the structs; 1 <= ctx <= ctx_cap, k >= 0,
+ *                 w >= 0.
+ *   rope_base     RoPE base (> 1).
+ *   q             [B, H_q, d] dtype, pre-RoPE query of the token at position ctx - 1.
+ *   Lk, Lv        [B, ctx_cap, r] dtype latent caches; rows [0, ctx) are read.
+ *   Pk, Pv        [D, r] dtype.
+ *   out           [B, H_q, d] fp32, written.
+ *   sel_out       NULL, or [B, G, n_sel] int32 written with the selected positions, ascending,
+ *                 n_sel = min(k, T_c) + (ctx - T_c).
+ *   ws, ws_bytes  workspace of at least sals_decode_workspace_bytes(s, sel, ctx) bytes.
+ * Errors: as stated above; SALS_ERR_WORKSPACE if ws is NULL or too small.
+ */
+sals_status sals_decode_step(const sals_shape* s, const sals_select* sel, float rope_base,
+                             const void* q, const void* Lk, const void* Lv, const void* Pk,
+                             const void* Pv, int32_t ctx_cap, int32_t ctx, float* out,
+                             int32_t* sel_out, void* ws, size_t ws_bytes, sals_stream_t stream);
+
+/*
+ * sals_decode_step_traced - sals_decode_step that also records caller-created HIP events on
+ * `stream` at its stage boundaries, for per-kernel timing without a profiler (a tracing
+ * aid; the computation and results are identical to sals_decode_step):
+ *   events[0] before the latent query, events[1] before the scoring, events[2] before the
+ *   top-k selection, events[3] before rebuild + attention, events[4] before the split merge,
+ *   events[5] after the last kernel. A stage that does not run for a shape leaves its two
+ *   events back to back.
+ * events: at least 6 hipEvent_t handles from hipEventCreate (owned by the caller);
+ * SALS_ERR_NULL if events is NULL, SALS_ERR_RANGE if n_events < 6.
+ */
+sals_status sals_decode_step_traced(const sals_shape* s, const sals_select* sel, float rope_base,
+                                    const void* q, const void* Lk, const void* Lv, const void* Pk,
+                                    const void* Pv, int32_t ctx_cap, int32_t ctx, float* out,
+                                    int32_t* sel_out, void* ws, size_t ws_bytes,
+                                    sals_stream_t stream, void* const* events, int32_t n_events);
+
+/*
+ * kv_compact_workspace_bytes - exact workspace size of kv_compact for (c, ctx, w, k_keep).
+ */
+sals_status kv_compact_workspace_bytes(const kvc_shape* c, int32_t ctx, int32_t w, int32_t k_keep,
+                                       size_t* bytes);
+
+/*
+ * kv_compact - post-prefill compaction of a plain KV cache (VL-Cache responses KiPr W1/W2,
+ * XVzL W2/W3, X8F2 Q2; PureKV abstract).
+ *   For every sequence b and KV head g, with observation queries at positions p_i = ctx - w + i:
+ *     I[t]   = sum over query heads h of KV head g, sum over i < w, of
+ *              softmax_{t' <= p_i}(Qobs[b, h, i] . K[b, g, t'] / sqrt(d))[t]          (fp32)
+ *     kept   = the k_keep largest I (ties to the lowest index), ascending
+ *     Kc, Vc = K[b, g, kept], V[b, g, kept]   (bit-exact copies)
+ * Args
+ *   c             shape; K, V and Qobs use c->dtype.
+ *   K, V          [B, H_kv, ctx_cap, d] as stored (RoPE already applied), rows [0, ctx) read.
+ *   Qobs          [B, H_q, w, d] queries of the last w prompt positions (RoPE applied).
+ *   w             1 <= w <= ctx; ctx <= ctx_cap; 1 <= k_keep <= ctx.
+ *   Kc, Vc        [B, H_kv, k_keep, d] written.
+ *   kept          [B, H_kv, k_keep] int32 written.
+ *   importance    NULL, or [B, H_kv, ctx] fp32 written with I.
+ *   ws, ws_bytes  workspace of at least kv_compact_workspace_bytes(c, ctx, w, k_keep) bytes.
+ */
+sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const void* Qobs,
+                       int32_t w, int32_t ctx_cap, int32_t ctx, int32_t k_keep, void* Kc, void* Vc,
+                       int32_t* kept, float* importance, void* ws, size_t ws_bytes,
+                       sals_stream_t stream);
+
+/*
+ * sals_dense_decode_workspace_bytes - exact workspace size of sals_dense_decode for (c, n).
+ */
+sals_status sals_dense_decode_workspace_bytes(const kvc_shape* c, int32_t n, size_t* bytes);
+
+/*
+ * sals_dense_decode - one decode step of plain attention over a contiguous cache, e.g. the
+ * compact cache kv_compact produced (VL-Cache KiPr W1 formula, one query row):
+ *   out[b, h] = softmax(q[b, h] . K[b, g, :n]^T / sqrt(d)) . V[b, g, :n],  g = h * H_kv / H_q
+ * Args
+ *   q             [B, H_q, d] c->dtype, RoPE already applied.
+ *   K, V          [B, H_kv, stride_tokens, d] c->dtype; rows [0, n) read; 1 <= n <= stride_tokens.
+ *   out           [B, H_q, d] fp32 written.
+ *   ws, ws_bytes  workspace of at least sals_dense_decode_workspace_bytes(c, n) bytes.
+ */
+sals_status sals_dense_decode(const kvc_shape* c, const void* q, const void* K, const void* V,
+                              int32_t n, int32_t stride_tokens, float* out, void* ws,
+                              size_t ws_bytes, sals_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SALS_H */

@@ -1,0 +1,107 @@
+// Device-side helpers shared by the gfx950 kernels: element types, MFMA fragment access,
+// key transforms and wave-level reductions. Wavefronts are 64 lanes wide.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sals {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Storage element types. HILO: the latent query is split into bf16 high + low parts so that a
+// bf16 MFMA reproduces an fp32 dot product to ~2^-16 relative.
+struct F32 {
+  using elem = float;
+  static constexpr int KSTEP = 4;  // k per 16x16 MFMA
+  static constexpr int KPL = 1;    // k elements per lane per MFMA
+  static constexpr bool HILO = false;
+  using frag = float;
+  __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float to_f32(elem e) { return e; }
+};
+
+struct BF16 {
+  using elem = uint16_t;
+  static constexpr int KSTEP = 32;
+  static constexpr int KPL = 8;
+  static constexpr bool HILO = true;
+  using frag = bf16x8_t;
+  __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float to_f32(elem e) { return bf16_bits_to_f32(e); }
+};
+
+// A lane's MFMA operand data for one 16-row tile is a contiguous run of SEG = R/4 elements of
+// one row (the k dimension is permuted so that lane group q = lane/16 owns elements
+// [q*R/4, (q+1)*R/4) and step kb uses elements kb*KPL .. kb*KPL+KPL-1 of that run; A and B use
+// the same permutation, so the contraction is unchanged). The run is held as 16-byte chunks.
+template <class T, int R>
+struct Seg {
+  static constexpr int SEG = R / 4;
+  static constexpr int BYTES = SEG * (int)sizeof(typename T::elem);
+  static constexpr int NCH = BYTES / 16;
+  static constexpr int KS = R / T::KSTEP;  // MFMA steps over the full rank
+  static_assert(BYTES % 16 == 0, "lane segment must be a whole number of 16-byte chunks");
+};
+
+template <class T>
+__device__ __forceinline__ typename T::frag frag_at(const u32x4* ch, int kb);
+
+template <>
+__device__ __forceinline__ float frag_at<F32>(const u32x4* ch, int kb) {
+  return __uint_as_float(ch[kb >> 2][kb & 3]);
+}
+
+template <>
+__device__ __forceinline__ bf16x8_t frag_at<BF16>(const u32x4* ch, int kb) {
+  return __builtin_bit_cast(bf16x8_t, ch[kb]);
+}
+
+// Order-preserving uint32 key of a float: larger float -> larger key; -0.0 and +0.0 map to the
+// same key. Inputs are finite.
+__device__ __forceinline__ uint32_t float_key(float x) {
+  uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace sals

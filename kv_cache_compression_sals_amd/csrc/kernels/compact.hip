@@ -1,0 +1,421 @@
+// Post-prefill compaction (VL-Cache responses: reviewer KiPr W1 formula A = softmax(QK^T/sqrt(d)),
+// W2 post-vision query rows, XVzL W2/W3 top-k of the importance and eviction, X8F2 Q2 once after
+// prefill; PureKV abstract: no full attention matrix is formed) and plain decode attention over
+// a contiguous cache (VL-Cache KiPr W6: fewer cached tokens, less HBM traffic).
+//
+// Importance, per (sequence b, KV head g):
+//   I[t] = sum_{h of g} sum_{i < w} exp(l_{h,i,t} - m_{h,i}) / s_{h,i},   t <= p_i = ctx - w + i
+// with l = Qobs . K / sqrt(d) and (m, s) the row max and softmax denominator of query (h, i).
+// Pass 1 computes (m, s) per token chunk with an online update and merges the chunks; pass 2
+// recomputes the logits and accumulates I. Both passes are MFMA tiles of 16 tokens (A operand,
+// streamed from HBM) x 16 queries (B operand, in registers), so only the last w query rows are
+// ever formed, never the n x n attention matrix.
+#include "../common.h"
+#include "../launch.h"
+
+namespace sals {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 1024;  // tokens per workgroup
+constexpr int kQG = 64;       // observation queries per workgroup (4 MFMA column blocks)
+
+template <class T, int DH>
+struct Frags {
+  using SG = Seg<T, DH>;  // the head dimension plays the role of the contraction length
+  typename T::frag q[4][SG::KS];
+};
+
+// Query fragments of queries qg*64 + nb*16 + n16 (zero past w).
+template <class T, int DH>
+__device__ __forceinline__ void load_q_frags(const typename T::elem* __restrict__ Qh, int w, int qg,
+                                             int lane, Frags<T, DH>& f) {
+  using SG = Seg<T, DH>;
+  const int n16 = lane & 15, q4 = lane >> 4;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int qi = qg * kQG + nb * 16 + n16;
+    u32x4 ch[SG::NCH];
+    if (qi < w) {
+      const u32x4* p = (const u32x4*)(Qh + (size_t)qi * DH + q4 * SG::SEG);
+#pragma unroll
+      for (int c = 0; c < SG::NCH; ++c) ch[c] = p[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < SG::NCH; ++c) ch[c] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int kb = 0; kb < SG::KS; ++kb) f.q[nb][kb] = frag_at<T>(ch, kb);
+  }
+}
+
+// logits[nb][i] = K[t0 + q4*4 + i] . Qobs[qg*64 + nb*16 + n16]   (unscaled)
+template <class T, int DH>
+__device__ __forceinline__ void logit_tile(const typename T::elem* __restrict__ Kh, int t0, int ctx,
+                                           int lane, const Frags<T, DH>& f, f32x4* acc) {
+  using SG = Seg<T, DH>;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int t = min(t0 + n16, ctx - 1);
+  u32x4 ch[SG::NCH];
+  const u32x4* p = (const u32x4*)(Kh + (size_t)t * DH + q4 * SG::SEG);
+#pragma unroll
+  for (int c = 0; c < SG::NCH; ++c) ch[c] = p[c];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < SG::KS; ++kb) {
+    const typename T::frag a = frag_at<T>(ch, kb);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(a, f.q[nb][kb], acc[nb]);
+  }
+}
+
+// Pass 1: per chunk (m, s) of every observation query. grid (n_chunks, H_q * n_qg, B).
+template <class T, int DH>
+__global__ __launch_bounds__(kThreads) void imp_stats_kernel(const typename T::elem* __restrict__ K,
+                                                             const typename T::elem* __restrict__ Q,
+                                                             float* __restrict__ part, int H_q,
+                                                             int H_kv, int w, int ctx_cap, int ctx,
+                                                             int n_chunks, int n_qg) {
+  __shared__ float red[4][kQG][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int c = blockIdx.x, h = blockIdx.y / n_qg, qg = blockIdx.y % n_qg, b = blockIdx.z;
+  const int g = h / (H_q / H_kv);
+  const float scale = 1.0f / sqrtf((float)DH);
+  const typename T::elem* Kh = K + ((size_t)b * H_kv + g) * ctx_cap * DH;
+  Frags<T, DH> f;
+  load_q_frags<T, DH>(Q + ((size_t)b * H_q + h) * w * DH, w, qg, lane, f);
+  float m[4], s[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    m[nb] = -INFINITY;
+    s[nb] = 0.f;
+  }
+  const int cbeg = c * kChunk, cend = min(ctx, cbeg + kChunk);
+  for (int t0 = cbeg + wave * 16; t0 < cend; t0 += 64) {
+    f32x4 acc[4];
+    logit_tile<T, DH>(Kh, t0, ctx, lane, f, acc);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int qi = qg * kQG + nb * 16 + n16;
+      const int lim = ctx - w + qi;  // last visible position of query qi
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + q4 * 4 + i;
+        if (t < cend && t <= lim && qi < w) {
+          const float x = acc[nb][i] * scale;
+          if (x > m[nb]) {
+            s[nb] = s[nb] * expf(m[nb] - x) + 1.0f;
+            m[nb] = x;
+          } else {
+            s[nb] += expf(x - m[nb]);
+          }
+        }
+      }
+    }
+  }
+  // merge the 4 lane groups (same query), then the 4 waves
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int msk = 16; msk <= 32; msk <<= 1) {
+      const float mo = __shfl_xor(m[nb], msk), so = __shfl_xor(s[nb], msk);
+      const float mn = fmaxf(m[nb], mo);
+      s[nb] = (mn == -INFINITY) ? 0.f : s[nb] * expf(m[nb] - mn) + so * expf(mo - mn);
+      m[nb] = mn;
+    }
+    if (lane < 16) {
+      red[wave][nb * 16 + lane][0] = m[nb];
+      red[wave][nb * 16 + lane][1] = s[nb];
+    }
+  }
+  __syncthreads();
+  if (tid < kQG) {
+    const int qi = qg * kQG + tid;
+    float M = -INFINITY;
+    for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, red[wv][tid][0]);
+    float S = 0.f;
+    if (M != -INFINITY)
+      for (int wv = 0; wv < 4; ++wv) S += red[wv][tid][1] * expf(red[wv][tid][0] - M);
+    if (qi < w) {
+      float* p = part + ((((size_t)b * H_q + h) * w + qi) * n_chunks + c) * 2;
+      p[0] = M;
+      p[1] = S;
+    }
+  }
+}
+
+// Merge chunk partials: stats[b][h][i] = (M, S).
+__global__ void imp_merge_kernel(const float* __restrict__ part, float* __restrict__ stats, int n,
+                                 int n_chunks) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  const float* p = part + (size_t)e * n_chunks * 2;
+  float M = -INFINITY;
+  for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, p[2 * c]);
+  float S = 0.f;
+  for (int c = 0; c < n_chunks; ++c)
+    if (p[2 * c] != -INFINITY) S += p[2 * c + 1] * expf(p[2 * c] - M);
+  stats[2 * (size_t)e] = M;
+  stats[2 * (size_t)e + 1] = S;
+}
+
+// Pass 2: I[b][g][t]. grid (n_chunks, H_kv, B).
+template <class T, int DH>
+__global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::elem* __restrict__ K,
+                                                             const typename T::elem* __restrict__ Q,
+                                                             const float* __restrict__ stats,
+                                                             float* __restrict__ I, int H_q,
+                                                             int H_kv, int w, int ctx_cap, int ctx) {
+  __shared__ float acc_lds[kChunk];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int nqh = H_q / H_kv;
+  const float scale = 1.0f / sqrtf((float)DH);
+  const typename T::elem* Kh = K + ((size_t)b * H_kv + g) * ctx_cap * DH;
+  const int cbeg = c * kChunk, cend = min(ctx, cbeg + kChunk);
+  for (int j = tid; j < kChunk; j += kThreads) acc_lds[j] = 0.f;
+  __syncthreads();
+  const int n_qg = ceil_div(w, kQG);
+  for (int hh = 0; hh < nqh; ++hh) {
+    const int h = g * nqh + hh;
+    for (int qg = 0; qg < n_qg; ++qg) {
+      Frags<T, DH> f;
+      load_q_frags<T, DH>(Q + ((size_t)b * H_q + h) * w * DH, w, qg, lane, f);
+      float M[4], invS[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int qi = qg * kQG + nb * 16 + n16;
+        if (qi < w) {
+          const float* st = stats + (((size_t)b * H_q + h) * w + qi) * 2;
+          M[nb] = st[0];
+          invS[nb] = 1.0f / st[1];
+        } else {
+          M[nb] = 0.f;
+          invS[nb] = 0.f;
+        }
+      }
+      for (int t0 = cbeg + wave * 16; t0 < cend; t0 += 64) {
+        f32x4 acc[4];
+        logit_tile<T, DH>(Kh, t0, ctx, lane, f, acc);
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int qi = qg * kQG + nb * 16 + n16;
+          const int lim = ctx - w + qi;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = t0 + q4 * 4 + i;
+            if (qi < w && t <= lim) part[i] += expf(acc[nb][i] * scale - M[nb]) * invS[nb];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = part[i];
+          v += __shfl_xor(v, 1);
+          v += __shfl_xor(v, 2);
+          v += __shfl_xor(v, 4);
+          v += __shfl_xor(v, 8);
+          part[i] = v;
+        }
+        if (n16 == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = t0 + q4 * 4 + i;
+            if (t < cend) acc_lds[t - cbeg] += part[i];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < cend - cbeg; j += kThreads) I[((size_t)b * H_kv + g) * ctx + cbeg + j] = acc_lds[j];
+}
+
+// Kc/Vc rows: bit-exact 16-byte copies. One thread per 16-byte chunk.
+__global__ void gather_rows_kernel(const u32x4* __restrict__ K, const u32x4* __restrict__ V,
+                                   const int32_t* __restrict__ kept, u32x4* __restrict__ Kc,
+                                   u32x4* __restrict__ Vc, long n_chunks_total, int cpr, int ctx_cap,
+                                   int k_keep) {
+  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n_chunks_total) return;
+  const long row = e / cpr;
+  const int cc = (int)(e % cpr);
+  const long bg = row / k_keep;
+  const long src = (bg * ctx_cap + kept[row]) * cpr + cc;
+  Kc[e] = K[src];
+  Vc[e] = V[src];
+}
+
+// Dense flash-decode over a contiguous cache, one query head per workgroup and split.
+// Lane l of a wave reads token l/4, columns (l%4)*DH/4 .. : 4 lanes share one row.
+template <class T, int DH>
+__global__ __launch_bounds__(kThreads) void dense_decode_kernel(
+    const typename T::elem* __restrict__ q, const typename T::elem* __restrict__ K,
+    const typename T::elem* __restrict__ V, float* __restrict__ out, float* __restrict__ part,
+    int H_q, int H_kv, int n, int stride, int split_len, int n_splits) {
+  constexpr int CW = DH / 4;  // columns per lane
+  __shared__ float qsh[DH];
+  __shared__ float red[4][DH + 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (H_q / H_kv);
+  const float scale = 1.0f / sqrtf((float)DH);
+  for (int c = tid; c < DH; c += kThreads) qsh[c] = T::to_f32(q[((size_t)b * H_q + h) * DH + c]) * scale;
+  __syncthreads();
+  const int cb = (lane & 3) * CW;
+  float qv[CW];
+#pragma unroll
+  for (int j = 0; j < CW; ++j) qv[j] = qsh[cb + j];
+  const typename T::elem* Kh = K + ((size_t)b * H_kv + g) * stride * DH;
+  const typename T::elem* Vh = V + ((size_t)b * H_kv + g) * stride * DH;
+  const int jbeg = sp * split_len, jend = min(n, jbeg + split_len);
+  float m = -INFINITY, l = 0.f;
+  float o[CW];
+#pragma unroll
+  for (int j = 0; j < CW; ++j) o[j] = 0.f;
+  for (int t0 = jbeg + wave * 16; t0 < jend; t0 += 64) {
+    const int t = t0 + (lane >> 2);
+    const bool ok = t < jend;
+    const int tt = ok ? t : jend - 1;
+    float x = 0.f;
+    const typename T::elem* kr = Kh + (size_t)tt * DH + cb;
+#pragma unroll
+    for (int j = 0; j < CW; ++j) x = fmaf(qv[j], T::to_f32(kr[j]), x);
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    if (!ok) x = -INFINITY;
+    const float tm = wave_max(x);
+    const float mn = fmaxf(m, tm);
+    const float corr = expf(m - mn);
+    const float p = ok ? expf(x - mn) : 0.f;
+    float ps = p;
+    ps += __shfl_xor(ps, 4);
+    ps += __shfl_xor(ps, 8);
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = l * corr + ps;
+    m = mn;
+    const typename T::elem* vr = Vh + (size_t)tt * DH + cb;
+#pragma unroll
+    for (int j = 0; j < CW; ++j) o[j] = fmaf(p, T::to_f32(vr[j]), o[j] * corr);
+  }
+  // reduce o over the 16 tokens of the wave (lanes with equal lane%4)
+#pragma unroll
+  for (int j = 0; j < CW; ++j) {
+    float v = o[j];
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    o[j] = v;
+  }
+  if (lane < 4) {
+#pragma unroll
+    for (int j = 0; j < CW; ++j) red[wave][cb + j] = o[j];
+  }
+  if (lane == 0) {
+    red[wave][DH] = m;
+    red[wave][DH + 1] = l;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, red[wv][DH]);
+  float wgt[4], L = 0.f;
+  for (int wv = 0; wv < 4; ++wv) {
+    wgt[wv] = red[wv][DH] == -INFINITY ? 0.f : expf(red[wv][DH] - M);
+    L += red[wv][DH + 1] * wgt[wv];
+  }
+  for (int c = tid; c < DH; c += kThreads) {
+    float oc = 0.f;
+    for (int wv = 0; wv < 4; ++wv) oc += red[wv][c] * wgt[wv];
+    if (n_splits == 1) {
+      out[((size_t)b * H_q + h) * DH + c] = oc / L;
+    } else {
+      float* pp = part + (((size_t)b * H_q + h) * n_splits + sp) * (DH + 2);
+      pp[2 + c] = oc;
+      if (c == 0) {
+        pp[0] = M;
+        pp[1] = L;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+#define SALS_KVC_DISPATCH(dtype, d, CALL)        \
+  do {                                           \
+    if (dtype == 0 && d == 64) {                 \
+      using TT = F32;                            \
+      constexpr int DD = 64;                     \
+      CALL;                                      \
+    } else if (dtype == 0 && d == 128) {         \
+      using TT = F32;                            \
+      constexpr int DD = 128;                    \
+      CALL;                                      \
+    } else if (dtype == 1 && d == 64) {          \
+      using TT = BF16;                           \
+      constexpr int DD = 64;                     \
+      CALL;                                      \
+    } else if (dtype == 1 && d == 128) {         \
+      using TT = BF16;                           \
+      constexpr int DD = 128;                    \
+      CALL;                                      \
+    } else {                                     \
+      return hipErrorInvalidValue;               \
+    }                                            \
+  } while (0)
+
+hipError_t launch_importance_stats(int dtype, const void* K, const void* Qobs, float* stats,
+                                   int B, int H_q, int H_kv, int d, int w, int ctx_cap, int ctx,
+                                   hipStream_t st) {
+  // stats buffer layout: [B*H_q*w*n_chunks*2] chunk partials followed by [B*H_q*w*2] merged
+  const int n_chunks = ceil_div(ctx, kChunk), n_qg = ceil_div(w, kQG);
+  float* part = stats + (size_t)B * H_q * w * 2;
+  dim3 grid(n_chunks, H_q * n_qg, B);
+  SALS_KVC_DISPATCH(dtype, d,
+                    (imp_stats_kernel<TT, DD><<<grid, kThreads, 0, st>>>(
+                        (const TT::elem*)K, (const TT::elem*)Qobs, part, H_q, H_kv, w, ctx_cap, ctx,
+                        n_chunks, n_qg)));
+  const int n = B * H_q * w;
+  imp_merge_kernel<<<ceil_div(n, 256), 256, 0, st>>>(part, stats, n, n_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_importance_accum(int dtype, const void* K, const void* Qobs,
+                                   const float* stats, float* I, int B, int H_q, int H_kv, int d,
+                                   int w, int ctx_cap, int ctx, hipStream_t st) {
+  dim3 grid(ceil_div(ctx, kChunk), H_kv, B);
+  SALS_KVC_DISPATCH(dtype, d,
+                    (imp_accum_kernel<TT, DD><<<grid, kThreads, 0, st>>>(
+                        (const TT::elem*)K, (const TT::elem*)Qobs, stats, I, H_q, H_kv, w, ctx_cap,
+                        ctx)));
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(int dtype, const void* K, const void* V, const int32_t* kept,
+                              void* Kc, void* Vc, int BG, int d, int ctx_cap, int k_keep,
+                              hipStream_t st) {
+  const int cpr = d * (dtype == 0 ? 4 : 2) / 16;
+  const long total = (long)BG * k_keep * cpr;
+  if (total <= 0) return hipSuccess;
+  gather_rows_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(
+      (const u32x4*)K, (const u32x4*)V, kept, (u32x4*)Kc, (u32x4*)Vc, total, cpr, ctx_cap, k_keep);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_decode(int dtype, const void* q, const void* K, const void* V, float* out,
+                               float* part, int B, int H_q, int H_kv, int d, int n, int stride,
+                               int split_len, int n_splits, hipStream_t st) {
+  dim3 grid(n_splits, H_q, B);
+  SALS_KVC_DISPATCH(dtype, d,
+                    (dense_decode_kernel<TT, DD><<<grid, kThreads, 0, st>>>(
+                        (const TT::elem*)q, (const TT::elem*)K, (const TT::elem*)V, out, part, H_q,
+                        H_kv, n, stride, split_len, n_splits)));
+  return hipGetLastError();
+}
+
+}  // namespace sals

@@ -1,0 +1,72 @@
+// Internal launchers (host side). Each enqueues its kernels on `st` and returns the error
+// hipGetLastError reports right after the launches (hipSuccess when all were accepted).
+// Shapes were validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sals {
+
+// ---- decode path -------------------------------------------------------------------------
+
+// q~ partial sums: qpart[rs][b][j] = sum over rows i of row split rs of
+// qsum[b][i] * P_k[i][j], where qsum[b][i] is the sum of q[b][h][i % d] over the query heads
+// h that read KV head i / d. Row splits are `rps` rows long and never straddle a group.
+hipError_t launch_latent_query(int dtype, const void* q, const void* Pk, float* qpart, float* qt,
+                               int B, int H_q, int H_kv, int d, int r, int G, int rps,
+                               hipStream_t st);
+
+// S[b][s][t] = q~[b][s] . L_k[b][t], t < Tc.
+hipError_t launch_latent_score(int dtype, const float* qt, const void* Lk, float* S, int B, int G,
+                               int r, int Tc, int ctx_cap, hipStream_t st);
+
+// sel[row][0 .. kp) = top-kp of S[row][0 .. Tc) (ties to the lowest index), ascending;
+// sel[row][kp .. n_sel) = Tc .. ctx-1.
+hipError_t launch_topk_window(const float* S, int32_t* sel, int rows, int Tc, int kp, int ctx,
+                              int n_sel, hipStream_t st);
+
+// Gather + rebuild + RoPE + attention over the selected rows, split along the selected set.
+// With n_splits == 1 the normalised result goes to out; otherwise (m, l, o) partials go to part.
+hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const void* Lv,
+                                const void* Pk, const void* Pv, const int32_t* sel, float* out,
+                                float* part, int B, int H_q, int H_kv, int d, int r, int G,
+                                int ctx_cap, int ctx, int n_sel, int split_len, int n_splits,
+                                float rope_base, hipStream_t st);
+
+// LSE merge of split partials into out[b][h][:].
+hipError_t launch_combine(const float* part, float* out, int BH, int d, int n_splits,
+                          hipStream_t st);
+
+// Largest selected-set split that fits in on-chip memory for this shape (0 if unsupported).
+int select_attend_max_split(int dtype, int d, int r, int nqh);
+
+// ---- projection --------------------------------------------------------------------------
+
+hipError_t launch_project(int dtype, const void* X, const void* P, void* L, int B, int T, int D,
+                          int r, int ctx_cap, int t0, hipStream_t st);
+
+// ---- compaction and dense decode ---------------------------------------------------------
+
+// Per (b, g, observation query i): row max m and softmax denominator l of the causal logits.
+hipError_t launch_importance_stats(int dtype, const void* K, const void* Qobs, float* stats,
+                                   int B, int H_q, int H_kv, int d, int w, int ctx_cap, int ctx,
+                                   hipStream_t st);
+
+// I[b][g][t] from the stats (second pass over K).
+hipError_t launch_importance_accum(int dtype, const void* K, const void* Qobs,
+                                   const float* stats, float* I, int B, int H_q, int H_kv, int d,
+                                   int w, int ctx_cap, int ctx, hipStream_t st);
+
+// Kc/Vc[b][g][j] = K/V[b][g][kept[b][g][j]].
+hipError_t launch_gather_rows(int dtype, const void* K, const void* V, const int32_t* kept,
+                              void* Kc, void* Vc, int BG, int d, int ctx_cap, int k_keep,
+                              hipStream_t st);
+
+// Flash-decode over a contiguous cache: partials per split, or out directly (n_splits == 1).
+hipError_t launch_dense_decode(int dtype, const void* q, const void* K, const void* V, float* out,
+                               float* part, int B, int H_q, int H_kv, int d, int n, int stride,
+                               int split_len, int n_splits, hipStream_t st);
+
+}  // namespace sals

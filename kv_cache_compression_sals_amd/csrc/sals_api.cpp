@@ -1,0 +1,361 @@
+// C ABI of the SALS decode path and post-prefill compaction: argument validation (all before
+// any HIP call), workspace carving and the launch sequence on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/sals.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool misaligned(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) != 0; }
+
+int elem_size(int dtype) { return dtype == SALS_F32 ? 4 : 2; }
+
+bool rank_supported(int r) { return r == 32 || (r >= 64 && r <= 512 && r % 64 == 0); }
+
+sals_status check_layer_shape(const sals_shape* s) {
+  if (s->dtype != SALS_F32 && s->dtype != SALS_BF16) return SALS_ERR_DTYPE;
+  if (s->B < 1 || s->B > 65535 || s->H_q < 1 || s->H_kv < 1 || s->H_q % s->H_kv != 0 ||
+      s->H_q / s->H_kv > 8 || s->H_kv > 65535)
+    return SALS_ERR_SHAPE;
+  if (s->d != 64 && s->d != 128) return SALS_ERR_SHAPE;
+  if (!rank_supported(s->r)) return SALS_ERR_SHAPE;
+  if ((long)s->d * s->r * elem_size(s->dtype) > 128L * 1024) return SALS_ERR_SHAPE;
+  return SALS_OK;
+}
+
+sals_status check_kvc_shape(const kvc_shape* c) {
+  if (c->dtype != SALS_F32 && c->dtype != SALS_BF16) return SALS_ERR_DTYPE;
+  if (c->B < 1 || c->B > 65535 || c->H_q < 1 || c->H_kv < 1 || c->H_q % c->H_kv != 0 ||
+      c->H_q / c->H_kv > 8 || c->H_q > 65535)
+    return SALS_ERR_SHAPE;
+  if (c->d != 64 && c->d != 128) return SALS_ERR_SHAPE;
+  return SALS_OK;
+}
+
+sals_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int32_t)e;
+  return SALS_ERR_HIP;
+}
+
+// A device must be present and current; checked after validation, before any launch.
+sals_status device_ready() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  return SALS_OK;
+}
+
+// ---- decode plan ---------------------------------------------------------------------------
+
+struct DecodePlan {
+  int D, nqh, Tc, kp, n_sel;
+  int rps, spg;
+  int split_len, n_splits;
+  size_t off_qt, off_qpart, off_S, off_sel, off_part, total;
+};
+
+sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_t ctx,
+                             DecodePlan* p) {
+  if (!s || !sel) return SALS_ERR_NULL;
+  sals_status st = check_layer_shape(s);
+  if (st != SALS_OK) return st;
+  if (sel->G < 1 || s->H_kv % sel->G != 0) return SALS_ERR_SHAPE;
+  if (sel->k < 0 || sel->w < 0 || ctx < 1 || ctx > (1 << 26)) return SALS_ERR_RANGE;
+  p->D = s->H_kv * s->d;
+  p->nqh = s->H_q / s->H_kv;
+  p->Tc = ctx > sel->w ? ctx - sel->w : 0;
+  p->kp = sel->k < p->Tc ? sel->k : p->Tc;
+  p->n_sel = p->kp + (ctx - p->Tc);
+  // rows of P_k per latent-query workgroup: a whole group when it is at most 512 rows, else
+  // the largest whole number of KV heads that divides the group and stays within 512 rows
+  const int group_rows = p->D / sel->G;
+  if (group_rows <= 512) {
+    p->rps = group_rows;
+  } else {
+    const int m = s->H_kv / sel->G;
+    int best = 1;
+    for (int h = 1; h <= m; ++h)
+      if (m % h == 0 && h * s->d <= 512) best = h;
+    p->rps = best * s->d;
+  }
+  p->spg = group_rows / p->rps;
+  const int max_split = sals::select_attend_max_split(s->dtype, s->d, s->r, p->nqh);
+  if (max_split < 16) return SALS_ERR_SHAPE;
+  const long pairs = (long)s->B * s->H_kv;
+  const int desired = (int)((256 + pairs - 1) / pairs);
+  int split = (p->n_sel + desired - 1) / desired;
+  split = (split + 15) / 16 * 16;
+  if (split < 16) split = 16;
+  if (split > max_split) split = max_split;
+  p->split_len = split;
+  p->n_splits = (p->n_sel + split - 1) / split;
+  size_t off = 0;
+  p->off_qt = off;
+  off += align_up((size_t)s->B * sel->G * s->r * 4);
+  p->off_qpart = off;
+  if (p->spg > 1) off += align_up((size_t)(p->D / p->rps) * s->B * s->r * 4);
+  p->off_S = off;
+  off += align_up((size_t)s->B * sel->G * p->Tc * 4);
+  p->off_sel = off;
+  off += align_up((size_t)s->B * sel->G * p->n_sel * 4);
+  p->off_part = off;
+  if (p->n_splits > 1) off += align_up((size_t)s->B * s->H_q * p->n_splits * (s->d + 2) * 4);
+  p->total = off;
+  return SALS_OK;
+}
+
+// ---- compaction plan -----------------------------------------------------------------------
+
+constexpr int kImpChunk = 1024;
+
+struct CompactPlan {
+  size_t off_stats, off_I, total;
+};
+
+sals_status make_compact_plan(const kvc_shape* c, int32_t ctx, int32_t w, int32_t k_keep,
+                              CompactPlan* p) {
+  if (!c) return SALS_ERR_NULL;
+  sals_status st = check_kvc_shape(c);
+  if (st != SALS_OK) return st;
+  if (ctx < 1 || ctx > (1 << 26) || w < 1 || w > ctx || k_keep < 1 || k_keep > ctx)
+    return SALS_ERR_RANGE;
+  const size_t n_chunks = (ctx + kImpChunk - 1) / kImpChunk;
+  const size_t nq = (size_t)c->B * c->H_q * w;
+  p->off_stats = 0;
+  size_t off = align_up(nq * 2 * 4 + nq * n_chunks * 2 * 4);
+  p->off_I = off;
+  off += align_up((size_t)c->B * c->H_kv * ctx * 4);
+  p->total = off;
+  return SALS_OK;
+}
+
+// ---- dense decode plan ---------------------------------------------------------------------
+
+struct DensePlan {
+  int split_len, n_splits;
+  size_t total;
+};
+
+sals_status make_dense_plan(const kvc_shape* c, int32_t n, DensePlan* p) {
+  if (!c) return SALS_ERR_NULL;
+  sals_status st = check_kvc_shape(c);
+  if (st != SALS_OK) return st;
+  if (n < 1 || n > (1 << 26)) return SALS_ERR_RANGE;
+  const long heads = (long)c->B * c->H_q;
+  const int desired = (int)((1024 + heads - 1) / heads);
+  int split = (n + desired - 1) / desired;
+  split = (split + 63) / 64 * 64;
+  if (split < 256) split = 256;
+  p->split_len = split;
+  p->n_splits = (n + split - 1) / split;
+  p->total = p->n_splits > 1 ? align_up((size_t)heads * p->n_splits * (c->d + 2) * 4) : 0;
+  return SALS_OK;
+}
+
+}  // namespace
+
+namespace {
+
+sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_base, const void* q,
+                        const void* Lk, const void* Lv, const void* Pk, const void* Pv,
+                        int32_t ctx_cap, int32_t ctx, float* out, int32_t* sel_out, void* ws,
+                        size_t ws_bytes, sals_stream_t stream, void* const* events) {
+  if (!s || !sel || !q || !Lk || !Lv || !Pk || !Pv || !out) return SALS_ERR_NULL;
+  DecodePlan p;
+  sals_status st = make_decode_plan(s, sel, ctx, &p);
+  if (st != SALS_OK) return st;
+  if (ctx > ctx_cap || !(rope_base > 1.0f) || !isfinite(rope_base)) return SALS_ERR_RANGE;
+  if (misaligned(q) || misaligned(Lk) || misaligned(Lv) || misaligned(Pk) || misaligned(Pv) ||
+      misaligned(out) || misaligned(sel_out) || misaligned(ws))
+    return SALS_ERR_ALIGN;
+  if (!ws || ws_bytes < p.total) return SALS_ERR_WORKSPACE;
+  if ((st = device_ready()) != SALS_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* qt = (float*)(w + p.off_qt);
+  float* qpart = (float*)(w + p.off_qpart);
+  float* S = (float*)(w + p.off_S);
+  int32_t* selb = sel_out ? sel_out : (int32_t*)(w + p.off_sel);
+  float* part = (float*)(w + p.off_part);
+  const int G = sel->G;
+  hipError_t e = hipSuccess;
+  auto mark = [&](int i) {
+    if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], hs);
+  };
+  const bool score = p.kp > 0 && p.kp < p.Tc;
+  mark(0);
+  if (score && e == hipSuccess)
+    e = sals::launch_latent_query(s->dtype, q, Pk, qpart, qt, s->B, s->H_q, s->H_kv, s->d, s->r, G,
+                                  p.rps, hs);
+  mark(1);
+  if (score && e == hipSuccess)
+    e = sals::launch_latent_score(s->dtype, qt, Lk, S, s->B, G, s->r, p.Tc, ctx_cap, hs);
+  mark(2);
+  if (e == hipSuccess)
+    e = sals::launch_topk_window(S, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel, hs);
+  mark(3);
+  if (e == hipSuccess)
+    e = sals::launch_select_attend(s->dtype, q, Lk, Lv, Pk, Pv, selb, out, part, s->B, s->H_q,
+                                   s->H_kv, s->d, s->r, G, ctx_cap, ctx, p.n_sel, p.split_len,
+                                   p.n_splits, rope_base, hs);
+  mark(4);
+  if (e == hipSuccess && p.n_splits > 1)
+    e = sals::launch_combine(part, out, s->B * s->H_q, s->d, p.n_splits, hs);
+  mark(5);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sals_abi_version(void) { return SALS_ABI_VERSION; }
+
+const char* sals_status_string(sals_status status) {
+  switch (status) {
+    case SALS_OK: return "SALS_OK";
+    case SALS_ERR_NULL: return "SALS_ERR_NULL: a required pointer is NULL";
+    case SALS_ERR_SHAPE: return "SALS_ERR_SHAPE: unsupported or inconsistent shape";
+    case SALS_ERR_DTYPE: return "SALS_ERR_DTYPE: unknown element type";
+    case SALS_ERR_RANGE: return "SALS_ERR_RANGE: length or index out of range";
+    case SALS_ERR_WORKSPACE: return "SALS_ERR_WORKSPACE: workspace missing or too small";
+    case SALS_ERR_ALIGN: return "SALS_ERR_ALIGN: pointer not 16-byte aligned";
+    case SALS_ERR_HIP: return "SALS_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "unknown sals_status";
+}
+
+int32_t sals_last_hip_error(void) { return g_last_hip_error; }
+
+sals_status sals_project_kv(const sals_shape* s, const void* Xk, const void* Xv, const void* Pk,
+                            const void* Pv, void* Lk, void* Lv, int32_t ctx_cap, int32_t t0,
+                            int32_t T, sals_stream_t stream) {
+  if (!s || !Xk || !Pk || !Lk) return SALS_ERR_NULL;
+  const bool with_v = Xv != nullptr;
+  if (with_v != (Pv != nullptr) || with_v != (Lv != nullptr)) return SALS_ERR_NULL;
+  sals_status st = check_layer_shape(s);
+  if (st != SALS_OK) return st;
+  if (T < 1 || t0 < 0 || ctx_cap < 1 || (long)t0 + T > ctx_cap || T > (1 << 26)) return SALS_ERR_RANGE;
+  if (misaligned(Xk) || misaligned(Xv) || misaligned(Pk) || misaligned(Pv) || misaligned(Lk) ||
+      misaligned(Lv))
+    return SALS_ERR_ALIGN;
+  if ((st = device_ready()) != SALS_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  const int D = s->H_kv * s->d;
+  hipError_t e = sals::launch_project(s->dtype, Xk, Pk, Lk, s->B, T, D, s->r, ctx_cap, t0, hs);
+  if (e == hipSuccess && with_v)
+    e = sals::launch_project(s->dtype, Xv, Pv, Lv, s->B, T, D, s->r, ctx_cap, t0, hs);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
+sals_status sals_decode_workspace_bytes(const sals_shape* s, const sals_select* sel, int32_t ctx,
+                                        size_t* bytes) {
+  if (!bytes) return SALS_ERR_NULL;
+  DecodePlan p;
+  sals_status st = make_decode_plan(s, sel, ctx, &p);
+  if (st != SALS_OK) return st;
+  *bytes = p.total;
+  return SALS_OK;
+}
+
+sals_status sals_decode_step(const sals_shape* s, const sals_select* sel, float rope_base,
+                             const void* q, const void* Lk, const void* Lv, const void* Pk,
+                             const void* Pv, int32_t ctx_cap, int32_t ctx, float* out,
+                             int32_t* sel_out, void* ws, size_t ws_bytes, sals_stream_t stream) {
+  return decode_impl(s, sel, rope_base, q, Lk, Lv, Pk, Pv, ctx_cap, ctx, out, sel_out, ws,
+                     ws_bytes, stream, nullptr);
+}
+
+sals_status sals_decode_step_traced(const sals_shape* s, const sals_select* sel, float rope_base,
+                                    const void* q, const void* Lk, const void* Lv, const void* Pk,
+                                    const void* Pv, int32_t ctx_cap, int32_t ctx, float* out,
+                                    int32_t* sel_out, void* ws, size_t ws_bytes,
+                                    sals_stream_t stream, void* const* events, int32_t n_events) {
+  if (!events) return SALS_ERR_NULL;
+  if (n_events < 6) return SALS_ERR_RANGE;
+  for (int i = 0; i < 6; ++i)
+    if (!events[i]) return SALS_ERR_NULL;
+  return decode_impl(s, sel, rope_base, q, Lk, Lv, Pk, Pv, ctx_cap, ctx, out, sel_out, ws,
+                     ws_bytes, stream, events);
+}
+
+sals_status kv_compact_workspace_bytes(const kvc_shape* c, int32_t ctx, int32_t w, int32_t k_keep,
+                                       size_t* bytes) {
+  if (!bytes) return SALS_ERR_NULL;
+  CompactPlan p;
+  sals_status st = make_compact_plan(c, ctx, w, k_keep, &p);
+  if (st != SALS_OK) return st;
+  *bytes = p.total;
+  return SALS_OK;
+}
+
+sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const void* Qobs,
+                       int32_t w, int32_t ctx_cap, int32_t ctx, int32_t k_keep, void* Kc, void* Vc,
+                       int32_t* kept, float* importance, void* ws, size_t ws_bytes,
+                       sals_stream_t stream) {
+  if (!c || !K || !V || !Qobs || !Kc || !Vc || !kept) return SALS_ERR_NULL;
+  CompactPlan p;
+  sals_status st = make_compact_plan(c, ctx, w, k_keep, &p);
+  if (st != SALS_OK) return st;
+  if (ctx > ctx_cap) return SALS_ERR_RANGE;
+  if (misaligned(K) || misaligned(V) || misaligned(Qobs) || misaligned(Kc) || misaligned(Vc) ||
+      misaligned(kept) || misaligned(importance) || misaligned(ws))
+    return SALS_ERR_ALIGN;
+  if (!ws || ws_bytes < p.total) return SALS_ERR_WORKSPACE;
+  if ((st = device_ready()) != SALS_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  float* stats = (float*)((char*)ws + p.off_stats);
+  float* I = importance ? importance : (float*)((char*)ws + p.off_I);
+  hipError_t e = sals::launch_importance_stats(c->dtype, K, Qobs, stats, c->B, c->H_q, c->H_kv,
+                                               c->d, w, ctx_cap, ctx, hs);
+  if (e == hipSuccess)
+    e = sals::launch_importance_accum(c->dtype, K, Qobs, stats, I, c->B, c->H_q, c->H_kv, c->d, w,
+                                      ctx_cap, ctx, hs);
+  if (e == hipSuccess)
+    e = sals::launch_topk_window(I, kept, c->B * c->H_kv, ctx, k_keep, ctx, k_keep, hs);
+  if (e == hipSuccess)
+    e = sals::launch_gather_rows(c->dtype, K, V, kept, Kc, Vc, c->B * c->H_kv, c->d, ctx_cap,
+                                 k_keep, hs);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
+sals_status sals_dense_decode_workspace_bytes(const kvc_shape* c, int32_t n, size_t* bytes) {
+  if (!bytes) return SALS_ERR_NULL;
+  DensePlan p;
+  sals_status st = make_dense_plan(c, n, &p);
+  if (st != SALS_OK) return st;
+  *bytes = p.total;
+  return SALS_OK;
+}
+
+sals_status sals_dense_decode(const kvc_shape* c, const void* q, const void* K, const void* V,
+                              int32_t n, int32_t stride_tokens, float* out, void* ws,
+                              size_t ws_bytes, sals_stream_t stream) {
+  if (!c || !q || !K || !V || !out) return SALS_ERR_NULL;
+  DensePlan p;
+  sals_status st = make_dense_plan(c, n, &p);
+  if (st != SALS_OK) return st;
+  if (stride_tokens < n) return SALS_ERR_RANGE;
+  if (misaligned(q) || misaligned(K) || misaligned(V) || misaligned(out) || misaligned(ws))
+    return SALS_ERR_ALIGN;
+  if (p.total > 0 && (!ws || ws_bytes < p.total)) return SALS_ERR_WORKSPACE;
+  if ((st = device_ready()) != SALS_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  float* part = (float*)ws;
+  hipError_t e = sals::launch_dense_decode(c->dtype, q, K, V, out, part, c->B, c->H_q, c->H_kv,
+                                           c->d, n, stride_tokens, p.split_len, p.n_splits, hs);
+  if (e == hipSuccess && p.n_splits > 1)
+    e = sals::launch_combine(part, out, c->B * c->H_q, c->d, p.n_splits, hs);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
+}  // extern "C"

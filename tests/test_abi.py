@@ -1,0 +1,163 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and rejects bad
+arguments with the documented status before touching HIP (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_compression_sals_amd._lib import KvcShape, SalsSelect, SalsShape, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sals.h")
+
+OK, NULL, SHAPE, DTYPE, RANGE, WORKSPACE, ALIGN, HIP = range(8)
+P = 0x10000  # an aligned, never dereferenced stand-in pointer
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"^(?:sals_status|int32_t|const char\*)\s+(\w+)\(", src, flags=re.M)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 11, names
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.sals_abi_version() == 1
+
+
+def test_status_strings():
+    L = lib()
+    for code in range(8):
+        assert L.sals_status_string(code)
+    assert b"unknown" in L.sals_status_string(99)
+
+
+def _shape(**kw):
+    base = dict(B=2, H_q=8, H_kv=4, d=128, r=256, dtype=1)
+    base.update(kw)
+    return SalsShape(**base)
+
+
+def _ws_bytes(s, sel, ctx):
+    n = ctypes.c_size_t(0)
+    st = lib().sals_decode_workspace_bytes(ctypes.byref(s), ctypes.byref(sel), ctx, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), OK),
+    (dict(dtype=7), DTYPE),
+    (dict(d=96), SHAPE),
+    (dict(H_q=6, H_kv=4), SHAPE),
+    (dict(H_q=32, H_kv=2), SHAPE),  # more than 8 query heads per KV head
+    (dict(r=48), SHAPE),
+    (dict(r=1024), SHAPE),
+    (dict(r=512, dtype=0), SHAPE),  # fp32 slice of P would not fit on chip
+    (dict(B=0), SHAPE),
+])
+def test_decode_workspace_shape_checks(kw, want):
+    st, n = _ws_bytes(_shape(**kw), SalsSelect(16, 4, 2), 100)
+    assert st == want
+    if want == OK:
+        assert n > 0
+
+
+@pytest.mark.parametrize("sel,ctx,want", [
+    ((16, 4, 3), 100, SHAPE),   # H_kv % G != 0
+    ((16, 4, 0), 100, SHAPE),
+    ((-1, 4, 2), 100, RANGE),
+    ((16, -1, 2), 100, RANGE),
+    ((16, 4, 2), 0, RANGE),
+    ((0, 0, 1), 1, OK),
+])
+def test_decode_select_checks(sel, ctx, want):
+    assert _ws_bytes(_shape(), SalsSelect(*sel), ctx)[0] == want
+
+
+def _step(s=None, sel=None, base=10000.0, ptrs=None, cap=100, ctx=100, ws=P, ws_bytes=1 << 30, sel_out=None):
+    s = s or _shape()
+    sel = sel or SalsSelect(16, 4, 2)
+    p = dict(q=P, Lk=P, Lv=P, Pk=P, Pv=P, out=P)
+    p.update(ptrs or {})
+    return lib().sals_decode_step(ctypes.byref(s), ctypes.byref(sel), ctypes.c_float(base), p["q"], p["Lk"],
+                                  p["Lv"], p["Pk"], p["Pv"], cap, ctx, p["out"], sel_out, ws, ws_bytes, None)
+
+
+def test_decode_step_argument_errors():
+    assert _step(ptrs=dict(q=None)) == NULL
+    assert _step(ptrs=dict(out=None)) == NULL
+    assert _step(ptrs=dict(Lk=P + 8)) == ALIGN
+    assert _step(sel_out=P + 4) == ALIGN
+    assert _step(cap=99) == RANGE
+    assert _step(base=1.0) == RANGE
+    assert _step(base=float("nan")) == RANGE
+    assert _step(ws=None) == WORKSPACE
+    need = _ws_bytes(_shape(), SalsSelect(16, 4, 2), 100)[1]
+    assert _step(ws_bytes=need - 1) == WORKSPACE
+    assert _step(s=_shape(dtype=5)) == DTYPE
+
+
+def test_project_argument_errors():
+    L = lib()
+    s = _shape()
+
+    def call(Xk=P, Xv=P, Pk=P, Pv=P, Lk=P, Lv=P, cap=10, t0=0, T=10):
+        return L.sals_project_kv(ctypes.byref(s), Xk, Xv, Pk, Pv, Lk, Lv, cap, t0, T, None)
+
+    assert call(Xk=None) == NULL
+    assert call(Xv=None) == NULL  # V pointers must be all NULL or all set
+    assert call(T=0) == RANGE
+    assert call(t0=5, T=6) == RANGE
+    assert call(Pk=P + 2) == ALIGN
+
+
+def test_compact_argument_errors():
+    L = lib()
+    c = KvcShape(2, 4, 4, 128, 1)
+
+    def ws(ctx=100, w=8, k_keep=10, cc=c):
+        n = ctypes.c_size_t(0)
+        return L.kv_compact_workspace_bytes(ctypes.byref(cc), ctx, w, k_keep, ctypes.byref(n)), n.value
+
+    assert ws()[0] == OK and ws()[1] > 0
+    assert ws(w=0)[0] == RANGE
+    assert ws(w=101)[0] == RANGE
+    assert ws(k_keep=0)[0] == RANGE
+    assert ws(k_keep=101)[0] == RANGE
+    assert ws(cc=KvcShape(2, 4, 3, 128, 1))[0] == SHAPE
+    assert ws(cc=KvcShape(2, 4, 4, 128, 9))[0] == DTYPE
+
+    def call(K=P, Qobs=P, cap=100, ctx=100, wsp=P, wsb=1 << 30, imp=None):
+        return L.kv_compact(ctypes.byref(c), K, P, Qobs, 8, cap, ctx, 10, P, P, P, imp, wsp, wsb, None)
+
+    assert call(K=None) == NULL
+    assert call(cap=50) == RANGE
+    assert call(imp=P + 4) == ALIGN
+    assert call(wsb=16) == WORKSPACE
+
+
+def test_dense_decode_argument_errors():
+    L = lib()
+    c = KvcShape(2, 8, 4, 64, 1)
+    assert L.sals_dense_decode(ctypes.byref(c), P, P, None, 10, 10, P, P, 1 << 20, None) == NULL
+    assert L.sals_dense_decode(ctypes.byref(c), P, P, P, 11, 10, P, P, 1 << 20, None) == RANGE
+    assert L.sals_dense_decode(ctypes.byref(c), P, P, P, 0, 10, P, P, 1 << 20, None) == RANGE
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:  # noqa: BLE001
+        return False
+
+
+@pytest.mark.skipif(_gpu_present(), reason="stand-in pointers must never reach a real GPU")
+def test_valid_call_without_device_reports_hip_error():
+    assert _step() == HIP
+    assert lib().sals_last_hip_error() != 0

@@ -1,0 +1,127 @@
+"""GPU parity of sals_decode_step (through the C ABI) against the oracle."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - the GPU tests run on an MI355X
+    pytest.skip("no GPU", allow_module_level=True)
+
+import kv_cache_compression_sals_amd as sals  # noqa: E402
+from parity import decode_parity, to_device  # noqa: E402
+from workloads import CONFIGS, decode_case  # noqa: E402
+
+C1, C2, C3, C5 = CONFIGS["c1"], CONFIGS["c2"], CONFIGS["c3"], CONFIGS["c5"]
+
+
+def run_gpu(case):
+    dt = case["dtype"]
+    q, Lk, Lv = (to_device(case[n], dt) for n in ("q", "Lk", "Lv"))
+    Pk, Pv = to_device(case["Pk"], dt), to_device(case["Pv"], dt)
+    out, sel = sals.sals_decode_step(q, Lk, Lv, Pk, Pv, ctx=case["ctx"], k=case["k"], w=case["w"],
+                                     G=case["G"], rope_base=case["base"], want_sel=True)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), sel.cpu().numpy()
+
+
+def check(case, batches=None):
+    print(f"case {case['cfg'].name} B={case['B']} ctx={case['ctx']} cap={case['ctx_cap']} "
+          f"k={case['k']} w={case['w']} G={case['G']} r={case['r']} d={case['d']}", flush=True)
+    out, sel = run_gpu(case)
+    stats = decode_parity(case, out, sel, batches=batches)
+    print("  ", stats, flush=True)
+    return out, sel
+
+
+def test_c1_tiny_fp32_full():
+    check(decode_case(C1))
+
+
+SMALL = [
+    # name, base cfg, overrides, B, ctx, ctx_cap
+    ("c3_shape_ragged", C3, dict(calib_tokens=512), 2, 3001, 3100),
+    ("c2_shape_ragged", C2, dict(calib_tokens=1024), 2, 1500, 1500),
+    ("gqa_g2_d64", C3, dict(H_q=16, H_kv=8, d=64, r=128, G=2, k=50, w=8, rank=48, calib_tokens=512), 2, 777, 800),
+    ("nqh8_r64", C3, dict(H_q=16, H_kv=2, d=128, r=64, G=1, k=40, w=8, rank=32, calib_tokens=256), 1, 500, 512),
+    ("r32_g4", C3, dict(H_q=4, H_kv=4, d=64, r=32, G=4, k=20, w=4, rank=16, calib_tokens=256), 2, 300, 300),
+    ("nqh2_r384", C3, dict(H_q=8, H_kv=4, d=128, r=384, G=4, k=100, w=16, rank=200, calib_tokens=512), 1, 1200, 1200),
+    ("f32_d128_r256", C1, dict(H_q=8, H_kv=2, d=128, r=256, G=2, k=90, w=10, rank=64), 2, 700, 720),
+    ("f32_gqa_d64_r128", C1, dict(H_q=8, H_kv=4, d=64, r=128, G=1, k=33, w=7, rank=40), 1, 413, 413),
+    ("bf16_long_split", C3, dict(H_q=8, H_kv=2, r=256, G=2, k=1500, w=64, calib_tokens=512, rank=100), 1, 5000, 5000),
+]
+
+
+@pytest.mark.parametrize("name,cfg,ov,B,ctx,cap", SMALL, ids=[s[0] for s in SMALL])
+def test_small_shapes(name, cfg, ov, B, ctx, cap):
+    check(decode_case(cfg.with_(**ov), B=B, ctx=ctx, ctx_cap=cap))
+
+
+EDGES = [
+    ("w_ge_ctx", dict(k=10, w=64), 40),
+    ("k_zero", dict(k=0, w=16), 300),
+    ("k_plus_w_ge_ctx", dict(k=200, w=16), 150),
+    ("ctx_one", dict(k=8, w=4), 1),
+    ("no_window", dict(k=25, w=0), 200),
+    ("k_one", dict(k=1, w=0), 333),
+]
+
+
+@pytest.mark.parametrize("name,ov,ctx", EDGES, ids=[e[0] for e in EDGES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_edge_cases(name, ov, ctx, dtype):
+    base = C1 if dtype == "f32" else C3.with_(H_q=8, H_kv=4, r=64, G=2, rank=32, calib_tokens=256)
+    check(decode_case(base.with_(**ov), B=2, ctx=ctx, ctx_cap=ctx + 5))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_exact_ties_lowest_index(dtype):
+    """Latent rows drawn from 4 prototypes: scores take 4 values with massive exact ties; the
+    selected set must equal the oracle's exactly (lowest indices among the threshold ties)."""
+    base = C1 if dtype == "f32" else C3.with_(H_q=8, H_kv=4, r=64, G=2, rank=32, calib_tokens=256)
+    case = decode_case(base.with_(k=37, w=5), B=2, ctx=400)
+    rs = np.random.default_rng(5)
+    for name in ("Lk", "Lv"):
+        L = case[name]
+        proto = L[:, :4].copy()
+        pick = rs.integers(0, 4, size=L.shape[1])
+        case[name] = np.ascontiguousarray(proto[:, pick])
+    out, sel = run_gpu(case)
+    import oracle
+    ora = oracle.decode_step(case["q"], case["Lk"], case["Lv"], case["Pk"], case["Pv"], ctx=400, k=37, w=5,
+                             G=case["G"], H_kv=case["H_kv"], base=case["base"], dtype=dtype)
+    assert np.array_equal(sel, ora["sel"])
+    decode_parity(case, out, sel)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_query_all_ties(dtype):
+    """q = 0: every score is +-0, so the selection is the lowest k positions plus the window."""
+    base = C1 if dtype == "f32" else C3.with_(H_q=8, H_kv=4, r=64, G=2, rank=32, calib_tokens=256)
+    case = decode_case(base.with_(k=20, w=6), B=1, ctx=250)
+    case["q"] = np.zeros_like(case["q"])
+    out, sel = run_gpu(case)
+    want = np.concatenate([np.arange(20), np.arange(244, 250)])
+    assert all(np.array_equal(sel[0, s], want) for s in range(case["G"]))
+    decode_parity(case, out, sel)
+
+
+def test_determinism_bitwise():
+    case = decode_case(C3.with_(calib_tokens=512), B=2, ctx=2500)
+    a = run_gpu(case)
+    b = run_gpu(case)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_c2_full_size():
+    check(decode_case(C2), batches=[0, 7])
+
+
+def test_c3_full_size():
+    check(decode_case(C3), batches=[0, 3])
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_c5_full_context_layer(layer):
+    check(decode_case(C5, layer=layer))

@@ -226,7 +226,7 @@ def decode_case(cfg: DecodeConfig, layer: int = 0, B: Optional[int] = None, ctx:
         out["L" + which] = L
         if with_x:
             out["X" + which] = np.stack(xs)
-    q = rng(cfg.cfg_id, layer, "q").standard_normal((cfg.B, cfg.H_q, cfg.d), dtype=np.float32)[:B]
+    q = rng(cfg.cfg_id, layer, "q").standard_normal((max(B, cfg.B), cfg.H_q, cfg.d), dtype=np.float32)[:B]
     out["q"] = _store(q, cfg.dtype)
     return out
 
@@ -295,8 +295,9 @@ def compact_case(cfg: CompactConfig, B: Optional[int] = None, ctx: Optional[int]
     else:
         for b in range(B):
             one(b)
-    Qobs = rng(cfg.cfg_id, 0, "Qobs").standard_normal((cfg.B, cfg.H_q, cfg.w, cfg.d), dtype=np.float32)[:B]
-    q = rng(cfg.cfg_id, 0, "q_dec").standard_normal((cfg.B, cfg.H_q, cfg.d), dtype=np.float32)[:B]
+    nb = max(B, cfg.B)
+    Qobs = rng(cfg.cfg_id, 0, "Qobs").standard_normal((nb, cfg.H_q, cfg.w, cfg.d), dtype=np.float32)[:B]
+    q = rng(cfg.cfg_id, 0, "q_dec").standard_normal((nb, cfg.H_q, cfg.d), dtype=np.float32)[:B]
     return dict(cfg=cfg, B=B, ctx=ctx, ctx_cap=ctx_cap, H_q=cfg.H_q, H_kv=cfg.H_kv, d=cfg.d, w=cfg.w,
                 k_keep=int(np.floor(cfg.keep_frac * ctx)), dtype=cfg.dtype, K=K, V=V,
                 Qobs=f32_to_bf16_bits(Qobs), q=f32_to_bf16_bits(q))
