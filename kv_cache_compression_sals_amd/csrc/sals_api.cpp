@@ -242,7 +242,9 @@ sals_status sals_project_kv(const sals_shape* s, const void* Xk, const void* Xv,
   if (!s || !Xk || !Pk || !Lk) return SALS_ERR_NULL;
   const bool with_v = Xv != nullptr;
   if (with_v != (Pv != nullptr) || with_v != (Lv != nullptr)) return SALS_ERR_NULL;
-  sals_status st = check_layer_shape(s);
+  sals_shape sk = *s;  // the projection does not involve query heads
+  sk.H_q = sk.H_kv;
+  sals_status st = check_layer_shape(&sk);
   if (st != SALS_OK) return st;
   if (T < 1 || t0 < 0 || ctx_cap < 1 || (long)t0 + T > ctx_cap || T > (1 << 26)) return SALS_ERR_RANGE;
   if (misaligned(Xk) || misaligned(Xv) || misaligned(Pk) || misaligned(Pv) || misaligned(Lk) ||
