@@ -28,6 +28,10 @@ SOURCES = [
     "kernels/latent_score.hip",
     "kernels/topk.hip",
     "kernels/select_attend.hip",
+    "kernels/select_attend_bf16_d128.hip",
+    "kernels/select_attend_bf16_d64.hip",
+    "kernels/select_attend_f32_d128.hip",
+    "kernels/select_attend_f32_d64.hip",
     "kernels/project.hip",
     "kernels/compact.hip",
 ]

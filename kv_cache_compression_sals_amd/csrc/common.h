@@ -73,6 +73,30 @@ __device__ __forceinline__ bf16x8_t frag_at<BF16>(const u32x4* ch, int kb) {
   return __builtin_bit_cast(bf16x8_t, ch[kb]);
 }
 
+// Natural k layout for 16x16 MFMA operands read in 16-byte chunks: the contraction is cut into
+// windows of 4 chunks; lane group q = lane/16 holds chunk q of every window, so one load
+// instruction of a wave covers 64 contiguous bytes of each of its 16 rows. A window spans KW
+// MFMA steps (bf16: 1 step of k=32; fp32: 4 steps of k=4, one chunk element per step).
+template <class T>
+struct Win {
+  static constexpr int EPC = 16 / (int)sizeof(typename T::elem);  // elements per chunk
+  static constexpr int WLEN = 4 * EPC;                             // elements per window
+  static constexpr int KW = WLEN / T::KSTEP;                       // MFMA steps per window
+};
+
+template <class T>
+__device__ __forceinline__ typename T::frag chunk_frag(const u32x4& ch, int s);
+
+template <>
+__device__ __forceinline__ float chunk_frag<F32>(const u32x4& ch, int s) {
+  return __uint_as_float(ch[s]);
+}
+
+template <>
+__device__ __forceinline__ bf16x8_t chunk_frag<BF16>(const u32x4& ch, int) {
+  return __builtin_bit_cast(bf16x8_t, ch);
+}
+
 // Order-preserving uint32 key of a float: larger float -> larger key; -0.0 and +0.0 map to the
 // same key. Inputs are finite.
 __device__ __forceinline__ uint32_t float_key(float x) {

@@ -58,6 +58,7 @@ __global__ __launch_bounds__(kThreads) void lq_partial_kernel(
   for (int b0 = 0; b0 < B; b0 += kBC) {
     const int nb = min(kBC, B - b0);
     __syncthreads();
+#pragma unroll 8
     for (int e = tid; e < nb * rps; e += kThreads) {
       const int bb = e / rps, i = e % rps;
       const int row = row0 + i, g = row / d, c = row % d;
@@ -73,6 +74,7 @@ __global__ __launch_bounds__(kThreads) void lq_partial_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[bb][j] = 0.f;
     if (col_ok) {
+#pragma unroll 8
       for (int i = rp; i < rps; i += 32) {
         float p[8];
         load8<T>(Pk + (size_t)(row0 + i) * r + col0, p);

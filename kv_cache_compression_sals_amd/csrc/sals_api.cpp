@@ -19,7 +19,7 @@ bool misaligned(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) != 
 
 int elem_size(int dtype) { return dtype == SALS_F32 ? 4 : 2; }
 
-bool rank_supported(int r) { return r == 32 || (r >= 64 && r <= 512 && r % 64 == 0); }
+bool rank_supported(int r) { return r == 32 || r == 64 || r == 128 || r == 256 || r == 384 || r == 512; }
 
 sals_status check_layer_shape(const sals_shape* s) {
   if (s->dtype != SALS_F32 && s->dtype != SALS_BF16) return SALS_ERR_DTYPE;

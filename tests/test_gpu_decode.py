@@ -95,14 +95,15 @@ def test_exact_ties_lowest_index(dtype):
     decode_parity(case, out, sel)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_zero_query_all_ties(dtype):
-    """q = 0: every score is +-0, so the selection is the lowest k positions plus the window."""
+@pytest.mark.parametrize("dtype,ctx", [("f32", 250), ("bf16", 250), ("bf16", 6000), ("bf16", 40000)])
+def test_zero_query_all_ties(dtype, ctx):
+    """q = 0: every score is +-0, so the selection is the lowest k positions plus the window.
+    ctx 6000 ties more candidates than the short list holds; ctx 40000 exceeds the on-chip row."""
     base = C1 if dtype == "f32" else C3.with_(H_q=8, H_kv=4, r=64, G=2, rank=32, calib_tokens=256)
-    case = decode_case(base.with_(k=20, w=6), B=1, ctx=250)
+    case = decode_case(base.with_(k=20, w=6), B=1, ctx=ctx)
     case["q"] = np.zeros_like(case["q"])
     out, sel = run_gpu(case)
-    want = np.concatenate([np.arange(20), np.arange(244, 250)])
+    want = np.concatenate([np.arange(20), np.arange(ctx - 6, ctx)])
     assert all(np.array_equal(sel[0, s], want) for s in range(case["G"]))
     decode_parity(case, out, sel)
 
@@ -125,3 +126,32 @@ def test_c3_full_size():
 @pytest.mark.parametrize("layer", [0, 31])
 def test_c5_full_context_layer(layer):
     check(decode_case(C5, layer=layer))
+
+
+def test_graph_capture_replays_match_eager():
+    """A captured decode step, replayed several times with eager work and synchronisations in
+    between, reproduces the eager result bit for bit on every replay."""
+    case = decode_case(C3.with_(calib_tokens=512), B=2, ctx=3000)
+    dt = case["dtype"]
+    q, Lk, Lv, Pk, Pv = (to_device(case[n], dt) for n in ("q", "Lk", "Lv", "Pk", "Pv"))
+    kw = dict(ctx=case["ctx"], k=case["k"], w=case["w"], G=case["G"], rope_base=case["base"])
+    ref, ref_sel = sals.sals_decode_step(q, Lk, Lv, Pk, Pv, want_sel=True, **kw)
+    torch.cuda.synchronize()
+    ws = torch.empty(sals.sals_decode_workspace_bytes(q, Pk, ctx=case["ctx"], k=case["k"], w=case["w"],
+                                                      G=case["G"]), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(ref)
+    sel = torch.empty_like(ref_sel)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sals.sals_decode_step(q, Lk, Lv, Pk, Pv, out=out, sel_out=sel, workspace=ws, **kw)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        sel.fill_(-1)
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(sel, ref_sel), rep
+        # eager work between replays
+        sals.sals_decode_step(q, Lk, Lv, Pk, Pv, **kw)
+        torch.cuda.synchronize()
