@@ -59,7 +59,7 @@ typedef enum { SALS_F32 = 0, SALS_BF16 = 1 } sals_dtype;
  *   B      sequences (one new token each per decode step)
  *   H_q    query heads; H_kv KV heads, H_q % H_kv == 0, H_q / H_kv <= 8
  *   d      head dimension, 64 or 128
- *   r      latent rank: 32 or a multiple of 64 up to 512, with d * r * elemsize <= 128 KiB
+ *   r      latent rank: 32, 64, 128, 256, 384 or 512, with d * r * elemsize <= 128 KiB
  *   dtype  element type of q, X, P and L (fp32 accumulation throughout) */
 typedef struct {
     int32_t B, H_q, H_kv, d, r;

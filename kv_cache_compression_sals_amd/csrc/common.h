@@ -128,4 +128,26 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Element-wise copy with up to U loads in flight per thread: all U loads of a batch are issued
+// before any of them is consumed. A plain loop of (load, store) waits out the full memory
+// latency once per element, which dominates short kernels.
+template <int U, class LoadF, class StoreF>
+__device__ __forceinline__ void batched_copy(int n, int tid, int nthreads, LoadF load, StoreF store) {
+  for (int base = tid; base < n; base += U * nthreads) {
+    decltype(load(0)) v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * nthreads;
+      if (i < n) v[u] = load(i);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * nthreads;
+      if (i < n) store(i, v[u]);
+    }
+  }
+}
+
+
+
 }  // namespace sals

@@ -58,14 +58,16 @@ __global__ __launch_bounds__(kThreads) void lq_partial_kernel(
   for (int b0 = 0; b0 < B; b0 += kBC) {
     const int nb = min(kBC, B - b0);
     __syncthreads();
-#pragma unroll 8
-    for (int e = tid; e < nb * rps; e += kThreads) {
-      const int bb = e / rps, i = e % rps;
-      const int row = row0 + i, g = row / d, c = row % d;
-      const typename T::elem* qp = q + ((size_t)(b0 + bb) * H_q + (size_t)g * nqh) * d + c;
-      float s = 0.f;
-      for (int h = 0; h < nqh; ++h) s += T::to_f32(qp[(size_t)h * d]);
-      qsum[bb][i] = s;
+    // qsum[bb][i] = sum over the query heads of KV head g of q[b][h][c]: one load per head,
+    // batched so that many are in flight
+    for (int h = 0; h < nqh; ++h) {
+      batched_copy<8>(
+          nb * rps, tid, kThreads,
+          [&](int e) {
+            const int bb = e / rps, row = row0 + e % rps;
+            return T::to_f32(q[((size_t)(b0 + bb) * H_q + (size_t)(row / d) * nqh + h) * d + row % d]);
+          },
+          [&](int e, float v) { qsum[e / rps][e % rps] = (h == 0 ? 0.f : qsum[e / rps][e % rps]) + v; });
     }
     __syncthreads();
     float acc[kBC][8];
@@ -125,6 +127,7 @@ __global__ void lq_reduce_kernel(const float* __restrict__ qpart, float* __restr
   if (e >= B * G * r) return;
   const int j = e % r, s = (e / r) % G, b = e / (r * G);
   float v = 0.f;
+#pragma unroll 8
   for (int i = 0; i < splits_per_group; ++i)
     v += qpart[((size_t)(s * splits_per_group + i) * B + b) * r + j];
   qt[e] = v;

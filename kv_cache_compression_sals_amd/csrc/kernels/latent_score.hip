@@ -79,10 +79,10 @@ __global__ __launch_bounds__(256) void latent_score_kernel(const float* __restri
   const int n16 = lane & 15, q4 = lane >> 4;
   const int b = blockIdx.y, gb = blockIdx.z;
   const int ng = min(GPB, G - gb * GPB);
-  for (int e = tid; e < GPB * R; e += 256) {
-    const int g = e / R, c = e % R;
-    qsh[g][c] = g < ng ? qt[((size_t)b * G + gb * GPB + g) * R + c] : 0.f;
-  }
+  batched_copy<8>(
+      GPB * R, tid, 256,
+      [&](int e) { return e / R < ng ? qt[((size_t)b * G + gb * GPB + e / R) * R + e % R] : 0.f; },
+      [&](int e, float v) { qsh[e / R][e % R] = v; });
   const size_t brow = (size_t)b * ctx_cap;
   const int tile0 = blockIdx.x * (kWaves * kTilesPerWave) + wave;
   u32x4 c0[NW], c1[NW];

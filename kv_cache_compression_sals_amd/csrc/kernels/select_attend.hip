@@ -31,17 +31,53 @@ hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const 
 }
 
 // LSE merge: out[bh] = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}, M = max_s m_s.
-__global__ void combine_kernel(const float* __restrict__ part, float* __restrict__ out, int d,
-                               int n_splits) {
+// The split maxima are read in parallel, then the splits are merged in chunks of kChunk: each
+// chunk's weights e^{m_s - M} are staged in LDS and every thread sums its columns over the chunk
+// with independent loads.
+constexpr int kChunk = 1024;
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part,
+                                                      float* __restrict__ out, int d,
+                                                      int n_splits) {
+  __shared__ float wgt[kChunk];
+  __shared__ float red[2];
   const float* p = part + (size_t)blockIdx.x * n_splits * (d + 2);
+  const int tid = threadIdx.x;
   float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, p[(size_t)s * (d + 2)]);
-  float L = 0.f;
-  for (int s = 0; s < n_splits; ++s) L += p[(size_t)s * (d + 2) + 1] * expf(p[(size_t)s * (d + 2)] - M);
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    float o = 0.f;
-    for (int s = 0; s < n_splits; ++s) o += p[(size_t)s * (d + 2) + 2 + c] * expf(p[(size_t)s * (d + 2)] - M);
-    out[(size_t)blockIdx.x * d + c] = o / L;
+  for (int s = tid; s < n_splits; s += 128) M = fmaxf(M, p[(size_t)s * (d + 2)]);
+  M = wave_max(M);
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  __syncthreads();
+  float lsum = 0.f;
+  float o[2] = {0.f, 0.f};  // columns tid and tid + 128 (d <= 256)
+  for (int c0 = 0; c0 < n_splits; c0 += kChunk) {
+    const int nc = min(kChunk, n_splits - c0);
+    batched_copy<8>(nc, tid, 128, [&](int s) { return p[(size_t)(c0 + s) * (d + 2)]; },
+                    [&](int s, float m) { wgt[s] = expf(m - M); });
+    __syncthreads();
+    for (int s = tid; s < nc; s += 128) lsum += wgt[s] * p[(size_t)(c0 + s) * (d + 2) + 1];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = tid + 128 * h;
+      if (c < d) {
+        const float* col = p + (size_t)c0 * (d + 2) + 2 + c;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int s = 0; s < nc; ++s) acc += col[(size_t)s * (d + 2)] * wgt[s];
+        o[h] += acc;
+      }
+    }
+    __syncthreads();
+  }
+  lsum = wave_sum(lsum);
+  if ((tid & 63) == 0) red[tid >> 6] = lsum;
+  __syncthreads();
+  const float L = red[0] + red[1];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = tid + 128 * h;
+    if (c < d) out[(size_t)blockIdx.x * d + c] = o[h] / L;
   }
 }
 

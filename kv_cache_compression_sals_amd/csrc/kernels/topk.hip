@@ -82,7 +82,8 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
     return;
   }
   if constexpr (IN_LDS) {
-    for (int i = tid; i < Tc; i += kThreads) keys[i] = float_key(src[i]);
+    batched_copy<8>(Tc, tid, kThreads, [&](int i) { return src[i]; },
+                    [&](int i, float v) { keys[i] = float_key(v); });
   }
   auto key_at = [&](int i) -> uint32_t {
     if constexpr (IN_LDS) return keys[i];
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
   for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
   if (tid == 0) bcast[2] = 0;
   __syncthreads();
-  for (int i = tid; i < Tc; i += kThreads) atomicAdd(&hist[key_at(i) >> 21], 1u);
+  batched_copy<8>(Tc, tid, kThreads, key_at, [&](int, uint32_t k) { atomicAdd(&hist[k >> 21], 1u); });
   __syncthreads();
   uint32_t remaining = (uint32_t)kp;
   find_bin(hist, kBins, remaining, scan, bcast);
@@ -105,12 +106,12 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
   uint32_t prefix = bin1 << 21;
   if (n_in_bin <= (uint32_t)kCandMax) {
     // ---- gather the bin's keys, resolve bits [20:10] and [9:0] on the short list ----
-    for (int i = tid; i < Tc; i += kThreads) {
-      if ((key_at(i) >> 21) == bin1) {
+    batched_copy<8>(Tc, tid, kThreads, key_at, [&](int i, uint32_t k) {
+      if ((k >> 21) == bin1) {
         const uint32_t slot = atomicAdd(&bcast[2], 1u);
         cand[slot] = i;
       }
-    }
+    });
     __syncthreads();
     const int nc = (int)n_in_bin;
 #pragma unroll 1
@@ -139,10 +140,9 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
       const uint32_t pmask = pass == 0 ? 0xffe00000u : 0xfffffc00u;
       for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
       __syncthreads();
-      for (int i = tid; i < Tc; i += kThreads) {
-        const uint32_t k = key_at(i);
+      batched_copy<8>(Tc, tid, kThreads, key_at, [&](int, uint32_t k) {
         if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
-      }
+      });
       __syncthreads();
       find_bin(hist, kBins, remaining, scan, bcast);
       prefix |= bcast[0] << shift;
