@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     kv_compact_workspace_bytes,
     n_selected,
     sals_decode_step,
+    sals_decode_step_traced,
     sals_decode_workspace_bytes,
     sals_dense_decode,
     sals_dense_decode_workspace_bytes,

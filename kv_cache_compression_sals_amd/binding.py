@@ -123,6 +123,37 @@ def sals_decode_step(q: torch.Tensor, Lk: torch.Tensor, Lv: torch.Tensor, Pk: to
     return out, sel_out
 
 
+def sals_decode_step_traced(q: torch.Tensor, Lk: torch.Tensor, Lv: torch.Tensor, Pk: torch.Tensor,
+                            Pv: torch.Tensor, events, *, ctx: int, k: int, w: int, G: int,
+                            rope_base: float = 10000.0, out: Optional[torch.Tensor] = None,
+                            sel_out: Optional[torch.Tensor] = None, want_sel: bool = False,
+                            workspace: Optional[torch.Tensor] = None,
+                            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """sals_decode_step that also records six timing events on the launch stream at its stage
+    boundaries (before the latent query, the scoring, the top-k, rebuild + attention, the split
+    merge, and after the last kernel). events: six torch.cuda.Event(enable_timing=True), each
+    already recorded once so that its HIP event exists."""
+    if len(events) != 6:
+        raise ValueError("sals_decode_step_traced needs exactly 6 events")
+    dt = _dtype(q, Lk, Lv, Pk, Pv)
+    B, H_q, d = q.shape
+    s, sel = _decode_structs(q, Pk, Pk.shape[1], k, w, G, dt)
+    if out is None:
+        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+    if sel_out is None and want_sel:
+        sel_out = torch.empty((B, G, n_selected(ctx, k, w)), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = _ws(sals_decode_workspace_bytes(q, Pk, ctx=ctx, k=k, w=w, G=G), q.device, None)
+    handles = (ctypes.c_void_p * 6)(*[e.cuda_event for e in events])
+    if not all(handles):
+        raise ValueError("record each event once before passing it in")
+    _check("sals_decode_step_traced", lib().sals_decode_step_traced(
+        ctypes.byref(s), ctypes.byref(sel), ctypes.c_float(rope_base), _ptr(q), _ptr(Lk), _ptr(Lv),
+        _ptr(Pk), _ptr(Pv), Lk.shape[1], ctx, _ptr(out), _ptr(sel_out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream), handles, 6))
+    return out, sel_out
+
+
 # ---- compaction -----------------------------------------------------------------------------
 
 def kv_compact_workspace_bytes(K: torch.Tensor, Qobs: torch.Tensor, *, ctx: int, k_keep: int) -> int:

@@ -128,6 +128,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// The dispatcher deals the workgroups of a launch to the 8 XCDs in turn (workgroup L runs on XCD
+// L % 8), and every XCD has its own L2. xcd_remap turns the hardware index L into a logical
+// index such that each XCD receives one contiguous range of logical indices: workgroups that are
+// neighbours in logical order (and read the same rows) then share an L2. It is a bijection on
+// [0, N) for any N, so correctness never depends on the hardware's actual placement.
+constexpr int kXCDs = 8;
+__device__ __forceinline__ int xcd_remap(int L, int N) {
+  const int xcd = L % kXCDs, slot = L / kXCDs;
+  const int q = N / kXCDs, rmd = N % kXCDs;
+  return xcd < rmd ? xcd * (q + 1) + slot : rmd * (q + 1) + (xcd - rmd) * q + slot;
+}
+
 // Element-wise copy with up to U loads in flight per thread: all U loads of a batch are issued
 // before any of them is consumed. A plain loop of (load, store) waits out the full memory
 // latency once per element, which dominates short kernels.
@@ -140,6 +152,7 @@ __device__ __forceinline__ void batched_copy(int n, int tid, int nthreads, LoadF
       const int i = base + u * nthreads;
       if (i < n) v[u] = load(i);
     }
+    __builtin_amdgcn_sched_barrier(0);  // all loads of the batch before the first store
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = base + u * nthreads;

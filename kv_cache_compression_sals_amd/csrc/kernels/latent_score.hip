@@ -6,9 +6,9 @@
 // queries, split into bf16 high and low parts for a bf16 cache (8 groups per launch slice), so
 // the bf16 MFMA reproduces an fp32 dot product to ~2^-16 relative; for an fp32 cache the rows
 // are 16 groups and the fp32 MFMA is used. Latent rows are read in the natural k layout (each
-// load instruction covers 64 contiguous bytes of 16 consecutive rows); a wave walks 4 tiles and
-// loads the next tile while the current one is reduced. The workgroup stages the groups' queries
-// in LDS once and every wave builds its MFMA rows from there.
+// load instruction covers 64 contiguous bytes of 16 consecutive rows); a wave takes 2 or 4 tiles
+// (fewer when the cache is short, so that every CU gets work), loading two tiles at a time. The
+// workgroup stages the groups' queries in LDS once and every wave builds its MFMA rows there.
 #include "../common.h"
 #include "../launch.h"
 
@@ -16,8 +16,6 @@ namespace sals {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kTilesPerWave = 4;
-
 template <class T, int R>
 __device__ __forceinline__ void load_tile(const typename T::elem* __restrict__ Lk, size_t brow, int t,
                                           int q4, u32x4 (&ch)[R / Win<T>::WLEN]) {
@@ -64,9 +62,10 @@ __device__ __forceinline__ void score_tile(const u32x4 (&a)[R / Win<T>::WLEN],
   }
 }
 
-// grid (ceil(tiles / 16), B, group slices); block 256. Workgroup x covers tokens
-// [x*256, x*256 + 256); wave w takes tiles x*16 + w + 4*i, i < 4.
-template <class T, int R>
+// grid (ceil(tiles / (4 * TW)), B, group slices); block 256. Workgroup x covers tiles
+// [x*4*TW, (x+1)*4*TW); wave w takes tiles x*4*TW + w + 4*i, i < TW, two at a time: the loads of
+// both tiles of a pair are issued before either is reduced.
+template <class T, int R, int TW>
 __global__ __launch_bounds__(256) void latent_score_kernel(const float* __restrict__ qt,
                                                            const typename T::elem* __restrict__ Lk,
                                                            float* __restrict__ S, int G, int Tc,
@@ -74,19 +73,22 @@ __global__ __launch_bounds__(256) void latent_score_kernel(const float* __restri
   using W = Win<T>;
   constexpr int NW = R / W::WLEN;
   constexpr int GPB = T::HILO ? 8 : 16;
+  static_assert(TW % 2 == 0, "tiles are taken in pairs");
   __shared__ float qsh[GPB][R];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int b = blockIdx.y, gb = blockIdx.z;
   const int ng = min(GPB, G - gb * GPB);
+  const size_t brow = (size_t)b * ctx_cap;
+  const int tile0 = blockIdx.x * (kWaves * TW) + wave;
+  // the first pair's rows are requested before the query staging
+  u32x4 c0[NW], c1[NW];
+  load_tile<T, R>(Lk, brow, min(tile0 * 16 + n16, Tc - 1), q4, c0);
+  load_tile<T, R>(Lk, brow, min((tile0 + 4) * 16 + n16, Tc - 1), q4, c1);
   batched_copy<8>(
       GPB * R, tid, 256,
       [&](int e) { return e / R < ng ? qt[((size_t)b * G + gb * GPB + e / R) * R + e % R] : 0.f; },
       [&](int e, float v) { qsh[e / R][e % R] = v; });
-  const size_t brow = (size_t)b * ctx_cap;
-  const int tile0 = blockIdx.x * (kWaves * kTilesPerWave) + wave;
-  u32x4 c0[NW], c1[NW];
-  if (tile0 * 16 < Tc) load_tile<T, R>(Lk, brow, min(tile0 * 16 + n16, Tc - 1), q4, c0);
   __syncthreads();
   // MFMA A operand: row n16 of the 16 query rows, natural k layout
   u32x4 a[NW];
@@ -114,17 +116,17 @@ __global__ __launch_bounds__(256) void latent_score_kernel(const float* __restri
       }
     }
   }
-  if (tile0 * 16 >= Tc) return;
 #pragma unroll
-  for (int i = 0; i < kTilesPerWave; i += 2) {
+  for (int i = 0; i < TW; i += 2) {
     const int ta = tile0 + 4 * i, tb = ta + 4;
     if (ta * 16 >= Tc) break;
-    if (tb * 16 < Tc) load_tile<T, R>(Lk, brow, min(tb * 16 + n16, Tc - 1), q4, c1);
+    if (i > 0) {
+      load_tile<T, R>(Lk, brow, min(ta * 16 + n16, Tc - 1), q4, c0);
+      load_tile<T, R>(Lk, brow, min(tb * 16 + n16, Tc - 1), q4, c1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     score_tile<T, R>(a, c0, S, b, G, gb, Tc, ta * 16, lane);
-    if (tb * 16 >= Tc) break;
-    const int tc = tb + 4;
-    if (i + 2 < kTilesPerWave && tc * 16 < Tc) load_tile<T, R>(Lk, brow, min(tc * 16 + n16, Tc - 1), q4, c0);
-    score_tile<T, R>(a, c1, S, b, G, gb, Tc, tb * 16, lane);
+    if (tb * 16 < Tc) score_tile<T, R>(a, c1, S, b, G, gb, Tc, tb * 16, lane);
   }
 }
 
@@ -133,8 +135,16 @@ void launch_t(const float* qt, const void* Lk, float* S, int B, int G, int Tc, i
               hipStream_t st) {
   constexpr int GPB = T::HILO ? 8 : 16;
   const int tiles = ceil_div(Tc, 16);
-  dim3 grid(ceil_div(tiles, kWaves * kTilesPerWave), B, ceil_div(G, GPB));
-  latent_score_kernel<T, R><<<grid, 256, 0, st>>>(qt, (const typename T::elem*)Lk, S, G, Tc, ctx_cap);
+  const int slices = ceil_div(G, GPB);
+  // two tiles per wave unless that already gives the chip several workgroups per CU
+  const bool four = (long)ceil_div(tiles, kWaves * 4) * B * slices >= 256;
+  if (four) {
+    dim3 grid(ceil_div(tiles, kWaves * 4), B, slices);
+    latent_score_kernel<T, R, 4><<<grid, 256, 0, st>>>(qt, (const typename T::elem*)Lk, S, G, Tc, ctx_cap);
+  } else {
+    dim3 grid(ceil_div(tiles, kWaves * 2), B, slices);
+    latent_score_kernel<T, R, 2><<<grid, 256, 0, st>>>(qt, (const typename T::elem*)Lk, S, G, Tc, ctx_cap);
+  }
 }
 
 }  // namespace

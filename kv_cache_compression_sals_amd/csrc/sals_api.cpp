@@ -75,18 +75,9 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   p->Tc = ctx > sel->w ? ctx - sel->w : 0;
   p->kp = sel->k < p->Tc ? sel->k : p->Tc;
   p->n_sel = p->kp + (ctx - p->Tc);
-  // rows of P_k per latent-query workgroup: a whole group when it is at most 512 rows, else
-  // the largest whole number of KV heads that divides the group and stays within 512 rows
+  // rows of P_k per latent-query workgroup: one KV head
   const int group_rows = p->D / sel->G;
-  if (group_rows <= 512) {
-    p->rps = group_rows;
-  } else {
-    const int m = s->H_kv / sel->G;
-    int best = 1;
-    for (int h = 1; h <= m; ++h)
-      if (m % h == 0 && h * s->d <= 512) best = h;
-    p->rps = best * s->d;
-  }
+  p->rps = s->d;
   p->spg = group_rows / p->rps;
   const int max_split = sals::select_attend_max_split(s->dtype, s->d, s->r, p->nqh);
   if (max_split < 16) return SALS_ERR_SHAPE;
@@ -98,6 +89,7 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   if (split > max_split) split = max_split;
   p->split_len = split;
   p->n_splits = (p->n_sel + split - 1) / split;
+  if ((long)p->n_splits * s->H_kv * s->B > 0x7fffffffL) return SALS_ERR_RANGE;  // 1-D grid
   size_t off = 0;
   p->off_qt = off;
   off += align_up((size_t)s->B * sel->G * s->r * 4);
