@@ -12,13 +12,13 @@ GQA layer (B=4, 32/8 heads, ctx=32768, r=256, k=2048, w=128, G=8) is reported be
 
 Inputs are resident in HBM before timing starts. Several independent copies of each input set
 are rotated so that consecutive steps never find their inputs in the 256 MB Infinity Cache.
-W untimed eager steps run first. The timed region is exactly K eager steps, each issued through
-sals_decode_step_traced, which records HIP events on the launch stream at every stage boundary;
-the region is bracketed by device synchronisations and timed on the host clock (the value), and
-the events give every kernel's average duration over the same K steps. The same K steps are
-then captured as one HIP graph and replayed once untimed and once timed (graph_us_per_step:
-what a serving loop that captures its decode step sees). One JSON line goes to stdout; progress
-goes to stderr.
+W untimed eager steps run first. The K steps are then captured once as a HIP graph (as a serving
+loop runs its decode step), replayed once untimed (upload), and the timed region is exactly one
+replay of the K steps between two device synchronisations: that is the value. Right after it,
+the same K steps are issued eagerly through sals_decode_step_traced, which records HIP events on
+the launch stream at every stage boundary; the events give each kernel's average duration
+(stage_us, and the roofline's avg_launch_us), and the host clock around that pass gives
+eager_us_per_step. One JSON line goes to stdout; progress goes to stderr.
 
 --calib-copy-mib M first copies an M MiB buffer with torch (a plain copy kernel of known size),
 so that a counter run can scale FETCH_SIZE / WRITE_SIZE to bytes.
@@ -80,9 +80,13 @@ def stored_traffic(stage, label):
 
 
 def algorithmic(cfg, ctx):
-    """The method's own bytes and flops for one step (not the implementation's traffic)."""
+    """The method's own bytes and flops for one step (not the implementation's traffic).
+
+    Per stage: bytes = inputs read once + outputs written once; flops = the dense contractions
+    (the MFMA work). The value side of the attention is computed as (p^T L_v,sel) P_v^T, so its
+    flops are a weighted row sum plus one d x r product per query head, not a V rebuild."""
     s = 4 if cfg.dtype == "f32" else 2
-    B, G, r, d, D = cfg.B, cfg.G, cfg.r, cfg.d, cfg.H_kv * cfg.d
+    B, G, r, d, D, Hq, Hkv = cfg.B, cfg.G, cfg.r, cfg.d, cfg.H_kv * cfg.d, cfg.H_q, cfg.H_kv
     Tc = max(0, ctx - cfg.w)
     kp = min(cfg.k, Tc)
     n_sel = kp + (ctx - Tc)
@@ -90,14 +94,24 @@ def algorithmic(cfg, ctx):
     sel_rows = 2 * B * G * n_sel * r * s
     p_bytes = 2 * D * r * s
     scores = B * G * Tc * 4
+    k_rebuild = 2 * B * Hkv * n_sel * r * d
+    value_side = 2 * B * Hq * n_sel * r + 2 * B * Hq * d * r
+    logits = 2 * B * Hq * n_sel * d
     return dict(
         lk_read=lk_read, sel_rows=sel_rows, p_bytes=p_bytes, compulsory=lk_read + sel_rows + p_bytes,
-        recon_flops=4 * B * cfg.H_kv * n_sel * r * d, n_sel=n_sel, Tc=Tc,
+        k_rebuild_flops=k_rebuild, n_sel=n_sel, Tc=Tc,
         stage_bytes={
-            "latent_query": D * r * s + B * cfg.H_q * d * s + B * G * r * 4,
+            "latent_query": D * r * s + B * Hq * d * s + B * G * r * 4,
             "latent_score": lk_read + B * G * r * 4 + scores,
             "topk_window": scores + B * G * n_sel * 4,
-            "select_attend": sel_rows + p_bytes + B * G * n_sel * 4 + B * cfg.H_q * d * (s + 4),
+            "select_attend": sel_rows + p_bytes + B * G * n_sel * 4 + B * Hq * d * (s + 4),
+            "combine": 0,
+        },
+        stage_flops={
+            "latent_query": 2 * B * Hq * d * r,
+            "latent_score": 2 * B * G * Tc * r,
+            "topk_window": 0,
+            "select_attend": k_rebuild + value_side + logits,
             "combine": 0,
         },
     )
@@ -143,9 +157,21 @@ def run_workload(cfg, steps, warmup, label):
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps, events between the kernels on the launch stream ----
+    # ---- timed region: the K steps captured once as a graph, replayed between two syncs ----
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    us_step = (time.perf_counter() - t_start) / steps * 1e6
+
+    # ---- per-kernel durations: the same K steps, eagerly, with HIP events on the launch stream ----
     # The C entry point is called with argument lists marshalled beforehand, so the host issues
-    # the steps faster than the GPU runs them (as a native serving loop would).
+    # the steps faster than the GPU runs them.
     shape = SalsShape(cfg.B, cfg.H_q, cfg.H_kv, cfg.d, cfg.r, 1 if cfg.dtype == "bf16" else 0)
     selc = SalsSelect(cfg.k, cfg.w, cfg.G)
     stream = torch.cuda.current_stream().cuda_stream
@@ -161,48 +187,44 @@ def run_workload(cfg, steps, warmup, label):
     t_start = time.perf_counter()
     status = [fn(*a) for a in calls]
     torch.cuda.synchronize()
-    us_step = (time.perf_counter() - t_start) / steps * 1e6
+    eager_us = (time.perf_counter() - t_start) / steps * 1e6
     if any(status):
         raise RuntimeError(f"sals_decode_step_traced returned {set(status)}")
     stage_us = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps * 1e3
                 for j, name in enumerate(STAGES)}
     event_step_us = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(steps)) / steps * 1e3
-
-    # ---- the same K steps as one captured graph (reported beside the value) ----
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(steps):
-            step(i)
-    graph.replay()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    graph.replay()
-    torch.cuda.synchronize()
-    graph_us = (time.perf_counter() - t_start) / steps * 1e6
     del graph, copies
     torch.cuda.empty_cache()
-    return dict(case=case, us=us_step, stage_us=stage_us, event_step_us=event_step_us, graph_us=graph_us)
+    return dict(case=case, us=us_step, stage_us=stage_us, event_step_us=event_step_us, eager_us=eager_us)
 
 
 def roofline_for(cfg, ctx, stage_us, label):
+    """Roofline of the kernel that takes the most time: bound by HBM or by bf16 MFMA, whichever
+    peak gives the longer time for its algorithmic bytes / flops."""
     alg = algorithmic(cfg, ctx)
     dom = max(stage_us, key=stage_us.get)
     t = stage_us[dom] * 1e-6
+    nbytes, nflops = alg["stage_bytes"][dom], alg["stage_flops"][dom]
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = nflops / (BF16_MFMA_PEAK_TFLOPS * 1e12)
     traffic = stored_traffic(dom, label)
-    if dom == "select_attend":
-        achieved = alg["recon_flops"] / t / 1e12
+    if t_mfma > t_hbm:
+        achieved = nflops / t / 1e12
         rl = dict(kernel=dom, bound="mfma", achieved=round(achieved, 2), peak=BF16_MFMA_PEAK_TFLOPS,
                   unit="TFLOP/s", frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), traffic=traffic,
-                  algorithmic_per_launch=alg["recon_flops"], avg_launch_us=round(stage_us[dom], 2))
+                  algorithmic_per_launch=nflops, avg_launch_us=round(stage_us[dom], 2))
     else:
-        achieved = alg["stage_bytes"][dom] / t / 1e9
+        achieved = nbytes / t / 1e9
         rl = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                   frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic,
-                  algorithmic_per_launch=alg["stage_bytes"][dom], avg_launch_us=round(stage_us[dom], 2))
+                  algorithmic_per_launch=nbytes, avg_launch_us=round(stage_us[dom], 2))
     return rl, alg
 
 
-def cpu_baseline(case, budget_s=12.0):
+def cpu_baseline(case, budget_s=10.0):
+    """The oracle (fp64 NumPy, as it stands) on the same stored inputs: whole decode steps of the
+    workload (all sequences, all heads), repeated until about budget_s of CPU time has passed;
+    the mean step time is reported."""
     import oracle
 
     try:
@@ -210,18 +232,16 @@ def cpu_baseline(case, budget_s=12.0):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
         cores = 1
-    B = case["q"].shape[0]
-    done, t0 = 0, time.perf_counter()
-    while done < B:
+    n, t0 = 0, time.perf_counter()
+    while n == 0 or time.perf_counter() - t0 < budget_s:
         oracle.decode_step(case["q"], case["Lk"], case["Lv"], case["Pk"], case["Pv"], ctx=case["ctx"],
                            k=case["k"], w=case["w"], G=case["G"], H_kv=case["H_kv"], base=case["base"],
-                           dtype=case["dtype"], batches=[done])
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    per_seq = (time.perf_counter() - t0) / done
-    return dict(value=round(per_seq * B * 1e6, 1), unit="us/decode_step", cores=cores, kind="oracle",
-                sample=f"oracle decode step on {done} of {B} sequences (all heads), scaled x{B}/{done}")
+                           dtype=case["dtype"])
+        n += 1
+    per_step = (time.perf_counter() - t0) / n
+    return dict(value=round(per_step * 1e6, 1), unit="us/decode_step", cores=cores, kind="oracle",
+                sample=f"{n} whole oracle decode steps of the same workload (all {case['B']} sequences, "
+                       f"all heads), mean, {n * per_step:.1f} s in total")
 
 
 def summary(cfg, r, label):
@@ -231,10 +251,10 @@ def summary(cfg, r, label):
         us_per_step=round(r["us"], 2),
         kv_gbps=round(gbps, 1),
         hbm_frac=round(gbps / HBM_PEAK_GBPS, 4),
-        graph_us_per_step=round(r["graph_us"], 2),
+        eager_us_per_step=round(r["eager_us"], 2),
         event_us_per_step=round(r["event_step_us"], 2),
         stage_us={k: round(v, 2) for k, v in r["stage_us"].items()},
-        recon_tflops=round(alg["recon_flops"] / (r["stage_us"]["select_attend"] * 1e-6) / 1e12, 1),
+        k_rebuild_tflops=round(alg["k_rebuild_flops"] / (r["stage_us"]["select_attend"] * 1e-6) / 1e12, 1),
         compulsory_bytes=alg["compulsory"],
         roofline=rl,
     )
@@ -278,7 +298,7 @@ def main():
         r = run_workload(cfg, args.steps, args.warmup, labels[key])
         res[key] = (cfg, r, summary(cfg, r, labels[key]))
         sm = res[key][2]
-        log(f"[{labels[key]}] {sm['us_per_step']:.1f} us/step (graph {sm['graph_us_per_step']:.1f}), "
+        log(f"[{labels[key]}] {sm['us_per_step']:.1f} us/step (eager traced {sm['eager_us_per_step']:.1f}), "
             f"{sm['kv_gbps']:.0f} GB/s effective, stages "
             + ", ".join(f"{k}={v:.1f}" for k, v in sm["stage_us"].items()))
 

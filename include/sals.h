@@ -126,10 +126,13 @@ sals_status sals_decode_workspace_bytes(const sals_shape* s, const sals_select* 
  *     K_hat   = RoPE(L_k[b, Sel] . P_k[g]^T, Sel),  V_hat = L_v[b, Sel] . P_v[g]^T
  *     out[b,h]= softmax(RoPE(q[b,h], ctx - 1) . K_hat^T / sqrt(d)) . V_hat
  *   P_x[g] = rows [g*d, (g+1)*d) of P_x. RoPE is rotate-half on pairs (i, i + d/2) with angle
- *   p * rope_base^(-2i/d); angles are reduced in fp64 before fp32 sin/cos.
+ *   p * rope_base^(-2i/d); angles are reduced in fp64 before fp32 sin/cos. V_hat carries no
+ *   rotation, so the value side is evaluated as (p^T L_v[b, Sel]) . P_v[g]^T (the same sum in
+ *   another order, fp32): V_hat itself is never formed.
  * Args
  *   s, sel        shapes and knobs as documented on the structs; 1 <= ctx <= ctx_cap, k >= 0,
- *                 w >= 0.
+ *                 w >= 0, and at least one token selected (k > 0 or w > 0), else
+ *                 SALS_ERR_RANGE.
  *   rope_base     RoPE base (> 1).
  *   q             [B, H_q, d] dtype, pre-RoPE query of the token at position ctx - 1.
  *   Lk, Lv        [B, ctx_cap, r] dtype latent caches; rows [0, ctx) are read.

@@ -75,6 +75,7 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   p->Tc = ctx > sel->w ? ctx - sel->w : 0;
   p->kp = sel->k < p->Tc ? sel->k : p->Tc;
   p->n_sel = p->kp + (ctx - p->Tc);
+  if (p->n_sel < 1) return SALS_ERR_RANGE;  // k = w = 0 selects nothing to attend over
   // rows of P_k per latent-query workgroup: one KV head
   const int group_rows = p->D / sel->G;
   p->rps = s->d;

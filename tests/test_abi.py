@@ -73,7 +73,9 @@ def test_decode_workspace_shape_checks(kw, want):
     ((-1, 4, 2), 100, RANGE),
     ((16, -1, 2), 100, RANGE),
     ((16, 4, 2), 0, RANGE),
-    ((0, 0, 1), 1, OK),
+    ((0, 0, 2), 100, RANGE),  # k = w = 0: nothing selected to attend over
+    ((0, 1, 2), 100, OK),
+    ((0, 0, 1), 1, RANGE),
 ])
 def test_decode_select_checks(sel, ctx, want):
     assert _ws_bytes(_shape(), SalsSelect(*sel), ctx)[0] == want
