@@ -2,17 +2,20 @@
 // index set S_{psi,k} of the VL-Cache responses, reviewer XVzL weakness 2).
 //
 // One workgroup of 1024 threads per row. Scores become order-preserving uint32 keys (signed
-// zeros equal). The k-th largest key tau is found by an MSB-first radix select:
-//   1. a 2048-bin histogram of the top 11 key bits (sign, exponent, 2 mantissa bits) over the
-//      whole row; scores spread over many such bins, so LDS atomics rarely collide;
-//   2. the keys of the bin holding the k-th largest are gathered into an LDS candidate list and
-//      the remaining 21 bits are resolved on that short list (11 + 10 bits);
-//   3. if that bin is too full for the list (heavily tied or degenerate rows), the remaining
-//      bits are resolved over the whole row instead (same digits, slower).
-// An ordered compaction then writes the selected indices ascending: the output slot of index i
-// is #(keys > tau before i) + min(#(keys == tau before i), take_eq), from one block-wide
-// exclusive scan of packed (gt, eq) counts per chunk. Rows up to 32768 candidates are staged
-// in LDS once; longer rows are re-read from global memory (L2) on every pass.
+// zeros equal). The k-th largest key tau is found by an MSB-first radix select, and the row is
+// read in full only twice:
+//   1. one pass stages the keys in LDS (rows up to 32768 candidates) and builds a 2048-bin
+//      histogram of the top 11 key bits (sign, exponent, 2 mantissa bits), from which the bin
+//      b1 holding the k-th largest follows;
+//   2. a second pass lists, in index order, every position whose key lies in b1 or above (the
+//      keys of the higher bins plus b1's keys: a short list, ranks from ballots) and builds the
+//      histogram of the next 11 key bits over b1's keys; the last 10 bits of tau come from one
+//      pass over the short list, and the selection is the list filtered by (key > tau, or
+//      key == tau for the first take_eq of them), which keeps the list's index order.
+// If the list would not fit (heavily tied or degenerate rows, or k close to the row length),
+// the remaining digits and the ordered compaction run over the whole row instead (slower).
+// Every pass is branch-free over the keys and ranks come from ballots, so per-key work is a few
+// VALU operations: with one row per CU the passes are bound by issue rate, not memory.
 #include "../common.h"
 #include "../launch.h"
 
@@ -22,27 +25,27 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLdsKeys = 32768;
-constexpr int kCandMax = 4096;
 constexpr int kBins = 2048;
-constexpr int kIPT = 8;  // consecutive items per thread in the compaction
+constexpr int kIPT = 16;  // keys per lane per chunk when a wave ranks a run (16 slices of 64)
 
-// Finds, in hist[0 .. nbins), the bin b holding the `remaining`-th largest item (bins ordered by
+template <bool IN_LDS>
+struct TopkLds {
+  static constexpr int LIST = IN_LDS ? 5120 : 16384;  // short-list capacity (positions)
+};
+
+// Finds, in hist[0 .. kBins), the bin b holding the `remaining`-th largest item (bins ordered by
 // value, highest bin = largest) and the number of items in bins above it. Uses all threads.
-__device__ __forceinline__ void find_bin(const uint32_t* hist, int nbins, uint32_t remaining,
-                                         uint32_t* scan, uint32_t* bcast) {
+__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remaining, uint32_t* scan,
+                                         uint32_t* bcast) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // each thread owns bins [2*tid, 2*tid + 2) of a 2048-bin histogram (fewer bins: zeros)
-  const int b0 = 2 * tid;
-  const uint32_t c0 = b0 < nbins ? hist[b0] : 0u, c1 = b0 + 1 < nbins ? hist[b0 + 1] : 0u;
+  const int b0 = 2 * tid;  // each thread owns bins [2*tid, 2*tid + 2)
+  const uint32_t c0 = hist[b0], c1 = hist[b0 + 1];
   const uint32_t tot = c0 + c1;
-  // suffix sum over the bins: within the wave, then over the waves above this one
-  uint32_t v = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_down(v, o);
-    if (lane + o < 64) v += t;
-  }
-  // v = sum over lanes >= lane of this wave
+  // suffix sum over the bins: within the wave (total minus the exclusive prefix), then the
+  // waves above
+  const uint32_t incl = wave_incl_scan(tot, lane);
+  const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  const uint32_t v = wtot - incl + tot;
   if (lane == 0) scan[wave] = v;
   __syncthreads();
   uint32_t above_waves = 0;
@@ -65,9 +68,10 @@ template <bool IN_LDS>
 __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __restrict__ S,
                                                                int32_t* __restrict__ sel, int Tc,
                                                                int kp, int ctx, int n_sel) {
-  __shared__ uint32_t keys[IN_LDS ? kLdsKeys : 1];
-  __shared__ uint32_t hist[kBins];
-  __shared__ int32_t cand[kCandMax];
+  constexpr int LIST = TopkLds<IN_LDS>::LIST;
+  __shared__ __attribute__((aligned(16))) uint32_t keys[IN_LDS ? kLdsKeys : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  __shared__ int32_t list[LIST];
   __shared__ uint32_t scan[kWaves];
   __shared__ uint32_t bcast[4];
   const int row = blockIdx.x;
@@ -81,117 +85,208 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
     for (int j = tid; j < Tc; j += kThreads) out[j] = j;
     return;
   }
-  if constexpr (IN_LDS) {
-    batched_copy<8>(Tc, tid, kThreads, [&](int i) { return src[i]; },
-                    [&](int i, float v) { keys[i] = float_key(v); });
-  }
   auto key_at = [&](int i) -> uint32_t {
     if constexpr (IN_LDS) return keys[i];
     else return float_key(src[i]);
   };
+  // Keys of this wave for the chunk starting at `base`: wave w owns [base + w*1024, +1024), in
+  // 16 slices of 64 (lane l reads the l-th key of each slice, so LDS reads are conflict-free).
+  // Reads are unconditional (an LDS row never exceeds the staging array; global indices clamp)
+  // so that all 16 are in flight before the first use.
+  constexpr int kChunk = kThreads * kIPT;
+  uint32_t kk[kIPT];
+  auto load_keys = [&](int base) {
+    const int w0 = base + wave * 64 * kIPT;
+#pragma unroll
+    for (int j = 0; j < kIPT; ++j) {
+      const int i = w0 + j * 64 + lane;
+      if constexpr (IN_LDS) kk[j] = keys[i];
+      else kk[j] = float_key(src[min(i, Tc - 1)]);
+    }
+  };
+  // Exclusive prefix of a per-wave count over the waves, and the block total.
+  auto wave_prefix = [&](uint32_t mine, uint32_t& before, uint32_t& total) {
+    if (lane == 0) scan[wave] = mine;
+    __syncthreads();
+    before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t v = scan[w];
+      before += (w < wave) ? v : 0u;
+      total += v;
+    }
+    __syncthreads();
+  };
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
 
-  // ---- digit 1: key bits [31:21] over the whole row ----
+  // ---- 1. keys to LDS and the digit-1 histogram (key bits [31:21]) in one pass ----
   for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
-  if (tid == 0) bcast[2] = 0;
   __syncthreads();
-  batched_copy<8>(Tc, tid, kThreads, key_at, [&](int, uint32_t k) { atomicAdd(&hist[k >> 21], 1u); });
+  if constexpr (IN_LDS) {
+    batched_copy<kLdsKeys / kThreads>(Tc, tid, kThreads, [&](int i) { return src[i]; },
+                                      [&](int i, float v) {
+                                        const uint32_t k = float_key(v);
+                                        keys[i] = k;
+                                        atomicAdd(&hist[k >> 21], 1u);
+                                      });
+  } else {
+    batched_copy<16>(Tc, tid, kThreads, [&](int i) { return src[i]; },
+                     [&](int, float v) { atomicAdd(&hist[float_key(v) >> 21], 1u); });
+  }
   __syncthreads();
-  uint32_t remaining = (uint32_t)kp;
-  find_bin(hist, kBins, remaining, scan, bcast);
+  find_bin(hist, (uint32_t)kp, scan, bcast);
   const uint32_t bin1 = bcast[0];
-  remaining -= bcast[1];
-  const uint32_t n_in_bin = hist[bin1];
+  const uint32_t above = bcast[1];            // keys in bins above bin1
+  const uint32_t nl = above + hist[bin1];     // keys in bin1 or above
+  uint32_t remaining = (uint32_t)kp - above;  // rank of tau inside bin1, >= 1
   __syncthreads();
 
-  uint32_t prefix = bin1 << 21;
-  if (n_in_bin <= (uint32_t)kCandMax) {
-    // ---- gather the bin's keys, resolve bits [20:10] and [9:0] on the short list ----
-    batched_copy<8>(Tc, tid, kThreads, key_at, [&](int i, uint32_t k) {
-      if ((k >> 21) == bin1) {
-        const uint32_t slot = atomicAdd(&bcast[2], 1u);
-        cand[slot] = i;
+  if (nl <= (uint32_t)LIST) {
+    // ---- 2. list every position whose key is in bin1 or above, in index order; the same pass
+    //      builds the histogram of key bits [20:10] over bin1's keys ----
+    for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+    __syncthreads();
+    const uint32_t lo = bin1 << 21;
+    uint32_t run = 0;
+    for (int base = 0; base < Tc; base += kChunk) {
+      load_keys(base);
+      const int w0 = base + wave * 64 * kIPT;
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kIPT; ++j)
+        cnt += (uint32_t)__popcll(__ballot(w0 + j * 64 + lane < Tc && kk[j] >= lo));
+      uint32_t before, total;
+      wave_prefix(cnt, before, total);
+      uint32_t at = run + before;
+#pragma unroll
+      for (int j = 0; j < kIPT; ++j) {
+        const int i = w0 + j * 64 + lane;
+        const bool hit = i < Tc && kk[j] >= lo;
+        const unsigned long long m = __ballot(hit);
+        if (hit) {
+          list[at + (uint32_t)__popcll(m & lt_mask)] = i;
+          if ((kk[j] >> 21) == bin1) atomicAdd(&hist[(kk[j] >> 10) & 0x7ffu], 1u);
+        }
+        at += (uint32_t)__popcll(m);
       }
+      run += total;
+    }
+    __syncthreads();
+    // ---- key bits [20:10], then [9:0] over the list's keys that match so far ----
+    find_bin(hist, remaining, scan, bcast);
+    uint32_t prefix = lo | (bcast[0] << 10);
+    remaining -= bcast[1];
+    for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+    __syncthreads();
+    {
+      constexpr int LU = (LIST + kThreads - 1) / kThreads;
+      int li[LU];
+#pragma unroll
+      for (int u = 0; u < LU; ++u) li[u] = list[min(tid + u * kThreads, (int)nl - 1)];
+      uint32_t lk[LU];
+#pragma unroll
+      for (int u = 0; u < LU; ++u) lk[u] = key_at(li[u]);
+#pragma unroll
+      for (int u = 0; u < LU; ++u)
+        if (tid + u * kThreads < (int)nl && (lk[u] & 0xfffffc00u) == prefix) atomicAdd(&hist[lk[u] & 0x3ffu], 1u);
+    }
+    __syncthreads();
+    find_bin(hist, remaining, scan, bcast);
+    if (tid == 0) {
+      bcast[2] = prefix | bcast[0];
+      bcast[3] = remaining - bcast[1];
+    }
+    __syncthreads();
+    const uint32_t tau = bcast[2], take_eq = bcast[3];
+    // ---- 3. the selection is the list filtered, in list (index) order ----
+    uint32_t run_gt = 0, run_eq = 0;
+    for (int base = 0; base < (int)nl; base += kThreads * 4) {
+      const int j0 = base + tid * 4;
+      uint32_t fgt = 0, feq = 0;
+      int idx[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = min(j0 + e, (int)nl - 1);
+        idx[e] = list[j];
+        const uint32_t k = key_at(idx[e]);
+        const bool valid = j0 + e < (int)nl;
+        fgt |= (uint32_t)(valid && k > tau) << e;
+        feq |= (uint32_t)(valid && k == tau) << e;
+      }
+      const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);
+      const uint32_t incl = wave_incl_scan(packed, lane);
+      uint32_t before, total;
+      wave_prefix(__shfl(incl, 63), before, total);  // lane 63 holds the wave's total
+      const uint32_t excl = before + incl - packed;
+      uint32_t ngt = run_gt + (excl & 0xffffu), neq = run_eq + (excl >> 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((fgt >> e) & 1u) {
+          out[ngt + min(neq, take_eq)] = idx[e];
+          ++ngt;
+        } else if ((feq >> e) & 1u) {
+          if (neq < take_eq) out[ngt + neq] = idx[e];
+          ++neq;
+        }
+      }
+      run_gt += total & 0xffffu;
+      run_eq += total >> 16;
+    }
+    return;
+  }
+
+  // ---- fallback: resolve the remaining digits over the whole row ----
+  uint32_t prefix = bin1 << 21;
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    const uint32_t dmask = pass == 0 ? 0x7ffu : 0x3ffu;
+    const uint32_t pmask = pass == 0 ? 0xffe00000u : 0xfffffc00u;
+    for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+    __syncthreads();
+    batched_copy<8>(Tc, tid, kThreads, key_at, [&](int, uint32_t k) {
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
     });
     __syncthreads();
-    const int nc = (int)n_in_bin;
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-      const int shift = pass == 0 ? 10 : 0;
-      const uint32_t dmask = pass == 0 ? 0x7ffu : 0x3ffu;
-      const uint32_t pmask = pass == 0 ? 0xffe00000u : 0xfffffc00u;
-      for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
-      __syncthreads();
-      for (int j = tid; j < nc; j += kThreads) {
-        const uint32_t k = key_at(cand[j]);
-        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
-      }
-      __syncthreads();
-      find_bin(hist, kBins, remaining, scan, bcast);
-      prefix |= bcast[0] << shift;
-      remaining -= bcast[1];
-      __syncthreads();
-    }
-  } else {
-    // ---- heavily tied row: resolve the remaining digits over the whole row ----
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-      const int shift = pass == 0 ? 10 : 0;
-      const uint32_t dmask = pass == 0 ? 0x7ffu : 0x3ffu;
-      const uint32_t pmask = pass == 0 ? 0xffe00000u : 0xfffffc00u;
-      for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
-      __syncthreads();
-      batched_copy<8>(Tc, tid, kThreads, key_at, [&](int, uint32_t k) {
-        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
-      });
-      __syncthreads();
-      find_bin(hist, kBins, remaining, scan, bcast);
-      prefix |= bcast[0] << shift;
-      remaining -= bcast[1];
-      __syncthreads();
-    }
+    find_bin(hist, remaining, scan, bcast);
+    prefix |= bcast[0] << shift;
+    remaining -= bcast[1];
+    __syncthreads();
   }
   const uint32_t tau = prefix;
   const uint32_t take_eq = remaining;  // >= 1
-
+  // ordered compaction over the whole row: ranks inside a wave's run from ballots, the runs'
+  // packed (gt, eq) totals (each at most 16384, so 16 bits apiece) exchanged per chunk
   uint32_t run_gt = 0, run_eq = 0;
-  for (int base = 0; base < Tc; base += kThreads * kIPT) {
-    const int i0 = base + tid * kIPT;
-    uint32_t fgt = 0, feq = 0;
+  for (int base = 0; base < Tc; base += kChunk) {
+    load_keys(base);
+    const int w0 = base + wave * 64 * kIPT;
+    uint32_t wgt = 0, weq = 0;
 #pragma unroll
     for (int j = 0; j < kIPT; ++j) {
-      const int i = i0 + j;
-      if (i < Tc) {
-        const uint32_t k = key_at(i);
-        fgt |= (uint32_t)(k > tau) << j;
-        feq |= (uint32_t)(k == tau) << j;
-      }
+      const bool valid = w0 + j * 64 + lane < Tc;
+      wgt += (uint32_t)__popcll(__ballot(valid && kk[j] > tau));
+      weq += (uint32_t)__popcll(__ballot(valid && kk[j] == tau));
     }
-    const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);
-    const uint32_t incl = wave_incl_scan(packed, lane);
-    if (lane == 63) scan[wave] = incl;
-    __syncthreads();
-    uint32_t wbase = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t s = scan[w];
-      wbase += (w < wave) ? s : 0u;
-      total += s;
-    }
-    const uint32_t excl = wbase + incl - packed;
-    uint32_t ngt = run_gt + (excl & 0xffffu), neq = run_eq + (excl >> 16);
+    uint32_t before, total;
+    wave_prefix(wgt | (weq << 16), before, total);
+    uint32_t ngt = run_gt + (before & 0xffffu), neq = run_eq + (before >> 16);
 #pragma unroll
     for (int j = 0; j < kIPT; ++j) {
-      if ((fgt >> j) & 1u) {
-        out[ngt + min(neq, take_eq)] = i0 + j;
-        ++ngt;
-      } else if ((feq >> j) & 1u) {
-        if (neq < take_eq) out[ngt + neq] = i0 + j;
-        ++neq;
-      }
+      const int i = w0 + j * 64 + lane;
+      const bool valid = i < Tc;
+      const bool gt = valid && kk[j] > tau, eq = valid && kk[j] == tau;
+      const unsigned long long mg = __ballot(gt), me = __ballot(eq);
+      const uint32_t bg = ngt + (uint32_t)__popcll(mg & lt_mask);  // gt keys before i
+      const uint32_t be = neq + (uint32_t)__popcll(me & lt_mask);  // eq keys before i
+      if (gt) out[bg + min(be, take_eq)] = i;
+      else if (eq && be < take_eq) out[bg + be] = i;
+      ngt += (uint32_t)__popcll(mg);
+      neq += (uint32_t)__popcll(me);
     }
     run_gt += total & 0xffffu;
     run_eq += total >> 16;
-    __syncthreads();
   }
 }
 
