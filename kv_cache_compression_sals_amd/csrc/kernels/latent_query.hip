@@ -41,13 +41,28 @@ __device__ __forceinline__ void unpack8<F32>(const u32x4 (&c)[2], float* v) {
   }
 }
 
+// Writes the final q~[b][s][j] into the scoring operand (see launch.h).
+template <class T>
+__device__ __forceinline__ void store_operand(void* qa, int b, int s, int j, float v, int G, int r) {
+  if constexpr (T::HILO) {
+    const int nsl = (G + 7) / 8;
+    uint16_t* base = (uint16_t*)qa + ((size_t)(b * nsl + s / 8) * 16) * r + j;
+    const uint32_t hi = f32_to_bf16_bits(v);
+    base[(size_t)(s % 8) * r] = (uint16_t)hi;
+    base[(size_t)(8 + s % 8) * r] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+  } else {
+    const int nsl = (G + 15) / 16;
+    ((float*)qa)[((size_t)(b * nsl + s / 16) * 16 + s % 16) * r + j] = v;
+  }
+}
+
 // grid (ceil(r/64), D/rps); rows [rs*rps, (rs+1)*rps) of P_k, 64 columns; rps = d, so a block
 // is exactly one KV head.
 template <class T>
 __global__ __launch_bounds__(kThreads) void lq_partial_kernel(
     const typename T::elem* __restrict__ q, const typename T::elem* __restrict__ Pk,
-    float* __restrict__ dst, int B, int H_q, int H_kv, int d, int r, int G, int rps,
-    int direct) {
+    float* __restrict__ dst, void* __restrict__ qa, int B, int H_q, int H_kv, int d, int r, int G,
+    int rps, int direct) {
   using elem = typename T::elem;
   constexpr int EPC = 16 / (int)sizeof(elem);  // elements per 16-byte chunk
   constexpr int NC = 8 / EPC;                  // chunks per 8 columns
@@ -150,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void lq_partial_kernel(
       if (col < r) {
         const float v = red[0][bb][cc] + red[1][bb][cc] + red[2][bb][cc] + red[3][bb][cc];
         if (direct)
-          dst[((size_t)(b0 + bb) * G + grp) * r + col] = v;
+          store_operand<T>(qa, b0 + bb, grp, col, v, G, r);
         else
           dst[((size_t)rs * B + b0 + bb) * r + col] = v;
       }
@@ -158,9 +173,11 @@ __global__ __launch_bounds__(kThreads) void lq_partial_kernel(
   }
 }
 
-// qt[b][s][j] = sum over the row blocks of group s of qpart[rs][b][j], in block order.
+// q~[b][s][j] = sum over the row blocks of group s of qpart[rs][b][j], in block order, stored
+// into the scoring operand.
+template <class T>
 __global__ __launch_bounds__(256) void lq_reduce_kernel(const float* __restrict__ qpart,
-                                                        float* __restrict__ qt, int B, int G, int r,
+                                                        void* __restrict__ qa, int B, int G, int r,
                                                         int splits_per_group) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= B * G * r) return;
@@ -176,12 +193,12 @@ __global__ __launch_bounds__(256) void lq_reduce_kernel(const float* __restrict_
 #pragma unroll
     for (int u = 0; u < 16; ++u) v += i0 + u < splits_per_group ? x[u] : 0.f;
   }
-  qt[e] = v;
+  store_operand<T>(qa, b, s, j, v, G, r);
 }
 
 }  // namespace
 
-hipError_t launch_latent_query(int dtype, const void* q, const void* Pk, float* qpart, float* qt,
+hipError_t launch_latent_query(int dtype, const void* q, const void* Pk, float* qpart, void* qa,
                                int B, int H_q, int H_kv, int d, int r, int G, int rps,
                                hipStream_t st) {
   const int D = H_kv * d;
@@ -189,16 +206,18 @@ hipError_t launch_latent_query(int dtype, const void* q, const void* Pk, float* 
   const int spg = (D / G) / rps;
   const bool direct = spg == 1;
   dim3 grid(ceil_div(r, 64), n_rs);
-  float* dst = direct ? qt : qpart;
   if (dtype == 0)
-    lq_partial_kernel<F32><<<grid, kThreads, 0, st>>>((const float*)q, (const float*)Pk, dst, B,
+    lq_partial_kernel<F32><<<grid, kThreads, 0, st>>>((const float*)q, (const float*)Pk, qpart, qa, B,
                                                       H_q, H_kv, d, r, G, rps, direct);
   else
-    lq_partial_kernel<BF16><<<grid, kThreads, 0, st>>>((const uint16_t*)q, (const uint16_t*)Pk,
-                                                       dst, B, H_q, H_kv, d, r, G, rps, direct);
+    lq_partial_kernel<BF16><<<grid, kThreads, 0, st>>>((const uint16_t*)q, (const uint16_t*)Pk, qpart,
+                                                       qa, B, H_q, H_kv, d, r, G, rps, direct);
   if (!direct) {
     const int n = B * G * r;
-    lq_reduce_kernel<<<ceil_div(n, 256), 256, 0, st>>>(qpart, qt, B, G, r, spg);
+    if (dtype == 0)
+      lq_reduce_kernel<F32><<<ceil_div(n, 256), 256, 0, st>>>(qpart, qa, B, G, r, spg);
+    else
+      lq_reduce_kernel<BF16><<<ceil_div(n, 256), 256, 0, st>>>(qpart, qa, B, G, r, spg);
   }
   return hipGetLastError();
 }

@@ -5,10 +5,10 @@
 // per step with one 16x16 MFMA chain over the rank: the 16 MFMA rows are the groups' fp32
 // queries, split into bf16 high and low parts for a bf16 cache (8 groups per launch slice), so
 // the bf16 MFMA reproduces an fp32 dot product to ~2^-16 relative; for an fp32 cache the rows
-// are 16 groups and the fp32 MFMA is used. Latent rows are read in the natural k layout (each
+// are 16 groups and the fp32 MFMA is used. The latent-query kernel writes these rows already in
+// operand form, so each wave loads its A fragments straight from L2. Latent rows are read in the natural k layout (each
 // load instruction covers 64 contiguous bytes of 16 consecutive rows); a wave takes 2 or 4 tiles
-// (fewer when the cache is short, so that every CU gets work), loading two tiles at a time. The
-// workgroup stages the groups' queries in LDS once and every wave builds its MFMA rows there.
+// (fewer when the cache is short, so that every CU gets work), loading two tiles at a time.
 #include "../common.h"
 #include "../launch.h"
 
@@ -66,7 +66,7 @@ __device__ __forceinline__ void score_tile(const u32x4 (&a)[R / Win<T>::WLEN],
 // [x*4*TW, (x+1)*4*TW); wave w takes tiles x*4*TW + w + 4*i, i < TW, two at a time: the loads of
 // both tiles of a pair are issued before either is reduced.
 template <class T, int R, int TW>
-__global__ __launch_bounds__(256) void latent_score_kernel(const float* __restrict__ qt,
+__global__ __launch_bounds__(256) void latent_score_kernel(const typename T::elem* __restrict__ qa,
                                                            const typename T::elem* __restrict__ Lk,
                                                            float* __restrict__ S, int G, int Tc,
                                                            int ctx_cap) {
@@ -74,47 +74,22 @@ __global__ __launch_bounds__(256) void latent_score_kernel(const float* __restri
   constexpr int NW = R / W::WLEN;
   constexpr int GPB = T::HILO ? 8 : 16;
   static_assert(TW % 2 == 0, "tiles are taken in pairs");
-  __shared__ float qsh[GPB][R];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int b = blockIdx.y, gb = blockIdx.z;
-  const int ng = min(GPB, G - gb * GPB);
   const size_t brow = (size_t)b * ctx_cap;
   const int tile0 = blockIdx.x * (kWaves * TW) + wave;
-  // the first pair's rows are requested before the query staging
+  // the first pair's rows (HBM) are requested first, then the operand rows (L2)
   u32x4 c0[NW], c1[NW];
   load_tile<T, R>(Lk, brow, min(tile0 * 16 + n16, Tc - 1), q4, c0);
   load_tile<T, R>(Lk, brow, min((tile0 + 4) * 16 + n16, Tc - 1), q4, c1);
-  batched_copy<8>(
-      GPB * R, tid, 256,
-      [&](int e) { return e / R < ng ? qt[((size_t)b * G + gb * GPB + e / R) * R + e % R] : 0.f; },
-      [&](int e, float v) { qsh[e / R][e % R] = v; });
-  __syncthreads();
-  // MFMA A operand: row n16 of the 16 query rows, natural k layout
+  // MFMA A operand: row n16 of this slice's 16 operand rows, natural k layout
   u32x4 a[NW];
   {
-    const int row = T::HILO ? (n16 & 7) : n16;
-    const bool lo = T::HILO && n16 >= 8;
+    const int nsl = (G + GPB - 1) / GPB;
+    const typename T::elem* arow = qa + ((size_t)(b * nsl + gb) * 16 + n16) * R + q4 * W::EPC;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float* src = &qsh[row][w * W::WLEN + q4 * W::EPC];
-      if constexpr (T::HILO) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t bits[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const float v = src[2 * j + e];
-            const uint32_t hi = f32_to_bf16_bits(v);
-            bits[e] = lo ? f32_to_bf16_bits(v - bf16_bits_to_f32(hi)) : hi;
-          }
-          a[w][j] = bits[0] | (bits[1] << 16);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[w][j] = __float_as_uint(src[j]);
-      }
-    }
+    for (int w = 0; w < NW; ++w) a[w] = *(const u32x4*)(arow + w * W::WLEN);
   }
 #pragma unroll
   for (int i = 0; i < TW; i += 2) {
@@ -131,8 +106,9 @@ __global__ __launch_bounds__(256) void latent_score_kernel(const float* __restri
 }
 
 template <class T, int R>
-void launch_t(const float* qt, const void* Lk, float* S, int B, int G, int Tc, int ctx_cap,
+void launch_t(const void* qa, const void* Lk, float* S, int B, int G, int Tc, int ctx_cap,
               hipStream_t st) {
+  using E = typename T::elem;
   constexpr int GPB = T::HILO ? 8 : 16;
   const int tiles = ceil_div(Tc, 16);
   const int slices = ceil_div(G, GPB);
@@ -140,24 +116,24 @@ void launch_t(const float* qt, const void* Lk, float* S, int B, int G, int Tc, i
   const bool four = (long)ceil_div(tiles, kWaves * 4) * B * slices >= 256;
   if (four) {
     dim3 grid(ceil_div(tiles, kWaves * 4), B, slices);
-    latent_score_kernel<T, R, 4><<<grid, 256, 0, st>>>(qt, (const typename T::elem*)Lk, S, G, Tc, ctx_cap);
+    latent_score_kernel<T, R, 4><<<grid, 256, 0, st>>>((const E*)qa, (const E*)Lk, S, G, Tc, ctx_cap);
   } else {
     dim3 grid(ceil_div(tiles, kWaves * 2), B, slices);
-    latent_score_kernel<T, R, 2><<<grid, 256, 0, st>>>(qt, (const typename T::elem*)Lk, S, G, Tc, ctx_cap);
+    latent_score_kernel<T, R, 2><<<grid, 256, 0, st>>>((const E*)qa, (const E*)Lk, S, G, Tc, ctx_cap);
   }
 }
 
 }  // namespace
 
-hipError_t launch_latent_score(int dtype, const float* qt, const void* Lk, float* S, int B, int G,
+hipError_t launch_latent_score(int dtype, const void* qa, const void* Lk, float* S, int B, int G,
                                int r, int Tc, int ctx_cap, hipStream_t st) {
   if (Tc <= 0) return hipSuccess;
 #define SALS_SCORE_CASE(RR)                                              \
   case RR:                                                               \
     if (dtype == 0)                                                      \
-      launch_t<F32, RR>(qt, Lk, S, B, G, Tc, ctx_cap, st);               \
+      launch_t<F32, RR>(qa, Lk, S, B, G, Tc, ctx_cap, st);               \
     else                                                                 \
-      launch_t<BF16, RR>(qt, Lk, S, B, G, Tc, ctx_cap, st);              \
+      launch_t<BF16, RR>(qa, Lk, S, B, G, Tc, ctx_cap, st);              \
     break;
   switch (r) {
     SALS_SCORE_CASE(32)

@@ -11,15 +11,26 @@ namespace sals {
 
 // ---- decode path -------------------------------------------------------------------------
 
+// The latent queries q~[b][s] are handed to the scoring kernel as its MFMA A operand: per
+// sequence b and slice of groups, 16 rows of r elements. bf16 caches: 8 groups per slice,
+// rows 0..7 the bf16 high parts and rows 8..15 the bf16 low parts (v - high) of the fp32
+// values; fp32 caches: 16 groups per slice, one row each. Rows of groups past G are unused.
+inline int score_groups_per_slice(int dtype) { return dtype == 0 ? 16 : 8; }
+inline size_t score_operand_bytes(int dtype, int B, int G, int r) {
+  const int gps = score_groups_per_slice(dtype);
+  return (size_t)B * ((G + gps - 1) / gps) * 16 * r * (dtype == 0 ? 4 : 2);
+}
+
 // q~ partial sums: qpart[rs][b][j] = sum over rows i of row split rs of
 // qsum[b][i] * P_k[i][j], where qsum[b][i] is the sum of q[b][h][i % d] over the query heads
-// h that read KV head i / d. Row splits are `rps` rows long and never straddle a group.
-hipError_t launch_latent_query(int dtype, const void* q, const void* Pk, float* qpart, float* qt,
+// h that read KV head i / d; the sums over the splits of a group go to the operand qa (above).
+// Row splits are `rps` rows long and never straddle a group.
+hipError_t launch_latent_query(int dtype, const void* q, const void* Pk, float* qpart, void* qa,
                                int B, int H_q, int H_kv, int d, int r, int G, int rps,
                                hipStream_t st);
 
-// S[b][s][t] = q~[b][s] . L_k[b][t], t < Tc.
-hipError_t launch_latent_score(int dtype, const float* qt, const void* Lk, float* S, int B, int G,
+// S[b][s][t] = q~[b][s] . L_k[b][t], t < Tc, with q~ given as the operand qa.
+hipError_t launch_latent_score(int dtype, const void* qa, const void* Lk, float* S, int B, int G,
                                int r, int Tc, int ctx_cap, hipStream_t st);
 
 // sel[row][0 .. kp) = top-kp of S[row][0 .. Tc) (ties to the lowest index), ascending;

@@ -60,7 +60,7 @@ struct DecodePlan {
   int D, nqh, Tc, kp, n_sel;
   int rps, spg;
   int split_len, n_splits;
-  size_t off_qt, off_qpart, off_S, off_sel, off_part, total;
+  size_t off_qa, off_qpart, off_S, off_sel, off_part, total;
 };
 
 sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_t ctx,
@@ -92,8 +92,8 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   p->n_splits = (p->n_sel + split - 1) / split;
   if ((long)p->n_splits * s->H_kv * s->B > 0x7fffffffL) return SALS_ERR_RANGE;  // 1-D grid
   size_t off = 0;
-  p->off_qt = off;
-  off += align_up((size_t)s->B * sel->G * s->r * 4);
+  p->off_qa = off;
+  off += align_up(sals::score_operand_bytes(s->dtype, s->B, sel->G, s->r));
   p->off_qpart = off;
   if (p->spg > 1) off += align_up((size_t)(p->D / p->rps) * s->B * s->r * 4);
   p->off_S = off;
@@ -174,7 +174,7 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   if ((st = device_ready()) != SALS_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
   char* w = (char*)ws;
-  float* qt = (float*)(w + p.off_qt);
+  void* qa = w + p.off_qa;
   float* qpart = (float*)(w + p.off_qpart);
   float* S = (float*)(w + p.off_S);
   int32_t* selb = sel_out ? sel_out : (int32_t*)(w + p.off_sel);
@@ -187,11 +187,11 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   const bool score = p.kp > 0 && p.kp < p.Tc;
   mark(0);
   if (score && e == hipSuccess)
-    e = sals::launch_latent_query(s->dtype, q, Pk, qpart, qt, s->B, s->H_q, s->H_kv, s->d, s->r, G,
+    e = sals::launch_latent_query(s->dtype, q, Pk, qpart, qa, s->B, s->H_q, s->H_kv, s->d, s->r, G,
                                   p.rps, hs);
   mark(1);
   if (score && e == hipSuccess)
-    e = sals::launch_latent_score(s->dtype, qt, Lk, S, s->B, G, s->r, p.Tc, ctx_cap, hs);
+    e = sals::launch_latent_score(s->dtype, qa, Lk, S, s->B, G, s->r, p.Tc, ctx_cap, hs);
   mark(2);
   if (e == hipSuccess)
     e = sals::launch_topk_window(S, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel, hs);
