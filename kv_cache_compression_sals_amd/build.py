@@ -32,6 +32,7 @@ SOURCES = [
     "kernels/select_attend_bf16_d64.hip",
     "kernels/select_attend_f32_d128.hip",
     "kernels/select_attend_f32_d64.hip",
+    "kernels/value.hip",
     "kernels/project.hip",
     "kernels/compact.hip",
 ]

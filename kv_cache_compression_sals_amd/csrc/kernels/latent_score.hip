@@ -113,7 +113,7 @@ void launch_t(const void* qa, const void* Lk, float* S, int B, int G, int Tc, in
   const int tiles = ceil_div(Tc, 16);
   const int slices = ceil_div(G, GPB);
   // two tiles per wave unless that already gives the chip several workgroups per CU
-  const bool four = (long)ceil_div(tiles, kWaves * 4) * B * slices >= 256;
+  const bool four = (long)ceil_div(tiles, kWaves * 4) * B * slices >= 1024;
   if (four) {
     dim3 grid(ceil_div(tiles, kWaves * 4), B, slices);
     latent_score_kernel<T, R, 4><<<grid, 256, 0, st>>>((const E*)qa, (const E*)Lk, S, G, Tc, ctx_cap);

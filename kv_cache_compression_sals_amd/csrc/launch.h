@@ -40,11 +40,37 @@ hipError_t launch_topk_window(const float* S, int32_t* sel, int rows, int Tc, in
 
 // Gather + rebuild + RoPE + attention over the selected rows, split along the selected set.
 // With n_splits == 1 the normalised result goes to out; otherwise (m, l, o) partials go to part.
+// With pbuf non-null the kernel stops after the softmax and hands the probabilities to the
+// shared-selection value kernels below: pbuf[b][h][j] = exp(logit_j - m_split) (rows of
+// round_up(n_sel, 4) floats) and pstat[b][h][split] = (m, l).
 hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const void* Lv,
                                 const void* Pk, const void* Pv, const int32_t* sel, float* out,
-                                float* part, int B, int H_q, int H_kv, int d, int r, int G,
-                                int ctx_cap, int ctx, int n_sel, int split_len, int n_splits,
-                                float rope_base, hipStream_t st);
+                                float* part, float* pbuf, float* pstat, int B, int H_q, int H_kv,
+                                int d, int r, int G, int ctx_cap, int ctx, int n_sel,
+                                int split_len, int n_splits, float rope_base, hipStream_t st);
+
+// Value side for selection groups shared by several KV heads (the group's rows are read once
+// per column block instead of once per KV head):
+//   zpart[c][b][h][j] = w[b][h][split(c)] sum_{t in chunk c} pbuf[b][h][t] L_v[b][sel[t]][j]
+//   out[b][h][col] = sum_j P_v[kv(h) d + col][j] sum_c zpart[c][b][h][j]
+// with w the log-sum-exp merge weight of the split and chunk c a piece (cl tokens) of split
+// c / nsub.
+struct ValuePlan {
+  int cb;      // latent columns per value_sum workgroup
+  int nsub;    // chunks per split
+  int cl;      // tokens per chunk
+  int nch;     // chunks in all (n_splits * nsub)
+  size_t lds;  // dynamic LDS of value_sum
+};
+// false when the shape does not fit the kernels' on-chip buffers
+bool value_plan(int dtype, int B, int H_q, int H_kv, int G, int r, int n_sel, int split_len,
+                int n_splits, ValuePlan* vp);
+hipError_t launch_value_sum(int dtype, const ValuePlan& vp, const float* pbuf, const float* pstat,
+                            const int32_t* sel, const void* Lv, float* zpart, int B, int H_q, int G,
+                            int r, int ctx_cap, int n_sel, int split_len, int n_splits,
+                            hipStream_t st);
+hipError_t launch_value_product(int dtype, const ValuePlan& vp, const float* zpart, const void* Pv,
+                                float* out, int B, int H_q, int H_kv, int d, int r, hipStream_t st);
 
 // LSE merge of split partials into out[b][h][:].
 hipError_t launch_combine(const float* part, float* out, int BH, int d, int n_splits,

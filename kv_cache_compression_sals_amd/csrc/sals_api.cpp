@@ -60,7 +60,9 @@ struct DecodePlan {
   int D, nqh, Tc, kp, n_sel;
   int rps, spg;
   int split_len, n_splits;
-  size_t off_qa, off_qpart, off_S, off_sel, off_part, total;
+  bool shared;  // value side by the shared-selection kernels (one selection per >= 4 KV heads)
+  sals::ValuePlan vp;
+  size_t off_qa, off_qpart, off_S, off_sel, off_part, off_p, off_pstat, off_zp, total;
 };
 
 sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_t ctx,
@@ -100,8 +102,20 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   off += align_up((size_t)s->B * sel->G * p->Tc * 4);
   p->off_sel = off;
   off += align_up((size_t)s->B * sel->G * p->n_sel * 4);
+  p->shared = s->H_kv / sel->G >= 4 &&
+              sals::value_plan(s->dtype, s->B, s->H_q, s->H_kv, sel->G, s->r, p->n_sel,
+                               p->split_len, p->n_splits, &p->vp);
   p->off_part = off;
-  if (p->n_splits > 1) off += align_up((size_t)s->B * s->H_q * p->n_splits * (s->d + 2) * 4);
+  if (p->n_splits > 1 && !p->shared)
+    off += align_up((size_t)s->B * s->H_q * p->n_splits * (s->d + 2) * 4);
+  p->off_p = p->off_pstat = p->off_zp = off;
+  if (p->shared) {
+    off += align_up((size_t)s->B * s->H_q * ((p->n_sel + 3) / 4 * 4) * 4);
+    p->off_pstat = off;
+    off += align_up((size_t)s->B * s->H_q * p->n_splits * 2 * 4);
+    p->off_zp = off;
+    off += align_up((size_t)p->vp.nch * s->B * s->H_q * s->r * 4);
+  }
   p->total = off;
   return SALS_OK;
 }
@@ -179,6 +193,9 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   float* S = (float*)(w + p.off_S);
   int32_t* selb = sel_out ? sel_out : (int32_t*)(w + p.off_sel);
   float* part = (float*)(w + p.off_part);
+  float* pbuf = p.shared ? (float*)(w + p.off_p) : nullptr;
+  float* pstat = p.shared ? (float*)(w + p.off_pstat) : nullptr;
+  float* zpart = (float*)(w + p.off_zp);
   const int G = sel->G;
   hipError_t e = hipSuccess;
   auto mark = [&](int i) {
@@ -197,12 +214,20 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
     e = sals::launch_topk_window(S, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel, hs);
   mark(3);
   if (e == hipSuccess)
-    e = sals::launch_select_attend(s->dtype, q, Lk, Lv, Pk, Pv, selb, out, part, s->B, s->H_q,
-                                   s->H_kv, s->d, s->r, G, ctx_cap, ctx, p.n_sel, p.split_len,
-                                   p.n_splits, rope_base, hs);
+    e = sals::launch_select_attend(s->dtype, q, Lk, Lv, Pk, Pv, selb, out, part, pbuf, pstat,
+                                   s->B, s->H_q, s->H_kv, s->d, s->r, G, ctx_cap, ctx, p.n_sel,
+                                   p.split_len, p.n_splits, rope_base, hs);
   mark(4);
-  if (e == hipSuccess && p.n_splits > 1)
+  if (p.shared) {
+    if (e == hipSuccess)
+      e = sals::launch_value_sum(s->dtype, p.vp, pbuf, pstat, selb, Lv, zpart, s->B, s->H_q, G,
+                                 s->r, ctx_cap, p.n_sel, p.split_len, p.n_splits, hs);
+    if (e == hipSuccess)
+      e = sals::launch_value_product(s->dtype, p.vp, zpart, Pv, out, s->B, s->H_q, s->H_kv, s->d,
+                                     s->r, hs);
+  } else if (e == hipSuccess && p.n_splits > 1) {
     e = sals::launch_combine(part, out, s->B * s->H_q, s->d, p.n_splits, hs);
+  }
   mark(5);
   return e == hipSuccess ? SALS_OK : hip_fail(e);
 }

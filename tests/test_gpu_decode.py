@@ -50,6 +50,10 @@ SMALL = [
     ("f32_d128_r256", C1, dict(H_q=8, H_kv=2, d=128, r=256, G=2, k=90, w=10, rank=64), 2, 700, 720),
     ("f32_gqa_d64_r128", C1, dict(H_q=8, H_kv=4, d=64, r=128, G=1, k=33, w=7, rank=40), 1, 413, 413),
     ("bf16_long_split", C3, dict(H_q=8, H_kv=2, r=256, G=2, k=1500, w=64, calib_tokens=512, rank=100), 1, 5000, 5000),
+    # one selection for >= 4 KV heads: value side by the shared-selection kernels
+    ("shared_r384_nqh2", C3, dict(H_q=16, H_kv=8, d=128, r=384, G=2, k=120, w=16, rank=200, calib_tokens=512), 2, 1300, 1333),
+    ("shared_hs24_splits", C3, dict(H_q=24, H_kv=12, d=64, r=128, G=1, k=300, w=20, rank=48, calib_tokens=256), 2, 2000, 2100),
+    ("shared_hs128", C3, dict(H_q=128, H_kv=16, d=64, r=64, G=1, k=150, w=16, rank=32, calib_tokens=256), 1, 1000, 1000),
 ]
 
 
