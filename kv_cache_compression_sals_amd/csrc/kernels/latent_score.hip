@@ -1,6 +1,6 @@
 // Latent scoring (SALS 技术框架 stage 2, second half; 关键创新 1-2): the RoPE-free score of
 // every cached token for every selection group,
-//   S[b][s][t] = q~[b][s] . L_k[b][t],  t < Tc.
+//   S[b][s][t] = q~[b][s] . L_k[b][t],  t < Tc (rows of ldS floats).
 // This streams the whole latent key cache once and is HBM-bound. Each wave computes 16 tokens
 // per step with one 16x16 MFMA chain over the rank: the 16 MFMA rows are the groups' fp32
 // queries, split into bf16 high and low parts for a bf16 cache (8 groups per launch slice), so
@@ -29,7 +29,7 @@ template <class T, int R>
 __device__ __forceinline__ void score_tile(const u32x4 (&a)[R / Win<T>::WLEN],
                                            const u32x4 (&ch)[R / Win<T>::WLEN],
                                            float* __restrict__ S, int b, int G, int gb, int Tc,
-                                           int t0, int lane) {
+                                           int ldS, int t0, int lane) {
   using W = Win<T>;
   const int n16 = lane & 15, q4 = lane >> 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -48,7 +48,7 @@ __device__ __forceinline__ void score_tile(const u32x4 (&a)[R / Win<T>::WLEN],
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int g = gb * 8 + q4 * 4 + i;
-        if (g < G) S[((size_t)b * G + g) * Tc + t] = acc[i] + other[i];
+        if (g < G) S[((size_t)b * G + g) * ldS + t] = acc[i] + other[i];
       }
     }
   } else {
@@ -56,7 +56,7 @@ __device__ __forceinline__ void score_tile(const u32x4 (&a)[R / Win<T>::WLEN],
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int g = gb * 16 + q4 * 4 + i;
-        if (g < G) S[((size_t)b * G + g) * Tc + t] = acc[i];
+        if (g < G) S[((size_t)b * G + g) * ldS + t] = acc[i];
       }
     }
   }
@@ -69,7 +69,7 @@ template <class T, int R, int TW>
 __global__ __launch_bounds__(256) void latent_score_kernel(const typename T::elem* __restrict__ qa,
                                                            const typename T::elem* __restrict__ Lk,
                                                            float* __restrict__ S, int G, int Tc,
-                                                           int ctx_cap) {
+                                                           int ldS, int ctx_cap) {
   using W = Win<T>;
   constexpr int NW = R / W::WLEN;
   constexpr int GPB = T::HILO ? 8 : 16;
@@ -100,13 +100,13 @@ __global__ __launch_bounds__(256) void latent_score_kernel(const typename T::ele
       load_tile<T, R>(Lk, brow, min(tb * 16 + n16, Tc - 1), q4, c1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    score_tile<T, R>(a, c0, S, b, G, gb, Tc, ta * 16, lane);
-    if (tb * 16 < Tc) score_tile<T, R>(a, c1, S, b, G, gb, Tc, tb * 16, lane);
+    score_tile<T, R>(a, c0, S, b, G, gb, Tc, ldS, ta * 16, lane);
+    if (tb * 16 < Tc) score_tile<T, R>(a, c1, S, b, G, gb, Tc, ldS, tb * 16, lane);
   }
 }
 
 template <class T, int R>
-void launch_t(const void* qa, const void* Lk, float* S, int B, int G, int Tc, int ctx_cap,
+void launch_t(const void* qa, const void* Lk, float* S, int ldS, int B, int G, int Tc, int ctx_cap,
               hipStream_t st) {
   using E = typename T::elem;
   constexpr int GPB = T::HILO ? 8 : 16;
@@ -116,24 +116,24 @@ void launch_t(const void* qa, const void* Lk, float* S, int B, int G, int Tc, in
   const bool four = (long)ceil_div(tiles, kWaves * 4) * B * slices >= 1024;
   if (four) {
     dim3 grid(ceil_div(tiles, kWaves * 4), B, slices);
-    latent_score_kernel<T, R, 4><<<grid, 256, 0, st>>>((const E*)qa, (const E*)Lk, S, G, Tc, ctx_cap);
+    latent_score_kernel<T, R, 4><<<grid, 256, 0, st>>>((const E*)qa, (const E*)Lk, S, G, Tc, ldS, ctx_cap);
   } else {
     dim3 grid(ceil_div(tiles, kWaves * 2), B, slices);
-    latent_score_kernel<T, R, 2><<<grid, 256, 0, st>>>((const E*)qa, (const E*)Lk, S, G, Tc, ctx_cap);
+    latent_score_kernel<T, R, 2><<<grid, 256, 0, st>>>((const E*)qa, (const E*)Lk, S, G, Tc, ldS, ctx_cap);
   }
 }
 
 }  // namespace
 
-hipError_t launch_latent_score(int dtype, const void* qa, const void* Lk, float* S, int B, int G,
-                               int r, int Tc, int ctx_cap, hipStream_t st) {
+hipError_t launch_latent_score(int dtype, const void* qa, const void* Lk, float* S, int ldS, int B,
+                               int G, int r, int Tc, int ctx_cap, hipStream_t st) {
   if (Tc <= 0) return hipSuccess;
 #define SALS_SCORE_CASE(RR)                                              \
   case RR:                                                               \
     if (dtype == 0)                                                      \
-      launch_t<F32, RR>(qa, Lk, S, B, G, Tc, ctx_cap, st);               \
+      launch_t<F32, RR>(qa, Lk, S, ldS, B, G, Tc, ctx_cap, st);          \
     else                                                                 \
-      launch_t<BF16, RR>(qa, Lk, S, B, G, Tc, ctx_cap, st);              \
+      launch_t<BF16, RR>(qa, Lk, S, ldS, B, G, Tc, ctx_cap, st);         \
     break;
   switch (r) {
     SALS_SCORE_CASE(32)

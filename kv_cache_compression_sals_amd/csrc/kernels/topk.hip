@@ -67,7 +67,8 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remainin
 template <bool IN_LDS>
 __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __restrict__ S,
                                                                int32_t* __restrict__ sel, int Tc,
-                                                               int kp, int ctx, int n_sel) {
+                                                               int ldS, int kp, int ctx, int n_sel,
+                                                               bool vec) {
   constexpr int LIST = TopkLds<IN_LDS>::LIST;
   __shared__ __attribute__((aligned(16))) uint32_t keys[IN_LDS ? kLdsKeys : 1];
   __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
   __shared__ uint32_t bcast[4];
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* __restrict__ src = S + (size_t)row * Tc;
+  const float* __restrict__ src = S + (size_t)row * ldS;
   int32_t* __restrict__ out = sel + (size_t)row * n_sel;
 
   for (int j = tid; j < ctx - Tc; j += kThreads) out[kp + j] = Tc + j;
@@ -124,12 +125,26 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
   for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
   __syncthreads();
   if constexpr (IN_LDS) {
-    batched_copy<kLdsKeys / kThreads>(Tc, tid, kThreads, [&](int i) { return src[i]; },
-                                      [&](int i, float v) {
-                                        const uint32_t k = float_key(v);
-                                        keys[i] = k;
-                                        atomicAdd(&hist[k >> 21], 1u);
-                                      });
+    if (vec) {  // 16-byte loads (rows start on 16-byte boundaries); keys past Tc are never used
+      const float4* s4 = (const float4*)src;
+      batched_copy<kLdsKeys / 4 / kThreads>((Tc + 3) / 4, tid, kThreads, [&](int u) { return s4[u]; },
+                                            [&](int u, const float4& v) {
+                                              const uint32_t k0 = float_key(v.x), k1 = float_key(v.y),
+                                                             k2 = float_key(v.z), k3 = float_key(v.w);
+                                              *(uint4*)&keys[4 * u] = make_uint4(k0, k1, k2, k3);
+                                              atomicAdd(&hist[k0 >> 21], 1u);
+                                              if (4 * u + 1 < Tc) atomicAdd(&hist[k1 >> 21], 1u);
+                                              if (4 * u + 2 < Tc) atomicAdd(&hist[k2 >> 21], 1u);
+                                              if (4 * u + 3 < Tc) atomicAdd(&hist[k3 >> 21], 1u);
+                                            });
+    } else {
+      batched_copy<kLdsKeys / kThreads>(Tc, tid, kThreads, [&](int i) { return src[i]; },
+                                        [&](int i, float v) {
+                                          const uint32_t k = float_key(v);
+                                          keys[i] = k;
+                                          atomicAdd(&hist[k >> 21], 1u);
+                                        });
+    }
   } else {
     batched_copy<16>(Tc, tid, kThreads, [&](int i) { return src[i]; },
                      [&](int, float v) { atomicAdd(&hist[float_key(v) >> 21], 1u); });
@@ -292,13 +307,14 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
 
 }  // namespace
 
-hipError_t launch_topk_window(const float* S, int32_t* sel, int rows, int Tc, int kp, int ctx,
-                              int n_sel, hipStream_t st) {
+hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, int Tc, int kp,
+                              int ctx, int n_sel, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  const bool vec = (ldS & 3) == 0 && ((uintptr_t)S & 15) == 0;
   if (Tc <= kLdsKeys)
-    topk_window_kernel<true><<<rows, kThreads, 0, st>>>(S, sel, Tc, kp, ctx, n_sel);
+    topk_window_kernel<true><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec);
   else
-    topk_window_kernel<false><<<rows, kThreads, 0, st>>>(S, sel, Tc, kp, ctx, n_sel);
+    topk_window_kernel<false><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec);
   return hipGetLastError();
 }
 

@@ -29,14 +29,14 @@ hipError_t launch_latent_query(int dtype, const void* q, const void* Pk, float* 
                                int B, int H_q, int H_kv, int d, int r, int G, int rps,
                                hipStream_t st);
 
-// S[b][s][t] = q~[b][s] . L_k[b][t], t < Tc, with q~ given as the operand qa.
-hipError_t launch_latent_score(int dtype, const void* qa, const void* Lk, float* S, int B, int G,
-                               int r, int Tc, int ctx_cap, hipStream_t st);
+// S[b][s][t] = q~[b][s] . L_k[b][t], t < Tc (rows of ldS floats), with q~ given as the operand qa.
+hipError_t launch_latent_score(int dtype, const void* qa, const void* Lk, float* S, int ldS, int B,
+                               int G, int r, int Tc, int ctx_cap, hipStream_t st);
 
 // sel[row][0 .. kp) = top-kp of S[row][0 .. Tc) (ties to the lowest index), ascending;
-// sel[row][kp .. n_sel) = Tc .. ctx-1.
-hipError_t launch_topk_window(const float* S, int32_t* sel, int rows, int Tc, int kp, int ctx,
-                              int n_sel, hipStream_t st);
+// sel[row][kp .. n_sel) = Tc .. ctx-1. Rows of S are ldS floats apart.
+hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, int Tc, int kp,
+                              int ctx, int n_sel, hipStream_t st);
 
 // Gather + rebuild + RoPE + attention over the selected rows, split along the selected set.
 // With n_splits == 1 the normalised result goes to out; otherwise (m, l, o) partials go to part.

@@ -57,7 +57,7 @@ sals_status device_ready() {
 // ---- decode plan ---------------------------------------------------------------------------
 
 struct DecodePlan {
-  int D, nqh, Tc, kp, n_sel;
+  int D, nqh, Tc, ldS, kp, n_sel;
   int rps, spg;
   int split_len, n_splits;
   bool shared;  // value side by the shared-selection kernels (one selection per >= 4 KV heads)
@@ -75,6 +75,7 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   p->D = s->H_kv * s->d;
   p->nqh = s->H_q / s->H_kv;
   p->Tc = ctx > sel->w ? ctx - sel->w : 0;
+  p->ldS = (p->Tc + 3) / 4 * 4;  // score rows start on 16-byte boundaries
   p->kp = sel->k < p->Tc ? sel->k : p->Tc;
   p->n_sel = p->kp + (ctx - p->Tc);
   if (p->n_sel < 1) return SALS_ERR_RANGE;  // k = w = 0 selects nothing to attend over
@@ -99,7 +100,7 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   p->off_qpart = off;
   if (p->spg > 1) off += align_up((size_t)(p->D / p->rps) * s->B * s->r * 4);
   p->off_S = off;
-  off += align_up((size_t)s->B * sel->G * p->Tc * 4);
+  off += align_up((size_t)s->B * sel->G * p->ldS * 4);
   p->off_sel = off;
   off += align_up((size_t)s->B * sel->G * p->n_sel * 4);
   p->shared = s->H_kv / sel->G >= 4 &&
@@ -208,10 +209,10 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
                                   p.rps, hs);
   mark(1);
   if (score && e == hipSuccess)
-    e = sals::launch_latent_score(s->dtype, qa, Lk, S, s->B, G, s->r, p.Tc, ctx_cap, hs);
+    e = sals::launch_latent_score(s->dtype, qa, Lk, S, p.ldS, s->B, G, s->r, p.Tc, ctx_cap, hs);
   mark(2);
   if (e == hipSuccess)
-    e = sals::launch_topk_window(S, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel, hs);
+    e = sals::launch_topk_window(S, p.ldS, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel, hs);
   mark(3);
   if (e == hipSuccess)
     e = sals::launch_select_attend(s->dtype, q, Lk, Lv, Pk, Pv, selb, out, part, pbuf, pstat,
@@ -341,7 +342,7 @@ sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const v
     e = sals::launch_importance_accum(c->dtype, K, Qobs, stats, I, c->B, c->H_q, c->H_kv, c->d, w,
                                       ctx_cap, ctx, hs);
   if (e == hipSuccess)
-    e = sals::launch_topk_window(I, kept, c->B * c->H_kv, ctx, k_keep, ctx, k_keep, hs);
+    e = sals::launch_topk_window(I, ctx, kept, c->B * c->H_kv, ctx, k_keep, ctx, k_keep, hs);
   if (e == hipSuccess)
     e = sals::launch_gather_rows(c->dtype, K, V, kept, Kc, Vc, c->B * c->H_kv, c->d, ctx_cap,
                                  k_keep, hs);

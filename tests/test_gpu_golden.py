@@ -43,3 +43,53 @@ def test_golden_selection_on_device(case):
     assert ora["sel"][0, 0].tolist() == case["sel"]
     err = np.abs(out.cpu().numpy().astype(np.float64) - ora["out"]).max()
     assert err <= 1e-4, err
+
+
+def _split_scores(name, T):
+    rs = np.random.default_rng(11)
+    if name == "ties_across_slices":
+        return rs.integers(0, 50, T).astype(np.float32) / 8
+    if name == "two_values":
+        return np.where(rs.random(T) < 0.3, 2.0, 1.0).astype(np.float32)
+    if name == "signed_zeros_and_ones":
+        return rs.choice(np.array([-0.0, 0.0, -1.0, 1.0], dtype=np.float32), T)
+    if name == "list_overflow":
+        s = np.full(T, 0.5, dtype=np.float32)
+        s[rs.choice(T, 40, replace=False)] = 3.0
+        return s
+    if name == "ascending":
+        return np.linspace(-3.0, 3.0, T).astype(np.float32)
+    raise ValueError(name)
+
+
+SPLIT = [("ties_across_slices", 8000, 1000, 16), ("two_values", 6000, 2500, 8),
+         ("signed_zeros_and_ones", 7000, 3000, 32), ("list_overflow", 20000, 500, 64),
+         ("ascending", 5000, 777, 0)]
+
+
+@pytest.mark.parametrize("name,T,k,w", SPLIT, ids=[c[0] for c in SPLIT])
+def test_split_selection_ties(name, T, k, w):
+    """Rows long enough for the many-workgroups-per-row selection, with exact ties at the
+    threshold spread over every slice: the set must be the top-k by (score desc, index asc)."""
+    d = r = 64
+    scores = _split_scores(name, T - w)
+    rs = np.random.default_rng(3)
+    Lk = (0.1 * rs.standard_normal((1, T, r))).astype(np.float32)
+    Lv = rs.standard_normal((1, T, r)).astype(np.float32)
+    Lk[0, : T - w, 0] = scores
+    P = np.eye(d, r, dtype=np.float32)
+    q = np.zeros((1, 1, d), dtype=np.float32)
+    q[0, 0, 0] = 1.0
+    print(f"split selection {name} T={T} k={k} w={w}", flush=True)
+    dev = {n: torch.from_numpy(a).cuda() for n, a in dict(q=q, Lk=Lk, Lv=Lv, P=P).items()}
+    out, sel = sals.sals_decode_step(dev["q"], dev["Lk"], dev["Lv"], dev["P"], dev["P"], ctx=T, k=k, w=w,
+                                     G=1, rope_base=10000.0, want_sel=True)
+    torch.cuda.synchronize()
+    order = np.lexsort((np.arange(T - w), -scores.astype(np.float64)))  # score desc, index asc
+    want = np.concatenate([np.sort(order[:k]), np.arange(T - w, T)])
+    got = sel.cpu().numpy()[0, 0]
+    assert np.array_equal(got, want)
+    ora = oracle.decode_step(q, Lk, Lv, P, P, ctx=T, k=k, w=w, G=1, H_kv=1, base=10000.0, dtype="f32")
+    assert np.array_equal(ora["sel"][0, 0], want)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ora["out"]).max()
+    assert err <= 1e-4, err
