@@ -75,7 +75,9 @@ def build(jobs: int = 0, verbose: bool = True) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    # every symbol must resolve at link time (a kernel template whose host stub is missing
+    # would otherwise only fail when the library is loaded)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{res.stderr}")
