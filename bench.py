@@ -42,6 +42,18 @@ HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 STAGES = ["latent_query", "latent_score", "topk_window", "select_attend", "combine"]
+
+
+def stages_of(cfg):
+    """Stage names of one step, in launch order. When one selection serves four or more KV heads
+    the attention stops after the softmax and the value side runs as its own two kernels
+    ("value": weighted latent row sum + P_v product); otherwise the split partials are merged
+    ("combine")."""
+    return STAGES[:4] + (["value"] if shared_value(cfg) else ["combine"])
+
+
+def shared_value(cfg):
+    return cfg.H_kv // cfg.G >= 4
 KDIR = os.path.join(ROOT, "kv_cache_compression_sals_amd", "csrc")
 # sources whose change invalidates a kernel's stored traffic counters
 KERNEL_SOURCES = {
@@ -50,6 +62,7 @@ KERNEL_SOURCES = {
     "topk_window": ["kernels/topk.hip", "common.h"],
     "latent_query": ["kernels/latent_query.hip", "common.h"],
     "combine": ["kernels/select_attend.hip", "common.h"],
+    "value": ["kernels/value.hip", "common.h"],
 }
 
 
@@ -91,29 +104,36 @@ def algorithmic(cfg, ctx):
     kp = min(cfg.k, Tc)
     n_sel = kp + (ctx - Tc)
     lk_read = B * Tc * r * s
-    sel_rows = 2 * B * G * n_sel * r * s
+    half_rows = B * G * n_sel * r * s  # the selected rows of one of L_k, L_v
+    sel_rows = 2 * half_rows
     p_bytes = 2 * D * r * s
     scores = B * G * Tc * 4
     k_rebuild = 2 * B * Hkv * n_sel * r * d
     value_side = 2 * B * Hq * n_sel * r + 2 * B * Hq * d * r
     logits = 2 * B * Hq * n_sel * d
+    sel_idx = B * G * n_sel * 4
+    q_in, o_out = B * Hq * d * s, B * Hq * d * 4
+    stage_bytes = {
+        "latent_query": D * r * s + q_in + B * G * r * 4,
+        "latent_score": lk_read + B * G * r * 4 + scores,
+        "topk_window": scores + sel_idx,
+    }
+    stage_flops = {"latent_query": 2 * B * Hq * d * r, "latent_score": 2 * B * G * Tc * r, "topk_window": 0}
+    if shared_value(cfg):
+        # attention up to the softmax, probabilities out; then the value kernels read them back
+        probs = B * Hq * n_sel * 4
+        stage_bytes["select_attend"] = half_rows + D * r * s + sel_idx + q_in + probs
+        stage_bytes["value"] = half_rows + D * r * s + sel_idx + probs + o_out
+        stage_flops["select_attend"] = k_rebuild + logits
+        stage_flops["value"] = value_side
+    else:
+        stage_bytes["select_attend"] = sel_rows + p_bytes + sel_idx + q_in + o_out
+        stage_bytes["combine"] = 0
+        stage_flops["select_attend"] = k_rebuild + value_side + logits
+        stage_flops["combine"] = 0
     return dict(
         lk_read=lk_read, sel_rows=sel_rows, p_bytes=p_bytes, compulsory=lk_read + sel_rows + p_bytes,
-        k_rebuild_flops=k_rebuild, n_sel=n_sel, Tc=Tc,
-        stage_bytes={
-            "latent_query": D * r * s + B * Hq * d * s + B * G * r * 4,
-            "latent_score": lk_read + B * G * r * 4 + scores,
-            "topk_window": scores + B * G * n_sel * 4,
-            "select_attend": sel_rows + p_bytes + B * G * n_sel * 4 + B * Hq * d * (s + 4),
-            "combine": 0,
-        },
-        stage_flops={
-            "latent_query": 2 * B * Hq * d * r,
-            "latent_score": 2 * B * G * Tc * r,
-            "topk_window": 0,
-            "select_attend": k_rebuild + value_side + logits,
-            "combine": 0,
-        },
+        k_rebuild_flops=k_rebuild, n_sel=n_sel, Tc=Tc, stage_bytes=stage_bytes, stage_flops=stage_flops,
     )
 
 
@@ -191,7 +211,7 @@ def run_workload(cfg, steps, warmup, label):
     if any(status):
         raise RuntimeError(f"sals_decode_step_traced returned {set(status)}")
     stage_us = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps * 1e3
-                for j, name in enumerate(STAGES)}
+                for j, name in enumerate(stages_of(cfg))}
     event_step_us = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(steps)) / steps * 1e3
     del graph, copies
     torch.cuda.empty_cache()
