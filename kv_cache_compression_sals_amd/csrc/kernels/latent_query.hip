@@ -3,10 +3,13 @@
 //   q~[b][s][j] = sum_{h : group(kv(h)) = s} sum_c q[b][h][c] * P_k[kv(h)*d + c][j].
 // Reordered as a sum over the rows of P_k: row i (KV head g = i / d, c = i % d) is weighted by
 // qsum[b][i] = sum over the query heads of g of q[b][h][c]. P_k is read once per launch, spread
-// over many workgroups: each takes the d rows of one KV head and 64 columns, stages the query
-// values of its rows with 16-byte loads, and issues all of its P_k loads before the first use.
-// The partial sums of the row blocks of one group are added by a second small kernel in a fixed
-// order (skipped when one block covers a whole group), so the result is deterministic.
+// over many workgroups: each takes RB rows inside one group and 64 latent columns. It issues
+// all of its P_k loads first (a wave instruction reads 8 rows x 128 bytes, whole cache lines),
+// forms qsum for its rows while they are in flight, and accumulates per thread over its rows.
+// The 32 row phases of a workgroup are added by one DPP step and then through LDS, in a fixed
+// order. The result is the partial sum over the block's rows, qpart[part][b][s][j]; with one
+// block per group it is q~ itself, otherwise the scoring kernel adds the parts of a group in
+// part order before use. Every sum has a fixed order, so the result is deterministic.
 #include "../common.h"
 #include "../launch.h"
 
@@ -15,9 +18,7 @@ namespace {
 
 constexpr int kBC = 8;         // sequences per pass
 constexpr int kThreads = 256;  // 8 column groups x 32 row phases
-constexpr int kMaxRows = 128;  // rows per block (one KV head: rps = d)
-constexpr int kMaxQH = 8;      // query heads per KV head
-constexpr int kRowIt = kMaxRows / 32;
+constexpr int kQB = 8;         // query-head loads in flight per qsum chunk
 
 template <class T>
 __device__ __forceinline__ void unpack8(const u32x4 (&c)[16 / sizeof(typename T::elem) == 8 ? 1 : 2],
@@ -41,84 +42,73 @@ __device__ __forceinline__ void unpack8<F32>(const u32x4 (&c)[2], float* v) {
   }
 }
 
-// Writes the final q~[b][s][j] into the scoring operand (see launch.h).
-template <class T>
-__device__ __forceinline__ void store_operand(void* qa, int b, int s, int j, float v, int G, int r) {
-  if constexpr (T::HILO) {
-    const int nsl = (G + 7) / 8;
-    uint16_t* base = (uint16_t*)qa + ((size_t)(b * nsl + s / 8) * 16) * r + j;
-    const uint32_t hi = f32_to_bf16_bits(v);
-    base[(size_t)(s % 8) * r] = (uint16_t)hi;
-    base[(size_t)(8 + s % 8) * r] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
-  } else {
-    const int nsl = (G + 15) / 16;
-    ((float*)qa)[((size_t)(b * nsl + s / 16) * 16 + s % 16) * r + j] = v;
-  }
-}
-
-// grid (ceil(r/64), D/rps); rows [rs*rps, (rs+1)*rps) of P_k, 64 columns; rps = d, so a block
-// is exactly one KV head.
-template <class T>
-__global__ __launch_bounds__(kThreads) void lq_partial_kernel(
-    const typename T::elem* __restrict__ q, const typename T::elem* __restrict__ Pk,
-    float* __restrict__ dst, void* __restrict__ qa, int B, int H_q, int H_kv, int d, int r, int G,
-    int rps, int direct) {
+// grid (ceil(r/64), D/RB): block y covers rows [y*RB, (y+1)*RB) of P_k (inside one group),
+// block x latent columns [x*64, x*64 + 64). Thread (cg = tid & 7, rp = tid >> 3) owns columns
+// x*64 + cg*8 .. +8 and rows rp + 32*i.
+template <class T, int RB>
+__global__ __launch_bounds__(kThreads) void latent_query_kernel(const typename T::elem* __restrict__ q,
+                                                                const typename T::elem* __restrict__ Pk,
+                                                                float* __restrict__ qpart, int B,
+                                                                int H_q, int H_kv, int d, int r, int G) {
   using elem = typename T::elem;
   constexpr int EPC = 16 / (int)sizeof(elem);  // elements per 16-byte chunk
   constexpr int NC = 8 / EPC;                  // chunks per 8 columns
-  __shared__ float qv[kMaxQH][kBC][kMaxRows];  // query values of this block's rows, per head
-  __shared__ float qsum[kBC][kMaxRows];
-  __shared__ float red[4][kBC][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int RPT = RB / 32;                 // rows per thread
+  constexpr int QCH = RB / EPC;                // 16-byte query chunks per sequence
+  static_assert(RB % 32 == 0 && RB <= 256, "row block");
+  __shared__ float qsum[kBC][RB];
+  __shared__ __attribute__((aligned(16))) float red[16][kBC][64];  // even row phases after DPP
+  const int tid = threadIdx.x;
   const int cg = tid & 7, rp = tid >> 3;
-  const int rs = blockIdx.y;
-  const int row0 = rs * rps;
-  const int col0 = min(blockIdx.x * 64 + cg * 8, r - 8);  // columns past r are never written
+  const int row0 = blockIdx.y * RB;
+  const int c0 = blockIdx.x * 64;
+  const int col = min(c0 + cg * 8, r - 8);  // columns past r are computed but never stored
   const int nqh = H_q / H_kv;
-  const int D = H_kv * d;
-  const int grp = row0 / (D / G);
-  const int g = row0 / d, c0 = row0 % d;  // the block lies inside KV head g (rps <= d)
+  const int group_rows = H_kv * d / G;
+  const int s = row0 / group_rows, part = (row0 % group_rows) / RB;
 
-  // P_k rows of this thread, all in flight before the query staging completes
-  u32x4 pc[kRowIt][NC];
+  // P_k rows of this thread, all in flight before the query staging starts
+  u32x4 pc[RPT][NC];
 #pragma unroll
-  for (int it = 0; it < kRowIt; ++it) {
-    const int i = min(rp + 32 * it, rps - 1);
+  for (int i = 0; i < RPT; ++i)
 #pragma unroll
-    for (int m = 0; m < NC; ++m) pc[it][m] = *(const u32x4*)(Pk + (size_t)(row0 + i) * r + col0 + m * EPC);
-  }
+    for (int m = 0; m < NC; ++m) pc[i][m] = *(const u32x4*)(Pk + (size_t)(row0 + rp + 32 * i) * r + col + m * EPC);
 
   for (int b0 = 0; b0 < B; b0 += kBC) {
     const int nb = min(kBC, B - b0);
-    __syncthreads();
-    // qv[h][bb][i] = q[b0 + bb][g * nqh + h][c0 + i], 16 bytes per load
-    const int cpr = rps / EPC;  // chunks per (head, sequence)
-    batched_copy<4>(
-        nqh * nb * cpr, tid, kThreads,
-        [&](int e) {
-          const int h = e / (nb * cpr), bb = (e / cpr) % nb, ch = e % cpr;
-          return *(const u32x4*)(q + ((size_t)(b0 + bb) * H_q + (size_t)g * nqh + h) * d + c0 + ch * EPC);
-        },
-        [&](int e, const u32x4& v) {
-          const int h = e / (nb * cpr), bb = (e / cpr) % nb, ch = e % cpr;
-          float* dstp = &qv[h][bb][ch * EPC];
-          if constexpr (EPC == 8) {
+    __syncthreads();  // the previous pass is done with qsum and red
+    // qsum[bb][i] = sum_h q[b0 + bb][g * nqh + h][c] for row row0 + i = g * d + c; a chunk of
+    // EPC rows never straddles a KV head (d is a multiple of EPC)
+    for (int e = tid; e < nb * QCH; e += kThreads) {
+      const int bb = e / QCH, ch = e % QCH;
+      const int row = row0 + ch * EPC;
+      const int g = row / d, c = row % d;
+      const elem* qp = q + ((size_t)(b0 + bb) * H_q + (size_t)g * nqh) * d + c;
+      float acc[EPC];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              dstp[2 * j] = __uint_as_float(v[j] << 16);
-              dstp[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+      for (int x = 0; x < EPC; ++x) acc[x] = 0.f;
+      for (int h0 = 0; h0 < nqh; h0 += kQB) {
+        u32x4 v[kQB];
+#pragma unroll
+        for (int u = 0; u < kQB; ++u) v[u] = *(const u32x4*)(qp + (size_t)min(h0 + u, nqh - 1) * d);
+#pragma unroll
+        for (int u = 0; u < kQB; ++u) {
+          if (h0 + u < nqh) {
+            if constexpr (EPC == 8) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                acc[2 * j] += __uint_as_float(v[u][j] << 16);
+                acc[2 * j + 1] += __uint_as_float(v[u][j] & 0xffff0000u);
+              }
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[j] += __uint_as_float(v[u][j]);
             }
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dstp[j] = __uint_as_float(v[j]);
           }
-        });
-    __syncthreads();
-    for (int e = tid; e < nb * rps; e += kThreads) {
-      const int bb = e / rps, i = e % rps;
-      float s = 0.f;
-      for (int h = 0; h < nqh; ++h) s += qv[h][bb][i];
-      qsum[bb][i] = s;
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < EPC; ++x) qsum[bb][ch * EPC + x] = acc[x];
     }
     __syncthreads();
     float acc[kBC][8];
@@ -127,98 +117,83 @@ __global__ __launch_bounds__(kThreads) void lq_partial_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[bb][j] = 0.f;
 #pragma unroll
-    for (int it = 0; it < kRowIt; ++it) {
-      const int i = rp + 32 * it;
-      if (i < rps) {
-        float p[8];
-        unpack8<T>(pc[it], p);
+    for (int i = 0; i < RPT; ++i) {
+      const int rr = rp + 32 * i;
+      float p[8];
+      unpack8<T>(pc[i], p);
 #pragma unroll
-        for (int bb = 0; bb < kBC; ++bb) {
-          const float wgt = bb < nb ? qsum[bb][i] : 0.f;
+      for (int bb = 0; bb < kBC; ++bb) {
+        const float wgt = bb < nb ? qsum[bb][rr] : 0.f;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[bb][j] = fmaf(wgt, p[j], acc[bb][j]);
-        }
+        for (int j = 0; j < 8; ++j) acc[bb][j] = fmaf(wgt, p[j], acc[bb][j]);
       }
     }
-    // reduce the 8 row phases of a wave (lane bits 3..5), then the 4 waves
+    // row phases rp and rp ^ 1 sit 8 lanes apart in one DPP row: one rotation by 8 adds them
 #pragma unroll
     for (int bb = 0; bb < kBC; ++bb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = acc[bb][j];
-        v += __shfl_xor(v, 8);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[bb][j] = v;
+      for (int j = 0; j < 8; ++j) acc[bb][j] += dpp_f32<0x128>(acc[bb][j]);
+    if ((rp & 1) == 0) {
+#pragma unroll
+      for (int bb = 0; bb < kBC; ++bb) {
+        float4* dst = (float4*)&red[rp >> 1][bb][cg * 8];
+        dst[0] = make_float4(acc[bb][0], acc[bb][1], acc[bb][2], acc[bb][3]);
+        dst[1] = make_float4(acc[bb][4], acc[bb][5], acc[bb][6], acc[bb][7]);
       }
-    if (lane < 8) {
-#pragma unroll
-      for (int bb = 0; bb < kBC; ++bb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) red[wave][bb][lane * 8 + j] = acc[bb][j];
     }
     __syncthreads();
-    for (int e = tid; e < nb * 64; e += kThreads) {
-      const int bb = e / 64, cc = e % 64;
-      const int col = blockIdx.x * 64 + cc;
-      // (col0 is clamped only for column groups lying wholly at or past r, skipped here)
-      if (col < r) {
-        const float v = red[0][bb][cc] + red[1][bb][cc] + red[2][bb][cc] + red[3][bb][cc];
-        if (direct)
-          store_operand<T>(qa, b0 + bb, grp, col, v, G, r);
-        else
-          dst[((size_t)rs * B + b0 + bb) * r + col] = v;
+    // 16 column quads per sequence; the 16 pair sums are added in row-phase order
+    if (tid < nb * 16) {
+      const int bb = tid >> 4, cq = tid & 15;
+      if (c0 + cq * 4 < r) {
+        float4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = *(const float4*)&red[u][bb][cq * 4];
+        float4 sum = v[0];
+#pragma unroll
+        for (int u = 1; u < 16; ++u) {
+          sum.x += v[u].x;
+          sum.y += v[u].y;
+          sum.z += v[u].z;
+          sum.w += v[u].w;
+        }
+        *(float4*)(qpart + (((size_t)part * B + b0 + bb) * G + s) * r + c0 + cq * 4) = sum;
       }
     }
   }
 }
 
-// q~[b][s][j] = sum over the row blocks of group s of qpart[rs][b][j], in block order, stored
-// into the scoring operand.
 template <class T>
-__global__ __launch_bounds__(256) void lq_reduce_kernel(const float* __restrict__ qpart,
-                                                        void* __restrict__ qa, int B, int G, int r,
-                                                        int splits_per_group) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= B * G * r) return;
-  const int j = e % r, s = (e / r) % G, b = e / (r * G);
-  const float* src = qpart + ((size_t)s * splits_per_group * B + b) * r + j;
-  const size_t stride = (size_t)B * r;
-  float v = 0.f;
-  for (int i0 = 0; i0 < splits_per_group; i0 += 16) {
-    float x[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) x[u] = src[(size_t)min(i0 + u, splits_per_group - 1) * stride];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < 16; ++u) v += i0 + u < splits_per_group ? x[u] : 0.f;
-  }
-  store_operand<T>(qa, b, s, j, v, G, r);
+void launch_t(const void* q, const void* Pk, float* qpart, int B, int H_q, int H_kv, int d, int r,
+              int G, int rb, hipStream_t st) {
+  using E = typename T::elem;
+  const dim3 grid(ceil_div(r, 64), H_kv * d / rb);
+  if (rb == 64)
+    latent_query_kernel<T, 64><<<grid, kThreads, 0, st>>>((const E*)q, (const E*)Pk, qpart, B, H_q, H_kv, d, r, G);
+  else if (rb == 128)
+    latent_query_kernel<T, 128><<<grid, kThreads, 0, st>>>((const E*)q, (const E*)Pk, qpart, B, H_q, H_kv, d, r, G);
+  else
+    latent_query_kernel<T, 256><<<grid, kThreads, 0, st>>>((const E*)q, (const E*)Pk, qpart, B, H_q, H_kv, d, r, G);
 }
 
 }  // namespace
 
-hipError_t launch_latent_query(int dtype, const void* q, const void* Pk, float* qpart, void* qa,
-                               int B, int H_q, int H_kv, int d, int r, int G, int rps,
-                               hipStream_t st) {
-  const int D = H_kv * d;
-  const int n_rs = D / rps;
-  const int spg = (D / G) / rps;
-  const bool direct = spg == 1;
-  dim3 grid(ceil_div(r, 64), n_rs);
+int latent_query_rows(int H_kv, int d, int r, int G) {
+  const int group_heads = H_kv / G;
+  // two KV heads per block when that still gives the chip enough workgroups: fewer parts for
+  // the scoring kernel to add
+  if (2 * d <= 256 && group_heads % 2 == 0 && (long)ceil_div(r, 64) * (H_kv / 2) >= kLqMinBlocks)
+    return 2 * d;
+  return d;
+}
+
+hipError_t launch_latent_query(int dtype, const void* q, const void* Pk, float* qpart, int B,
+                               int H_q, int H_kv, int d, int r, int G, int rb, hipStream_t st) {
+  if (rb != 64 && rb != 128 && rb != 256) return hipErrorInvalidValue;
   if (dtype == 0)
-    lq_partial_kernel<F32><<<grid, kThreads, 0, st>>>((const float*)q, (const float*)Pk, qpart, qa, B,
-                                                      H_q, H_kv, d, r, G, rps, direct);
+    launch_t<F32>(q, Pk, qpart, B, H_q, H_kv, d, r, G, rb, st);
   else
-    lq_partial_kernel<BF16><<<grid, kThreads, 0, st>>>((const uint16_t*)q, (const uint16_t*)Pk, qpart,
-                                                       qa, B, H_q, H_kv, d, r, G, rps, direct);
-  if (!direct) {
-    const int n = B * G * r;
-    if (dtype == 0)
-      lq_reduce_kernel<F32><<<ceil_div(n, 256), 256, 0, st>>>(qpart, qa, B, G, r, spg);
-    else
-      lq_reduce_kernel<BF16><<<ceil_div(n, 256), 256, 0, st>>>(qpart, qa, B, G, r, spg);
-  }
+    launch_t<BF16>(q, Pk, qpart, B, H_q, H_kv, d, r, G, rb, st);
   return hipGetLastError();
 }
 

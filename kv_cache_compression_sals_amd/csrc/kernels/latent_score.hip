@@ -5,10 +5,12 @@
 // per step with one 16x16 MFMA chain over the rank: the 16 MFMA rows are the groups' fp32
 // queries, split into bf16 high and low parts for a bf16 cache (8 groups per launch slice), so
 // the bf16 MFMA reproduces an fp32 dot product to ~2^-16 relative; for an fp32 cache the rows
-// are 16 groups and the fp32 MFMA is used. The latent-query kernel writes these rows already in
-// operand form, so each wave loads its A fragments straight from L2. Latent rows are read in the natural k layout (each
-// load instruction covers 64 contiguous bytes of 16 consecutive rows); a wave takes 2 or 4 tiles
-// (fewer when the cache is short, so that every CU gets work), loading two tiles at a time.
+// are 16 groups and the fp32 MFMA is used. A workgroup first issues the loads of its first
+// latent tiles, then adds the latent-query partial sums of its groups (part order), writes the
+// operand rows to LDS and takes its A fragments from there. Latent rows are read in the
+// natural k layout (each load instruction covers 64 contiguous bytes of 16 consecutive rows); a
+// wave takes 2 or 4 tiles (fewer when the cache is short, so that every CU gets work), loading
+// two tiles at a time.
 #include "../common.h"
 #include "../launch.h"
 
@@ -62,35 +64,108 @@ __device__ __forceinline__ void score_tile(const u32x4 (&a)[R / Win<T>::WLEN],
   }
 }
 
+// Operand row entries of group slot gs, columns 4 cq .. 4 cq + 3 (bf16: high parts in row gs,
+// low parts in row 8 + gs).
+template <class T>
+__device__ __forceinline__ void store_operand_quad(typename T::elem* opnd, int ost, int gs, int cq,
+                                                   const float4& v) {
+  const float x[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (T::HILO) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t hi = f32_to_bf16_bits(x[i]);
+      opnd[gs * ost + cq * 4 + i] = (typename T::elem)hi;
+      opnd[(8 + gs) * ost + cq * 4 + i] = (typename T::elem)f32_to_bf16_bits(x[i] - bf16_bits_to_f32(hi));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) opnd[gs * ost + cq * 4 + i] = x[i];
+  }
+}
+
 // grid (ceil(tiles / (4 * TW)), B, group slices); block 256. Workgroup x covers tiles
 // [x*4*TW, (x+1)*4*TW); wave w takes tiles x*4*TW + w + 4*i, i < TW, two at a time: the loads of
 // both tiles of a pair are issued before either is reduced.
-template <class T, int R, int TW>
-__global__ __launch_bounds__(256) void latent_score_kernel(const typename T::elem* __restrict__ qa,
+// PB: latent-query part loads in flight per thread (1 when every group has a single part).
+template <class T, int R, int TW, int PB>
+__global__ __launch_bounds__(256) void latent_score_kernel(const float* __restrict__ qpart, int npart,
                                                            const typename T::elem* __restrict__ Lk,
-                                                           float* __restrict__ S, int G, int Tc,
+                                                           float* __restrict__ S, int B, int G, int Tc,
                                                            int ldS, int ctx_cap) {
   using W = Win<T>;
+  using elem = typename T::elem;
   constexpr int NW = R / W::WLEN;
   constexpr int GPB = T::HILO ? 8 : 16;
+  constexpr int OST = R + W::EPC;  // operand row stride in LDS (elements), padded by one chunk
   static_assert(TW % 2 == 0, "tiles are taken in pairs");
+  __shared__ __attribute__((aligned(16))) elem opnd[16 * OST];
+  __shared__ float4 rsum[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int b = blockIdx.y, gb = blockIdx.z;
   const size_t brow = (size_t)b * ctx_cap;
   const int tile0 = blockIdx.x * (kWaves * TW) + wave;
-  // the first pair's rows (HBM) are requested first, then the operand rows (L2)
+  // the first pair's rows (HBM) are requested first, then the latent-query parts (L2)
   u32x4 c0[NW], c1[NW];
   load_tile<T, R>(Lk, brow, min(tile0 * 16 + n16, Tc - 1), q4, c0);
   load_tile<T, R>(Lk, brow, min((tile0 + 4) * 16 + n16, Tc - 1), q4, c1);
-  // MFMA A operand: row n16 of this slice's 16 operand rows, natural k layout
-  u32x4 a[NW];
+  // operand rows: q~ of group slot gs in row gs (bf16: high part; row 8 + gs the low part).
+  // Rows of slots past G are never written; the MFMA rows they feed are never stored. The parts
+  // of a column quad are split into npg contiguous ranges (npg = 256 / quads when there are
+  // fewer than 256 quads), each summed by one thread with all its loads in flight; the range
+  // sums are then added in range order.
   {
-    const int nsl = (G + GPB - 1) / GPB;
-    const typename T::elem* arow = qa + ((size_t)(b * nsl + gb) * 16 + n16) * R + q4 * W::EPC;
+    const int gv = min(GPB, G - gb * GPB);
+    const int nq = gv * (R / 4);  // column quads of the slice
+    const int npg = nq >= 256 ? 1 : min(256 / nq, npart);
+    const int per = (npart + npg - 1) / npg;
+    const size_t pstride = (size_t)B * G * R;
+    for (int e = tid; e < nq * npg; e += 256) {
+      const int quad = e % nq, pg = e / nq;
+      const int gs = quad / (R / 4), cq = quad % (R / 4);
+      const float* src = qpart + ((size_t)b * G + gb * GPB + gs) * R + cq * 4;
+      const int pa = pg * per, pe = min(npart, pa + per);
+      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int p0 = pa; p0 < pe; p0 += PB) {
+        float4 v[PB];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) a[w] = *(const u32x4*)(arow + w * W::WLEN);
+        for (int u = 0; u < PB; ++u) v[u] = *(const float4*)(src + (size_t)min(p0 + u, pe - 1) * pstride);
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+          if (p0 + u < pe) {
+            sum.x += v[u].x;
+            sum.y += v[u].y;
+            sum.z += v[u].z;
+            sum.w += v[u].w;
+          }
+        }
+      }
+      if (npg == 1) {
+        store_operand_quad<T>(opnd, OST, gs, cq, sum);
+      } else {
+        rsum[pg * nq + quad] = sum;
+      }
+    }
+    if (npg > 1) {
+      __syncthreads();
+      for (int quad = tid; quad < nq; quad += 256) {
+        float4 sum = rsum[quad];
+        for (int pg = 1; pg < npg; ++pg) {
+          const float4 v = rsum[pg * nq + quad];
+          sum.x += v.x;
+          sum.y += v.y;
+          sum.z += v.z;
+          sum.w += v.w;
+        }
+        store_operand_quad<T>(opnd, OST, quad / (R / 4), quad % (R / 4), sum);
+      }
+    }
   }
+  __syncthreads();
+  // MFMA A operand: row n16 of the operand, natural k layout
+  u32x4 a[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) a[w] = *(const u32x4*)(opnd + n16 * OST + w * W::WLEN + q4 * W::EPC);
 #pragma unroll
   for (int i = 0; i < TW; i += 2) {
     const int ta = tile0 + 4 * i, tb = ta + 4;
@@ -105,35 +180,44 @@ __global__ __launch_bounds__(256) void latent_score_kernel(const typename T::ele
   }
 }
 
-template <class T, int R>
-void launch_t(const void* qa, const void* Lk, float* S, int ldS, int B, int G, int Tc, int ctx_cap,
-              hipStream_t st) {
+template <class T, int R, int TW>
+void launch_tw(dim3 grid, const float* qpart, int npart, const void* Lk, float* S, int ldS, int B,
+               int G, int Tc, int ctx_cap, hipStream_t st) {
   using E = typename T::elem;
+  if (npart == 1)
+    latent_score_kernel<T, R, TW, 1><<<grid, 256, 0, st>>>(qpart, npart, (const E*)Lk, S, B, G, Tc, ldS, ctx_cap);
+  else
+    latent_score_kernel<T, R, TW, 8><<<grid, 256, 0, st>>>(qpart, npart, (const E*)Lk, S, B, G, Tc, ldS, ctx_cap);
+}
+
+template <class T, int R>
+void launch_t(const float* qpart, int npart, const void* Lk, float* S, int ldS, int B, int G, int Tc,
+              int ctx_cap, hipStream_t st) {
   constexpr int GPB = T::HILO ? 8 : 16;
   const int tiles = ceil_div(Tc, 16);
   const int slices = ceil_div(G, GPB);
   // two tiles per wave unless that already gives the chip several workgroups per CU
   const bool four = (long)ceil_div(tiles, kWaves * 4) * B * slices >= 1024;
-  if (four) {
-    dim3 grid(ceil_div(tiles, kWaves * 4), B, slices);
-    latent_score_kernel<T, R, 4><<<grid, 256, 0, st>>>((const E*)qa, (const E*)Lk, S, G, Tc, ldS, ctx_cap);
-  } else {
-    dim3 grid(ceil_div(tiles, kWaves * 2), B, slices);
-    latent_score_kernel<T, R, 2><<<grid, 256, 0, st>>>((const E*)qa, (const E*)Lk, S, G, Tc, ldS, ctx_cap);
-  }
+  if (four)
+    launch_tw<T, R, 4>(dim3(ceil_div(tiles, kWaves * 4), B, slices), qpart, npart, Lk, S, ldS, B, G, Tc,
+                       ctx_cap, st);
+  else
+    launch_tw<T, R, 2>(dim3(ceil_div(tiles, kWaves * 2), B, slices), qpart, npart, Lk, S, ldS, B, G, Tc,
+                       ctx_cap, st);
 }
 
 }  // namespace
 
-hipError_t launch_latent_score(int dtype, const void* qa, const void* Lk, float* S, int ldS, int B,
-                               int G, int r, int Tc, int ctx_cap, hipStream_t st) {
+hipError_t launch_latent_score(int dtype, const float* qpart, int npart, const void* Lk, float* S,
+                               int ldS, int B, int G, int r, int Tc, int ctx_cap, hipStream_t st) {
   if (Tc <= 0) return hipSuccess;
-#define SALS_SCORE_CASE(RR)                                              \
-  case RR:                                                               \
-    if (dtype == 0)                                                      \
-      launch_t<F32, RR>(qa, Lk, S, ldS, B, G, Tc, ctx_cap, st);          \
-    else                                                                 \
-      launch_t<BF16, RR>(qa, Lk, S, ldS, B, G, Tc, ctx_cap, st);         \
+  if (npart < 1) return hipErrorInvalidValue;
+#define SALS_SCORE_CASE(RR)                                                  \
+  case RR:                                                                   \
+    if (dtype == 0)                                                          \
+      launch_t<F32, RR>(qpart, npart, Lk, S, ldS, B, G, Tc, ctx_cap, st);    \
+    else                                                                     \
+      launch_t<BF16, RR>(qpart, npart, Lk, S, ldS, B, G, Tc, ctx_cap, st);   \
     break;
   switch (r) {
     SALS_SCORE_CASE(32)

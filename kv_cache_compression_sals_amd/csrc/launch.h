@@ -11,27 +11,20 @@ namespace sals {
 
 // ---- decode path -------------------------------------------------------------------------
 
-// The latent queries q~[b][s] are handed to the scoring kernel as its MFMA A operand: per
-// sequence b and slice of groups, 16 rows of r elements. bf16 caches: 8 groups per slice,
-// rows 0..7 the bf16 high parts and rows 8..15 the bf16 low parts (v - high) of the fp32
-// values; fp32 caches: 16 groups per slice, one row each. Rows of groups past G are unused.
-inline int score_groups_per_slice(int dtype) { return dtype == 0 ? 16 : 8; }
-inline size_t score_operand_bytes(int dtype, int B, int G, int r) {
-  const int gps = score_groups_per_slice(dtype);
-  return (size_t)B * ((G + gps - 1) / gps) * 16 * r * (dtype == 0 ? 4 : 2);
-}
+// Latent queries as partial sums over row blocks of P_k: qpart[part][b][s][j] = sum over the
+// rows i of block `part` of group s of qsum[b][i] * P_k[i][j], where qsum[b][i] is the sum of
+// q[b][h][i % d] over the query heads h that read KV head i / d. Blocks are `rb` rows long
+// (rb = latent_query_rows(...), a multiple of d inside one group), so a group has
+// npart = (H_kv d / G) / rb parts and q~[b][s] = sum over its parts, in part order.
+constexpr int kLqMinBlocks = 192;
+int latent_query_rows(int H_kv, int d, int r, int G);
+hipError_t launch_latent_query(int dtype, const void* q, const void* Pk, float* qpart, int B,
+                               int H_q, int H_kv, int d, int r, int G, int rb, hipStream_t st);
 
-// q~ partial sums: qpart[rs][b][j] = sum over rows i of row split rs of
-// qsum[b][i] * P_k[i][j], where qsum[b][i] is the sum of q[b][h][i % d] over the query heads
-// h that read KV head i / d; the sums over the splits of a group go to the operand qa (above).
-// Row splits are `rps` rows long and never straddle a group.
-hipError_t launch_latent_query(int dtype, const void* q, const void* Pk, float* qpart, void* qa,
-                               int B, int H_q, int H_kv, int d, int r, int G, int rps,
-                               hipStream_t st);
-
-// S[b][s][t] = q~[b][s] . L_k[b][t], t < Tc (rows of ldS floats), with q~ given as the operand qa.
-hipError_t launch_latent_score(int dtype, const void* qa, const void* Lk, float* S, int ldS, int B,
-                               int G, int r, int Tc, int ctx_cap, hipStream_t st);
+// S[b][s][t] = q~[b][s] . L_k[b][t], t < Tc (rows of ldS floats), with q~ the sum of the npart
+// partial sums in qpart (layout above).
+hipError_t launch_latent_score(int dtype, const float* qpart, int npart, const void* Lk, float* S,
+                               int ldS, int B, int G, int r, int Tc, int ctx_cap, hipStream_t st);
 
 // sel[row][0 .. kp) = top-kp of S[row][0 .. Tc) (ties to the lowest index), ascending;
 // sel[row][kp .. n_sel) = Tc .. ctx-1. Rows of S are ldS floats apart.

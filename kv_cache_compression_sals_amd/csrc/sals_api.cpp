@@ -58,11 +58,11 @@ sals_status device_ready() {
 
 struct DecodePlan {
   int D, nqh, Tc, ldS, kp, n_sel;
-  int rps, spg;
+  int rb, npart;  // latent-query row block and parts per group
   int split_len, n_splits;
   bool shared;  // value side by the shared-selection kernels (one selection per >= 4 KV heads)
   sals::ValuePlan vp;
-  size_t off_qa, off_qpart, off_S, off_sel, off_part, off_p, off_pstat, off_zp, total;
+  size_t off_qpart, off_S, off_sel, off_part, off_p, off_pstat, off_zp, total;
 };
 
 sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_t ctx,
@@ -79,10 +79,9 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   p->kp = sel->k < p->Tc ? sel->k : p->Tc;
   p->n_sel = p->kp + (ctx - p->Tc);
   if (p->n_sel < 1) return SALS_ERR_RANGE;  // k = w = 0 selects nothing to attend over
-  // rows of P_k per latent-query workgroup: one KV head
   const int group_rows = p->D / sel->G;
-  p->rps = s->d;
-  p->spg = group_rows / p->rps;
+  p->rb = sals::latent_query_rows(s->H_kv, s->d, s->r, sel->G);
+  p->npart = group_rows / p->rb;
   const int max_split = sals::select_attend_max_split(s->dtype, s->d, s->r, p->nqh);
   if (max_split < 16) return SALS_ERR_SHAPE;
   const long pairs = (long)s->B * s->H_kv;
@@ -95,10 +94,8 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   p->n_splits = (p->n_sel + split - 1) / split;
   if ((long)p->n_splits * s->H_kv * s->B > 0x7fffffffL) return SALS_ERR_RANGE;  // 1-D grid
   size_t off = 0;
-  p->off_qa = off;
-  off += align_up(sals::score_operand_bytes(s->dtype, s->B, sel->G, s->r));
   p->off_qpart = off;
-  if (p->spg > 1) off += align_up((size_t)(p->D / p->rps) * s->B * s->r * 4);
+  off += align_up((size_t)p->npart * s->B * sel->G * s->r * 4);
   p->off_S = off;
   off += align_up((size_t)s->B * sel->G * p->ldS * 4);
   p->off_sel = off;
@@ -189,7 +186,6 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   if ((st = device_ready()) != SALS_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
   char* w = (char*)ws;
-  void* qa = w + p.off_qa;
   float* qpart = (float*)(w + p.off_qpart);
   float* S = (float*)(w + p.off_S);
   int32_t* selb = sel_out ? sel_out : (int32_t*)(w + p.off_sel);
@@ -205,11 +201,12 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   const bool score = p.kp > 0 && p.kp < p.Tc;
   mark(0);
   if (score && e == hipSuccess)
-    e = sals::launch_latent_query(s->dtype, q, Pk, qpart, qa, s->B, s->H_q, s->H_kv, s->d, s->r, G,
-                                  p.rps, hs);
+    e = sals::launch_latent_query(s->dtype, q, Pk, qpart, s->B, s->H_q, s->H_kv, s->d, s->r, G,
+                                  p.rb, hs);
   mark(1);
   if (score && e == hipSuccess)
-    e = sals::launch_latent_score(s->dtype, qa, Lk, S, p.ldS, s->B, G, s->r, p.Tc, ctx_cap, hs);
+    e = sals::launch_latent_score(s->dtype, qpart, p.npart, Lk, S, p.ldS, s->B, G, s->r, p.Tc,
+                                  ctx_cap, hs);
   mark(2);
   if (e == hipSuccess)
     e = sals::launch_topk_window(S, p.ldS, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel, hs);
