@@ -119,6 +119,23 @@ __device__ __forceinline__ float lane_f32(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// global loads (which stay in flight), then synchronises the waves. __syncthreads() also
+// waits for every outstanding global load.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// v[l] + v[l ^ 32] in every lane l, as (lower half + upper half) in both halves, by one
+// cross-half lane swap (no LDS traffic).
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum / max over the 16 lanes of a DPP row (lanes sharing lane/16), result in every lane of it.
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f32<0xB1>(v);

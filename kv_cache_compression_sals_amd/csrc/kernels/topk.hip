@@ -8,10 +8,12 @@
 //      histogram of the top 11 key bits (sign, exponent, 2 mantissa bits), from which the bin
 //      b1 holding the k-th largest follows;
 //   2. a second pass lists, in index order, every position whose key lies in b1 or above (the
-//      keys of the higher bins plus b1's keys: a short list, ranks from ballots) and builds the
-//      histogram of the next 11 key bits over b1's keys; the last 10 bits of tau come from one
-//      pass over the short list, and the selection is the list filtered by (key > tau, or
-//      key == tau for the first take_eq of them), which keeps the list's index order.
+//      keys of the higher bins plus b1's keys: a short list). Each thread tests 16 consecutive
+//      keys into a 16-bit hit mask; its list position is a prefix sum of the mask counts. The
+//      next 11 key bits of tau come from a histogram over the listed keys of b1, the last 10
+//      from one more pass over the short list, and the selection is the list filtered by
+//      (key > tau, or key == tau for the first take_eq of them), which keeps the list's index
+//      order.
 // If the list would not fit (heavily tied or degenerate rows, or k close to the row length),
 // the remaining digits and the ordered compaction run over the whole row instead (slower).
 // Every pass is branch-free over the keys and ranks come from ballots, so per-key work is a few
@@ -37,7 +39,7 @@ struct TopkLds {
 // value, highest bin = largest) and the number of items in bins above it. Uses all threads.
 __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remaining, uint32_t* scan,
                                          uint32_t* bcast) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b0 = 2 * tid;  // each thread owns bins [2*tid, 2*tid + 2)
   const uint32_t c0 = hist[b0], c1 = hist[b0 + 1];
   const uint32_t tot = c0 + c1;
@@ -48,8 +50,20 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remainin
   const uint32_t v = wtot - incl + tot;
   if (lane == 0) scan[wave] = v;
   __syncthreads();
+  // the totals of all waves in four 16-byte reads, then the ones above this wave (no chain of
+  // dependent LDS reads)
+  uint32_t sv[kWaves];
+#pragma unroll
+  for (int q = 0; q < kWaves / 4; ++q) {
+    const uint4 t = ((const uint4*)scan)[q];
+    sv[4 * q] = t.x;
+    sv[4 * q + 1] = t.y;
+    sv[4 * q + 2] = t.z;
+    sv[4 * q + 3] = t.w;
+  }
   uint32_t above_waves = 0;
-  for (int w = wave + 1; w < kWaves; ++w) above_waves += scan[w];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) above_waves += w > wave ? sv[w] : 0u;
   const uint32_t suf = v + above_waves;  // items in this thread's bins and all higher bins
   const uint32_t above = suf - tot;
   if (above < remaining && remaining <= suf) {
@@ -73,10 +87,10 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
   __shared__ __attribute__((aligned(16))) uint32_t keys[IN_LDS ? kLdsKeys : 1];
   __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
   __shared__ int32_t list[LIST];
-  __shared__ uint32_t scan[kWaves];
+  __shared__ __attribute__((aligned(16))) uint32_t scan[kWaves];
   __shared__ uint32_t bcast[4];
   const int row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float* __restrict__ src = S + (size_t)row * ldS;
   int32_t* __restrict__ out = sel + (size_t)row * n_sel;
 
@@ -164,28 +178,66 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
     __syncthreads();
     const uint32_t lo = bin1 << 21;
     uint32_t run = 0;
-    for (int base = 0; base < Tc; base += kChunk) {
-      load_keys(base);
-      const int w0 = base + wave * 64 * kIPT;
-      uint32_t cnt = 0;
+    if constexpr (IN_LDS) {
+      // each thread tests 16 consecutive keys (four 16-byte reads in a lane-dependent order, so
+      // that the 8 lanes sharing an LDS bank row hit 8 different 16-byte slots), keeps a 16-bit
+      // hit mask, and writes its hits in index order at its prefix-sum position
+      for (int base = 0; base < Tc; base += kChunk) {
+        const int b0 = base + tid * 16;
+        uint32_t hm = 0;
 #pragma unroll
-      for (int j = 0; j < kIPT; ++j)
-        cnt += (uint32_t)__popcll(__ballot(w0 + j * 64 + lane < Tc && kk[j] >= lo));
-      uint32_t before, total;
-      wave_prefix(cnt, before, total);
-      uint32_t at = run + before;
-#pragma unroll
-      for (int j = 0; j < kIPT; ++j) {
-        const int i = w0 + j * 64 + lane;
-        const bool hit = i < Tc && kk[j] >= lo;
-        const unsigned long long m = __ballot(hit);
-        if (hit) {
-          list[at + (uint32_t)__popcll(m & lt_mask)] = i;
-          if ((kk[j] >> 21) == bin1) atomicAdd(&hist[(kk[j] >> 10) & 0x7ffu], 1u);
+        for (int c = 0; c < 4; ++c) {
+          const int cc = ((lane >> 1) + c) & 3;
+          const uint4 k4 = *(const uint4*)&keys[b0 + cc * 4];
+          hm |= ((k4.x >= lo ? 1u : 0u) | (k4.y >= lo ? 2u : 0u) | (k4.z >= lo ? 4u : 0u) |
+                 (k4.w >= lo ? 8u : 0u)) << (cc * 4);
         }
-        at += (uint32_t)__popcll(m);
+        const int nv = min(max(Tc - b0, 0), 16);
+        hm &= nv >= 16 ? 0xffffu : ((1u << nv) - 1u);
+        const uint32_t cnt = (uint32_t)__popc(hm);
+        const uint32_t incl = wave_incl_scan(cnt, lane);
+        uint32_t before, total;
+        wave_prefix((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), before, total);
+        uint32_t at = run + before + incl - cnt;
+        while (hm) {
+          list[at++] = b0 + __builtin_ctz(hm);
+          hm &= hm - 1u;
+        }
+        run += total;
       }
-      run += total;
+    } else {
+      for (int base = 0; base < Tc; base += kChunk) {
+        load_keys(base);
+        const int w0 = base + wave * 64 * kIPT;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kIPT; ++j)
+          cnt += (uint32_t)__popcll(__ballot(w0 + j * 64 + lane < Tc && kk[j] >= lo));
+        uint32_t before, total;
+        wave_prefix(cnt, before, total);
+        uint32_t at = run + before;
+        // the same tests as the count pass, recomputed: keeping its 16 ballots live across the
+        // barrier would spill scalar registers (the empty asm hides the equality from the
+        // compiler)
+        uint32_t lo_w = lo;
+        int tc_w = Tc;
+        asm volatile("" : "+v"(lo_w), "+v"(tc_w));
+#pragma unroll
+        for (int j = 0; j < kIPT; ++j) {
+          const int i = w0 + j * 64 + lane;
+          const bool hit = i < tc_w && kk[j] >= lo_w;
+          const unsigned long long m = __ballot(hit);
+          if (hit) list[at + (uint32_t)__popcll(m & lt_mask)] = i;
+          at += (uint32_t)__popcll(m);
+        }
+        run += total;
+      }
+    }
+    __syncthreads();
+    // histogram of key bits [20:10] over the listed keys of bin1
+    for (int u = tid; u < (int)nl; u += kThreads) {
+      const uint32_t k = key_at(list[u]);
+      if ((k >> 21) == bin1) atomicAdd(&hist[(k >> 10) & 0x7ffu], 1u);
     }
     __syncthreads();
     // ---- key bits [20:10], then [9:0] over the list's keys that match so far ----
