@@ -36,7 +36,8 @@ struct TopkLds {
 };
 
 // Finds, in hist[0 .. kBins), the bin b holding the `remaining`-th largest item (bins ordered by
-// value, highest bin = largest) and the number of items in bins above it. Uses all threads.
+// value, highest bin = largest): bcast[0] = b, bcast[1] = items in bins above b, bcast[2] =
+// items in b. Uses all threads; hist is no longer read once it returns.
 __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remaining, uint32_t* scan,
                                          uint32_t* bcast) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -70,9 +71,11 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remainin
     if (above + c1 >= remaining) {
       bcast[0] = (uint32_t)(b0 + 1);
       bcast[1] = above;
+      bcast[2] = c1;
     } else {
       bcast[0] = (uint32_t)b0;
       bcast[1] = above + c1;
+      bcast[2] = c0;
     }
   }
   __syncthreads();
@@ -167,15 +170,15 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
   find_bin(hist, (uint32_t)kp, scan, bcast);
   const uint32_t bin1 = bcast[0];
   const uint32_t above = bcast[1];            // keys in bins above bin1
-  const uint32_t nl = above + hist[bin1];     // keys in bin1 or above
+  const uint32_t nl = above + bcast[2];       // keys in bin1 or above
   uint32_t remaining = (uint32_t)kp - above;  // rank of tau inside bin1, >= 1
-  __syncthreads();
+  // (bcast is next written inside a find_bin, after barriers every thread passes after these
+  // reads; hist is free: the zeroing below is ordered before the next atomics by barriers)
 
   if (nl <= (uint32_t)LIST) {
     // ---- 2. list every position whose key is in bin1 or above, in index order; the same pass
     //      builds the histogram of key bits [20:10] over bin1's keys ----
     for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
-    __syncthreads();
     const uint32_t lo = bin1 << 21;
     uint32_t run = 0;
     if constexpr (IN_LDS) {
@@ -260,20 +263,16 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
     }
     __syncthreads();
     find_bin(hist, remaining, scan, bcast);
-    if (tid == 0) {
-      bcast[2] = prefix | bcast[0];
-      bcast[3] = remaining - bcast[1];
-    }
-    __syncthreads();
-    const uint32_t tau = bcast[2], take_eq = bcast[3];
+    const uint32_t tau = prefix | bcast[0], take_eq = remaining - bcast[1];
     // ---- 3. the selection is the list filtered, in list (index) order ----
+    constexpr int FPT = (LIST + kThreads - 1) / kThreads;  // list entries per thread: one pass
     uint32_t run_gt = 0, run_eq = 0;
-    for (int base = 0; base < (int)nl; base += kThreads * 4) {
-      const int j0 = base + tid * 4;
+    for (int base = 0; base < (int)nl; base += kThreads * FPT) {
+      const int j0 = base + tid * FPT;
       uint32_t fgt = 0, feq = 0;
-      int idx[4];
+      int idx[FPT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < FPT; ++e) {
         const int j = min(j0 + e, (int)nl - 1);
         idx[e] = list[j];
         const uint32_t k = key_at(idx[e]);
@@ -284,11 +283,11 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
       const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);
       const uint32_t incl = wave_incl_scan(packed, lane);
       uint32_t before, total;
-      wave_prefix(__shfl(incl, 63), before, total);  // lane 63 holds the wave's total
+      wave_prefix((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), before, total);  // wave total
       const uint32_t excl = before + incl - packed;
       uint32_t ngt = run_gt + (excl & 0xffffu), neq = run_eq + (excl >> 16);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < FPT; ++e) {
         if ((fgt >> e) & 1u) {
           out[ngt + min(neq, take_eq)] = idx[e];
           ++ngt;
