@@ -22,6 +22,12 @@ eager_us_per_step. One JSON line goes to stdout; progress goes to stderr.
 
 --calib-copy-mib M first copies an M MiB buffer with torch (a plain copy kernel of known size),
 so that a counter run can scale FETCH_SIZE / WRITE_SIZE to bytes.
+
+--only may also name c4 (post-prefill compaction of the 16K-context VLM-shaped cache, then the
+dense decode over the compact cache) and c5 (one decode step through 32 independent layers of
+the 128K-context GQA workload, all resident). They are reported as extra objects of the JSON
+line (timed as K back-to-back calls between HIP events, resp. one replay of K captured 32-layer
+steps); the default run leaves them out because their inputs take a minute to generate.
 """
 
 from __future__ import annotations
@@ -218,6 +224,120 @@ def run_workload(cfg, steps, warmup, label):
     return dict(case=case, us=us_step, stage_us=stage_us, event_step_us=event_step_us, eager_us=eager_us)
 
 
+def run_compact_workload(cfg, steps, warmup, label):
+    """kv_compact on the full compaction workload, then sals_dense_decode over the compact cache;
+    each timed as `steps` back-to-back calls between two HIP events."""
+    import numpy as np
+    import torch
+
+    import kv_cache_compression_sals_amd as sals
+    from workloads import compact_case
+
+    t0 = time.time()
+    case = compact_case(cfg, threads=16)
+    log(f"[{label}] generated inputs in {time.time() - t0:.1f}s")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    K, V, Qobs, q = (dev(case[n]) for n in ("K", "V", "Qobs", "q"))
+    del case
+    B, H_kv, ctx_cap, d = K.shape
+    ctx, kk = cfg.ctx, cfg.k_keep
+    Kc = torch.empty((B, H_kv, kk, d), dtype=K.dtype, device="cuda")
+    Vc, kept = torch.empty_like(Kc), torch.empty((B, H_kv, kk), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Qobs.shape[1], d), dtype=torch.float32, device="cuda")
+    ws_c = torch.empty(sals.kv_compact_workspace_bytes(K, Qobs, ctx=ctx, k_keep=kk), dtype=torch.uint8, device="cuda")
+    ws_d = torch.empty(sals.sals_dense_decode_workspace_bytes(q, Kc, n=kk), dtype=torch.uint8, device="cuda")
+    compact = lambda: sals.kv_compact(K, V, Qobs, ctx=ctx, k_keep=kk, Kc=Kc, Vc=Vc, kept=kept, workspace=ws_c)
+    decode = lambda: sals.sals_dense_decode(q, Kc, Vc, n=kk, out=out, workspace=ws_d)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    c_us, d_us = timed(compact), timed(decode)
+    s = 2
+    # compaction: K once for the importance (its second pass is recomputation), the kept K and V
+    # rows read and written once, the observation queries; decode: the compact cache once
+    c_bytes = B * H_kv * ctx * d * s + 4 * B * H_kv * kk * d * s + Qobs.numel() * s
+    d_bytes = 2 * B * H_kv * kk * d * s
+    H_q = Qobs.shape[1]
+    del K, V, Qobs, Kc, Vc, ws_c, ws_d
+    torch.cuda.empty_cache()
+    return dict(workload=f"{label}: B={B} H_q={H_q} H_kv={H_kv} d={d} ctx={ctx} w={cfg.w} "
+                         f"k_keep={kk}, bf16",
+                compact_us=round(c_us, 1), compact_gbps=round(c_bytes / (c_us * 1e-6) / 1e9, 1),
+                decode_us=round(d_us, 2), decode_gbps=round(d_bytes / (d_us * 1e-6) / 1e9, 1),
+                compact_bytes=c_bytes, decode_bytes=d_bytes)
+
+
+def _layer_inputs(layer):
+    """One layer of the 128K-context workload, generated in a worker process."""
+    from threadpoolctl import threadpool_limits
+
+    from workloads import CONFIGS, decode_case
+
+    with threadpool_limits(1):
+        c = decode_case(CONFIGS["c5"], layer=layer)
+    return layer, {n: c[n] for n in ("q", "Lk", "Lv", "Pk", "Pv")}
+
+
+def run_layers_workload(cfg, steps, warmup, label, n_layers=32):
+    """One decode step through n_layers independent layers (all resident): `steps` steps captured
+    as one HIP graph, one upload replay, then one timed replay."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import torch
+
+    import kv_cache_compression_sals_amd as sals
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    t0 = time.time()
+    layers = [None] * n_layers
+    with mp.get_context("spawn").Pool(min(16, os.cpu_count() or 1)) as pool:
+        for l, arrs in pool.imap_unordered(_layer_inputs, range(n_layers)):
+            layers[l] = {n: dev(a) for n, a in arrs.items()}
+    log(f"[{label}] generated and uploaded {n_layers} layers in {time.time() - t0:.1f}s")
+    ctx = cfg.ctx
+    kw = dict(ctx=ctx, k=cfg.k, w=cfg.w, G=cfg.G, rope_base=cfg.base)
+    ws = torch.empty(sals.sals_decode_workspace_bytes(layers[0]["q"], layers[0]["Pk"], ctx=ctx, k=cfg.k, w=cfg.w,
+                                                      G=cfg.G), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((cfg.B, cfg.H_q, cfg.d), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+
+    def step():
+        for l, t in enumerate(layers):
+            sals.sals_decode_step(t["q"], t["Lk"], t["Lv"], t["Pk"], t["Pv"], out=outs[l], workspace=ws, **kw)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t_start) / steps * 1e6
+    alg = algorithmic(cfg, ctx)
+    del graph, layers, ws
+    torch.cuda.empty_cache()
+    return dict(workload=f"{label}: {n_layers} layers, B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} d={cfg.d} "
+                         f"ctx={ctx} r={cfg.r} k={cfg.k} w={cfg.w} G={cfg.G}",
+                us_per_step=round(us, 1), us_per_layer=round(us / n_layers, 2),
+                kv_gbps=round(n_layers * alg["compulsory"] / (us * 1e-6) / 1e9, 1),
+                compulsory_bytes_per_step=n_layers * alg["compulsory"])
+
+
 def roofline_for(cfg, ctx, stage_us, label):
     """Roofline of the kernel that takes the most time: bound by HBM or by bf16 MFMA, whichever
     peak gives the longer time for its algorithmic bytes / flops."""
@@ -310,8 +430,17 @@ def main():
         log(f"[calib] copied {args.calib_copy_mib} MiB")
         del a, b
 
-    labels = {"c2": "ctx4k", "c3": "ctx32k"}
+    labels = {"c2": "ctx4k", "c3": "ctx32k", "c4": "compact_ctx16k", "c5": "ctx128k_32layers"}
     keys = [k for k in args.only.split(",") if k]
+    extra = {}
+    for key in [k for k in keys if k in ("c4", "c5")]:
+        fn = run_compact_workload if key == "c4" else run_layers_workload
+        extra[labels[key]] = fn(CONFIGS[key], min(args.steps, 10), min(args.warmup, 2), labels[key])
+        log(f"[{labels[key]}] {extra[labels[key]]}")
+    keys = [k for k in keys if k not in ("c4", "c5")]
+    if not keys:
+        print("--only must name c2 or c3 (the step the JSON line's value reports)", file=sys.stderr)
+        sys.exit(2)
     res = {}
     for key in keys:
         cfg = CONFIGS[key]
@@ -348,6 +477,7 @@ def main():
         line[labels[key]] = dict(workload=f"{labels[key]} decode, one layer: B={c.B} H_q={c.H_q} "
                                           f"H_kv={c.H_kv} d={c.d} ctx={c.ctx} r={c.r} k={c.k} w={c.w} G={c.G}",
                                  **s)
+    line.update(extra)
     if not args.no_cpu_baseline:
         log(f"[cpu] timing the oracle on a bounded sample of the {labels[head]} workload")
         line["cpu_baseline"] = cpu_baseline(r["case"])

@@ -18,6 +18,8 @@
 // the remaining digits and the ordered compaction run over the whole row instead (slower).
 // Every pass is branch-free over the keys and ranks come from ballots, so per-key work is a few
 // VALU operations: with one row per CU the passes are bound by issue rate, not memory.
+#include <type_traits>
+
 #include "../common.h"
 #include "../launch.h"
 
@@ -32,7 +34,10 @@ constexpr int kIPT = 16;  // keys per lane per chunk when a wave ranks a run (16
 
 template <bool IN_LDS>
 struct TopkLds {
-  static constexpr int LIST = IN_LDS ? 5120 : 16384;  // short-list capacity (positions)
+  // short-list capacity (positions): rows staged in LDS have positions below 32768, so their
+  // list holds 16-bit entries
+  static constexpr int LIST = IN_LDS ? 10240 : 16384;
+  using entry = std::conditional_t<IN_LDS, uint16_t, int32_t>;
 };
 
 // Finds, in hist[0 .. kBins), the bin b holding the `remaining`-th largest item (bins ordered by
@@ -81,26 +86,35 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remainin
   __syncthreads();
 }
 
-template <bool IN_LDS>
-__global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __restrict__ S,
-                                                               int32_t* __restrict__ sel, int Tc,
-                                                               int ldS, int kp, int ctx, int n_sel,
-                                                               bool vec) {
+// The selection of one workgroup: the kp largest of n keys, ties to the lowest position, written
+// to out[0 .. kp) in ascending position order as map(position) (and, with okeys, their keys to
+// okeys[0 .. kp)), followed by the window out[kp + j] = wstart + j, j < wcount. Keys are
+// float_key(src[i]) with map(i) = obase + i, or (GATHER) the given keys ckeys[i] with
+// map(i) = cand[i]. GATHER requires IN_LDS.
+template <bool IN_LDS, bool GATHER>
+__device__ __forceinline__ void topk_body(const float* __restrict__ src, const int32_t* __restrict__ cand,
+                                          const uint32_t* __restrict__ ckeys, int n, int kp,
+                                          int32_t* __restrict__ out, uint32_t* __restrict__ okeys,
+                                          int obase, int wcount, int wstart, bool vec) {
+  static_assert(IN_LDS || !GATHER, "candidate keys are staged in LDS");
   constexpr int LIST = TopkLds<IN_LDS>::LIST;
   __shared__ __attribute__((aligned(16))) uint32_t keys[IN_LDS ? kLdsKeys : 1];
   __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
-  __shared__ int32_t list[LIST];
+  __shared__ typename TopkLds<IN_LDS>::entry list[LIST];
   __shared__ __attribute__((aligned(16))) uint32_t scan[kWaves];
   __shared__ uint32_t bcast[4];
-  const int row = blockIdx.x;
+  __shared__ uint32_t mm[GATHER ? 2 * kWaves : 1];  // per-wave key minima and maxima
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const float* __restrict__ src = S + (size_t)row * ldS;
-  int32_t* __restrict__ out = sel + (size_t)row * n_sel;
+  const int Tc = n;
+  auto map = [&](int i) -> int32_t {
+    if constexpr (GATHER) return cand[i];
+    else return obase + i;
+  };
 
-  for (int j = tid; j < ctx - Tc; j += kThreads) out[kp + j] = Tc + j;
+  for (int j = tid; j < wcount; j += kThreads) out[kp + j] = wstart + j;
   if (kp <= 0) return;
   if (kp >= Tc) {
-    for (int j = tid; j < Tc; j += kThreads) out[j] = j;
+    for (int j = tid; j < Tc; j += kThreads) out[j] = map(j);
     return;
   }
   auto key_at = [&](int i) -> uint32_t {
@@ -141,7 +155,41 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
   // ---- 1. keys to LDS and the digit-1 histogram (key bits [31:21]) in one pass ----
   for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
   __syncthreads();
-  if constexpr (IN_LDS) {
+  if constexpr (GATHER) {
+    // Candidate keys lie in a narrow range (each is among the largest of its slice), so their
+    // top 11 bits would fall in a few bins (long bin searches, contended histogram atomics).
+    // They are re-encoded as (key - min) << clz(max - min): strictly increasing on the range,
+    // so order and ties are unchanged, and the range fills the top key bits.
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+    batched_copy<kLdsKeys / kThreads>(Tc, tid, kThreads, [&](int i) { return ckeys[i]; },
+                                      [&](int i, uint32_t k) {
+                                        keys[i] = k;
+                                        kmn = min(kmn, k);
+                                        kmx = max(kmx, k);
+                                      });
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o));
+      kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o));
+    }
+    if (lane == 0) {
+      mm[wave] = kmn;
+      mm[kWaves + wave] = kmx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      kmn = min(kmn, mm[w]);
+      kmx = max(kmx, mm[kWaves + w]);
+    }
+    const uint32_t range = kmx - kmn;
+    const int ls = range ? __clz(range) : 0;
+    for (int i = tid; i < Tc; i += kThreads) {
+      const uint32_t k = (keys[i] - kmn) << ls;
+      keys[i] = k;
+      atomicAdd(&hist[k >> 21], 1u);
+    }
+  } else if constexpr (IN_LDS) {
     if (vec) {  // 16-byte loads (rows start on 16-byte boundaries); keys past Tc are never used
       const float4* s4 = (const float4*)src;
       batched_copy<kLdsKeys / 4 / kThreads>((Tc + 3) / 4, tid, kThreads, [&](int u) { return s4[u]; },
@@ -203,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
         wave_prefix((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), before, total);
         uint32_t at = run + before + incl - cnt;
         while (hm) {
-          list[at++] = b0 + __builtin_ctz(hm);
+          list[at++] = (uint16_t)(b0 + __builtin_ctz(hm));
           hm &= hm - 1u;
         }
         run += total;
@@ -271,11 +319,17 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
       const int j0 = base + tid * FPT;
       uint32_t fgt = 0, feq = 0;
       int idx[FPT];
+      uint32_t kv[FPT];
+#pragma unroll
+      for (int e = 0; e < FPT; ++e) idx[e] = list[min(j0 + e, (int)nl - 1)];
+      // output values requested before the block scan, so that their loads (candidate positions)
+      // are in flight while it runs
+      int32_t ov[FPT];
+#pragma unroll
+      for (int e = 0; e < FPT; ++e) ov[e] = map(idx[e]);
 #pragma unroll
       for (int e = 0; e < FPT; ++e) {
-        const int j = min(j0 + e, (int)nl - 1);
-        idx[e] = list[j];
-        const uint32_t k = key_at(idx[e]);
+        const uint32_t k = kv[e] = key_at(idx[e]);
         const bool valid = j0 + e < (int)nl;
         fgt |= (uint32_t)(valid && k > tau) << e;
         feq |= (uint32_t)(valid && k == tau) << e;
@@ -289,10 +343,14 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
 #pragma unroll
       for (int e = 0; e < FPT; ++e) {
         if ((fgt >> e) & 1u) {
-          out[ngt + min(neq, take_eq)] = idx[e];
+          out[ngt + min(neq, take_eq)] = ov[e];
+          if (okeys) okeys[ngt + min(neq, take_eq)] = kv[e];
           ++ngt;
         } else if ((feq >> e) & 1u) {
-          if (neq < take_eq) out[ngt + neq] = idx[e];
+          if (neq < take_eq) {
+            out[ngt + neq] = ov[e];
+            if (okeys) okeys[ngt + neq] = kv[e];
+          }
           ++neq;
         }
       }
@@ -346,8 +404,13 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
       const unsigned long long mg = __ballot(gt), me = __ballot(eq);
       const uint32_t bg = ngt + (uint32_t)__popcll(mg & lt_mask);  // gt keys before i
       const uint32_t be = neq + (uint32_t)__popcll(me & lt_mask);  // eq keys before i
-      if (gt) out[bg + min(be, take_eq)] = i;
-      else if (eq && be < take_eq) out[bg + be] = i;
+      if (gt) {
+        out[bg + min(be, take_eq)] = map(i);
+        if (okeys) okeys[bg + min(be, take_eq)] = kk[j];
+      } else if (eq && be < take_eq) {
+        out[bg + be] = map(i);
+        if (okeys) okeys[bg + be] = kk[j];
+      }
       ngt += (uint32_t)__popcll(mg);
       neq += (uint32_t)__popcll(me);
     }
@@ -356,16 +419,75 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __re
   }
 }
 
+template <bool IN_LDS>
+__global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __restrict__ S,
+                                                               int32_t* __restrict__ sel, int Tc,
+                                                               int ldS, int kp, int ctx, int n_sel,
+                                                               bool vec) {
+  const int row = blockIdx.x;
+  topk_body<IN_LDS, false>(S + (size_t)row * ldS, nullptr, nullptr, Tc, kp, sel + (size_t)row * n_sel,
+                           nullptr, 0, ctx - Tc, Tc, vec);
+}
+
+// Rows longer than the LDS staging array: one workgroup per (row, slice of slen keys) keeps the
+// kp largest of its slice (ties to the lowest position) as candidates, in ascending position
+// order, with their keys. Every element of the row's top kp is among its slice's top kp, with the
+// lowest-index ties of the row's threshold key included, so the row's selection over the
+// candidates (which are in ascending position order across slices) is exact.
+__global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __restrict__ S,
+                                                              int32_t* __restrict__ cand,
+                                                              uint32_t* __restrict__ ckeys, int Tc,
+                                                              int ldS, int kp, int slen, int ns,
+                                                              bool vec) {
+  const int row = blockIdx.x / ns, s = blockIdx.x % ns;
+  const int s0 = s * slen, n = min(slen, Tc - s0);
+  const size_t o = ((size_t)row * ns + s) * kp;
+  topk_body<true, false>(S + (size_t)row * ldS + s0, nullptr, nullptr, n, kp, cand + o, ckeys + o, s0, 0, 0,
+                         vec);
+}
+
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(const int32_t* __restrict__ cand,
+                                                              const uint32_t* __restrict__ ckeys,
+                                                              int32_t* __restrict__ sel, int Tc, int kp,
+                                                              int ns, int ctx, int n_sel) {
+  const int row = blockIdx.x;
+  const size_t o = (size_t)row * ns * kp;
+  topk_body<true, true>(nullptr, cand + o, ckeys + o, ns * kp, kp, sel + (size_t)row * n_sel, nullptr, 0,
+                        ctx - Tc, Tc, false);
+}
+
 }  // namespace
 
+int topk_slices(int Tc, int kp, int* slen) {
+  if (Tc <= kLdsKeys || kp <= 0) return 0;
+  const int ns = ceil_div(Tc, kLdsKeys);
+  const int len = (ceil_div(Tc, ns) + 3) / 4 * 4;
+  const int last = Tc - (ns - 1) * len;
+  if (len > kLdsKeys || last <= kp || (long)ns * kp > kLdsKeys) return 0;
+  if (slen) *slen = len;
+  return ns;
+}
+
+size_t topk_candidate_bytes(int rows, int Tc, int kp) {
+  const int ns = topk_slices(Tc, kp, nullptr);
+  return ns ? (size_t)rows * ns * kp * 8 : 0;  // positions, then keys
+}
+
 hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, int Tc, int kp,
-                              int ctx, int n_sel, hipStream_t st) {
+                              int ctx, int n_sel, int32_t* cand, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   const bool vec = (ldS & 3) == 0 && ((uintptr_t)S & 15) == 0;
-  if (Tc <= kLdsKeys)
+  int slen = 0;
+  const int ns = cand ? topk_slices(Tc, kp, &slen) : 0;
+  if (Tc <= kLdsKeys) {
     topk_window_kernel<true><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec);
-  else
+  } else if (ns > 0) {
+    uint32_t* ckeys = (uint32_t*)(cand + (size_t)rows * ns * kp);
+    topk_slice_kernel<<<rows * ns, kThreads, 0, st>>>(S, cand, ckeys, Tc, ldS, kp, slen, ns, vec);
+    topk_merge_kernel<<<rows, kThreads, 0, st>>>(cand, ckeys, sel, Tc, kp, ns, ctx, n_sel);
+  } else {
     topk_window_kernel<false><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec);
+  }
   return hipGetLastError();
 }
 

@@ -27,9 +27,14 @@ hipError_t launch_latent_score(int dtype, const float* qpart, int npart, const v
                                int ldS, int B, int G, int r, int Tc, int ctx_cap, hipStream_t st);
 
 // sel[row][0 .. kp) = top-kp of S[row][0 .. Tc) (ties to the lowest index), ascending;
-// sel[row][kp .. n_sel) = Tc .. ctx-1. Rows of S are ldS floats apart.
+// sel[row][kp .. n_sel) = Tc .. ctx-1. Rows of S are ldS floats apart. Rows longer than 32768
+// candidates are split into topk_slices(...) slices whose candidates (positions, then their
+// keys: topk_candidate_bytes(...) bytes) go to `cand`; with cand null, or no valid split, one
+// workgroup per row reads the row from memory in every pass instead.
+int topk_slices(int Tc, int kp, int* slen);
+size_t topk_candidate_bytes(int rows, int Tc, int kp);
 hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, int Tc, int kp,
-                              int ctx, int n_sel, hipStream_t st);
+                              int ctx, int n_sel, int32_t* cand, hipStream_t st);
 
 // Gather + rebuild + RoPE + attention over the selected rows, split along the selected set.
 // With n_splits == 1 the normalised result goes to out; otherwise (m, l, o) partials go to part.

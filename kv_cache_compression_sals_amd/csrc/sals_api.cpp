@@ -62,7 +62,7 @@ struct DecodePlan {
   int split_len, n_splits;
   bool shared;  // value side by the shared-selection kernels (one selection per >= 4 KV heads)
   sals::ValuePlan vp;
-  size_t off_qpart, off_S, off_sel, off_part, off_p, off_pstat, off_zp, total;
+  size_t off_qpart, off_cand, off_S, off_sel, off_part, off_p, off_pstat, off_zp, total;
 };
 
 sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_t ctx,
@@ -96,6 +96,8 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   size_t off = 0;
   p->off_qpart = off;
   off += align_up((size_t)p->npart * s->B * sel->G * s->r * 4);
+  p->off_cand = off;
+  off += align_up(sals::topk_candidate_bytes(s->B * sel->G, p->Tc, p->kp));
   p->off_S = off;
   off += align_up((size_t)s->B * sel->G * p->ldS * 4);
   p->off_sel = off;
@@ -209,7 +211,8 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
                                   ctx_cap, hs);
   mark(2);
   if (e == hipSuccess)
-    e = sals::launch_topk_window(S, p.ldS, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel, hs);
+    e = sals::launch_topk_window(S, p.ldS, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel,
+                                 (int32_t*)(w + p.off_cand), hs);
   mark(3);
   if (e == hipSuccess)
     e = sals::launch_select_attend(s->dtype, q, Lk, Lv, Pk, Pv, selb, out, part, pbuf, pstat,
@@ -339,7 +342,7 @@ sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const v
     e = sals::launch_importance_accum(c->dtype, K, Qobs, stats, I, c->B, c->H_q, c->H_kv, c->d, w,
                                       ctx_cap, ctx, hs);
   if (e == hipSuccess)
-    e = sals::launch_topk_window(I, ctx, kept, c->B * c->H_kv, ctx, k_keep, ctx, k_keep, hs);
+    e = sals::launch_topk_window(I, ctx, kept, c->B * c->H_kv, ctx, k_keep, ctx, k_keep, nullptr, hs);
   if (e == hipSuccess)
     e = sals::launch_gather_rows(c->dtype, K, V, kept, Kc, Vc, c->B * c->H_kv, c->d, ctx_cap,
                                  k_keep, hs);

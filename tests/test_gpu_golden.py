@@ -64,13 +64,19 @@ def _split_scores(name, T):
 
 SPLIT = [("ties_across_slices", 8000, 1000, 16), ("two_values", 6000, 2500, 8),
          ("signed_zeros_and_ones", 7000, 3000, 32), ("list_overflow", 20000, 500, 64),
-         ("ascending", 5000, 777, 0)]
+         ("ascending", 5000, 777, 0),
+         # rows past 32768 candidates: per-slice candidates, then one selection over them
+         ("ties_across_slices", 70000, 4000, 16), ("two_values", 50000, 9000, 8),
+         ("list_overflow", 100000, 6000, 64), ("ascending", 90000, 5000, 0),
+         # too many candidates for the slice path: one workgroup reads the row in every pass
+         ("two_values", 40000, 20000, 0)]
 
 
-@pytest.mark.parametrize("name,T,k,w", SPLIT, ids=[c[0] for c in SPLIT])
+@pytest.mark.parametrize("name,T,k,w", SPLIT, ids=[f"{c[0]}_T{c[1]}" for c in SPLIT])
 def test_split_selection_ties(name, T, k, w):
-    """Rows long enough for the many-workgroups-per-row selection, with exact ties at the
-    threshold spread over every slice: the set must be the top-k by (score desc, index asc)."""
+    """Rows with exact ties at the threshold spread over the whole row (and, past 32768
+    candidates, over every slice of the two-kernel selection): the set must be the top-k by
+    (score desc, index asc)."""
     d = r = 64
     scores = _split_scores(name, T - w)
     rs = np.random.default_rng(3)
