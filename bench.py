@@ -63,7 +63,8 @@ def shared_value(cfg):
 KDIR = os.path.join(ROOT, "kv_cache_compression_sals_amd", "csrc")
 # sources whose change invalidates a kernel's stored traffic counters
 KERNEL_SOURCES = {
-    "select_attend": ["kernels/select_attend.inc", "kernels/select_attend_bf16_d128.hip", "common.h"],
+    "select_attend": ["kernels/select_attend.inc", "kernels/select_attend_bf16_d128.hip",
+                      "kernels/select_shared.hip", "common.h"],
     "latent_score": ["kernels/latent_score.hip", "common.h"],
     "topk_window": ["kernels/topk.hip", "common.h"],
     "latent_query": ["kernels/latent_query.hip", "common.h"],

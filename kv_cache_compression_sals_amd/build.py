@@ -33,6 +33,7 @@ SOURCES = [
     "kernels/select_attend_f32_d128.hip",
     "kernels/select_attend_f32_d64.hip",
     "kernels/value.hip",
+    "kernels/select_shared.hip",
     "kernels/project.hip",
     "kernels/compact.hip",
 ]

@@ -47,6 +47,18 @@ hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const 
                                 int d, int r, int G, int ctx_cap, int ctx, int n_sel,
                                 int split_len, int n_splits, float rope_base, hipStream_t st);
 
+// Key side when one selection serves several KV heads (bf16, d = 128, an even number of KV heads
+// per group, at most 4 query heads per KV head, r in {128, 256, 384, 512}): the K rebuild of two
+// KV heads over one split of shared_keys_split() selected tokens per workgroup, then RoPE,
+// logits and the softmax over the split, written as pbuf / pstat (as select_attend's
+// shared-selection mode) for the value kernels below.
+bool shared_keys_supported(int dtype, int H_q, int H_kv, int G, int d, int r);
+int shared_keys_split();
+hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, const int32_t* sel,
+                              float* pbuf, float* pstat, int B, int H_q, int H_kv, int G, int r,
+                              int ctx_cap, int ctx, int n_sel, int n_splits, float rope_base,
+                              hipStream_t st);
+
 // Value side for selection groups shared by several KV heads (the group's rows are read once
 // per column block instead of once per KV head):
 //   zpart[c][b][h][j] = w[b][h][split(c)] sum_{t in chunk c} pbuf[b][h][t] L_v[b][sel[t]][j]

@@ -61,6 +61,7 @@ struct DecodePlan {
   int rb, npart;  // latent-query row block and parts per group
   int split_len, n_splits;
   bool shared;  // value side by the shared-selection kernels (one selection per >= 4 KV heads)
+  bool skeys;   // key side of a shared selection by the two-head tile kernel
   sals::ValuePlan vp;
   size_t off_qpart, off_cand, off_S, off_sel, off_part, off_p, off_pstat, off_zp, total;
 };
@@ -102,9 +103,23 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   off += align_up((size_t)s->B * sel->G * p->ldS * 4);
   p->off_sel = off;
   off += align_up((size_t)s->B * sel->G * p->n_sel * 4);
+  p->skeys = s->H_kv / sel->G >= 4 &&
+             sals::shared_keys_supported(s->dtype, s->H_q, s->H_kv, sel->G, s->d, s->r);
+  if (p->skeys) {  // splits of the tile kernel's token count
+    p->split_len = sals::shared_keys_split();
+    p->n_splits = (p->n_sel + p->split_len - 1) / p->split_len;
+  }
   p->shared = s->H_kv / sel->G >= 4 &&
               sals::value_plan(s->dtype, s->B, s->H_q, s->H_kv, sel->G, s->r, p->n_sel,
                                p->split_len, p->n_splits, &p->vp);
+  if (p->skeys && !p->shared) {  // no value plan for the tile kernel's splits: the general path
+    p->skeys = false;
+    p->split_len = split;
+    p->n_splits = (p->n_sel + split - 1) / split;
+    p->shared = sals::value_plan(s->dtype, s->B, s->H_q, s->H_kv, sel->G, s->r, p->n_sel,
+                                 p->split_len, p->n_splits, &p->vp);
+  }
+  if ((long)p->n_splits * s->H_kv * s->B > 0x7fffffffL) return SALS_ERR_RANGE;
   p->off_part = off;
   if (p->n_splits > 1 && !p->shared)
     off += align_up((size_t)s->B * s->H_q * p->n_splits * (s->d + 2) * 4);
@@ -214,7 +229,10 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
     e = sals::launch_topk_window(S, p.ldS, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel,
                                  (int32_t*)(w + p.off_cand), hs);
   mark(3);
-  if (e == hipSuccess)
+  if (e == hipSuccess && p.skeys)
+    e = sals::launch_shared_keys(q, Lk, Pk, selb, pbuf, pstat, s->B, s->H_q, s->H_kv, G, s->r,
+                                 ctx_cap, ctx, p.n_sel, p.n_splits, rope_base, hs);
+  else if (e == hipSuccess)
     e = sals::launch_select_attend(s->dtype, q, Lk, Lv, Pk, Pv, selb, out, part, pbuf, pstat,
                                    s->B, s->H_q, s->H_kv, s->d, s->r, G, ctx_cap, ctx, p.n_sel,
                                    p.split_len, p.n_splits, rope_base, hs);
