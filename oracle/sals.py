@@ -221,3 +221,42 @@ def decode_step(q, Lk, Lv, Pk, Pv, *, ctx: int, k: int, w: int, G: int, H_kv: in
         sel[b] = np.stack(sets)
         out[b], _ = attend_selected(qf[b], Lkb, Lvb, Pkf, Pvf, sets, T, base, H_kv, G)
     return dict(out=out, sel=sel, S=S, T_c=T_c, n_sel=n_sel)
+
+
+# ----------------------------------------------------------------------------------------------
+# the dense baseline the selection replaces: the whole latent cache rebuilt and rotated, then
+# plain attention over every token
+# ----------------------------------------------------------------------------------------------
+
+def reconstruct_cache(L: np.ndarray, P: np.ndarray, t0: int, T: int, H_kv: int, base: Optional[float]):
+    """Rows [t0, t0 + T) of one sequence rebuilt for every KV head: out[g, t - t0] = L[t] . P[g]^T,
+    then rotated at the absolute position t when ``base`` is given (keys) and left as is when it is
+    None (values). L[>= t0 + T, r], P[D, r] fp64; returns [H_kv, T, d].
+    (SALS 问题定义 and abstract: an uncompressed attention needs every key rebuilt before RoPE;
+    技术框架 stage 3 is the same product over the selected rows only.)"""
+    d = P.shape[0] // H_kv
+    pos = np.arange(t0, t0 + T)
+    out = np.empty((H_kv, T, d))
+    for g in range(H_kv):
+        rows = reconstruct(L[t0:t0 + T], P[g * d:(g + 1) * d])
+        out[g] = rope(rows, pos, base) if base is not None else rows
+    return out
+
+
+def dense_baseline(q, Lk, Lv, Pk, Pv, *, ctx: int, H_kv: int, base: float, dtype: str,
+                   batches: Optional[list] = None) -> np.ndarray:
+    """Attention of each query head over all ctx tokens of the rebuilt cache:
+    o_h = softmax(RoPE(q_h, ctx-1) . K_g^T / sqrt(d)) . V_g with K_g, V_g = reconstruct_cache(...)
+    over [0, ctx), g = kv(h). Stored inputs as in decode_step; returns fp64 out[B, H_q, d]."""
+    qf = stored_to_f64(q, dtype)
+    Pkf, Pvf = stored_to_f64(Pk, dtype), stored_to_f64(Pv, dtype)
+    B, H_q, d = qf.shape
+    out = np.full((B, H_q, d), np.nan)
+    for b in (range(B) if batches is None else batches):
+        K = reconstruct_cache(stored_to_f64(Lk[b, :ctx], dtype), Pkf, 0, ctx, H_kv, base)
+        V = reconstruct_cache(stored_to_f64(Lv[b, :ctx], dtype), Pvf, 0, ctx, H_kv, None)
+        for h in range(H_q):
+            g = kv_head_of(h, H_q, H_kv)
+            qh = rope(qf[b, h][None, :], ctx - 1, base)[0]
+            out[b, h] = _softmax(K[g] @ qh / np.sqrt(d)) @ V[g]
+    return out

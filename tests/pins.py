@@ -292,6 +292,47 @@ def pin_compact_identity_and_masked():
             assert np.allclose(Ib, ref_I, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------------------------
+# the full-rebuild baseline
+# ---------------------------------------------------------------------------------------------
+
+def pin_reconstruct_cache_identity():
+    """P = I (r = H_kv*d): the rebuilt rows of head g are its slice of the input, rotated at the
+    absolute position t (complex form, loops) for keys and unchanged for values, also with t0 > 0."""
+    H_kv, d, t0, T = 3, 8, 5, 7
+    D = H_kv * d
+    L = _rand(31, t0 + T + 2, D)
+    Kc = OS.reconstruct_cache(L, np.eye(D), t0, T, H_kv, 500.0)
+    Vc = OS.reconstruct_cache(L, np.eye(D), t0, T, H_kv, None)
+    for g in range(H_kv):
+        for j in range(T):
+            row = L[t0 + j, g * d:(g + 1) * d]
+            ref = brute.rope_complex(row.tolist(), t0 + j, 500.0)
+            assert np.allclose(Kc[g, j], ref, atol=TOL, rtol=0), (g, j)
+            assert np.array_equal(Vc[g, j], row)
+
+
+def pin_dense_baseline_identity_and_full_selection():
+    """P = I: the baseline is dense RoPE attention over the whole cache (loops, complex RoPE).
+    With a lossy P and k + w >= T, SALS selects every token, so it equals the baseline."""
+    for i, (H_q, H_kv, G, d) in enumerate(SHAPES):
+        D = H_kv * d
+        T = 13 + i
+        rs = np.random.default_rng(700 + i)
+        K, V, q = rs.standard_normal((T, D)), rs.standard_normal((T, D)), rs.standard_normal((H_q, d))
+        out = OS.dense_baseline(q[None], K[None], V[None], np.eye(D), np.eye(D), ctx=T, H_kv=H_kv,
+                                base=10000.0, dtype="f64")
+        ref = brute.dense_rope_attention(q.tolist(), K.tolist(), V.tolist(), range(T), T, 10000.0, H_q, H_kv, d)
+        assert np.allclose(out[0], ref, atol=TOL, rtol=0), (H_q, H_kv, G, d)
+        r = max(2, D // 2)
+        Pk, Pv = _orthogonal(710 + i, D, r), _orthogonal(720 + i, D, r)
+        Lk, Lv = rs.standard_normal((T, r)), rs.standard_normal((T, r))
+        base_out = OS.dense_baseline(q[None], Lk[None], Lv[None], Pk, Pv, ctx=T, H_kv=H_kv, base=10000.0,
+                                     dtype="f64")
+        sals_out = _run_decode(q, Lk, Lv, Pk, Pv, T, T, 3, G, H_kv)["out"]
+        assert np.allclose(base_out, sals_out, atol=TOL, rtol=0), (H_q, H_kv, G, d)
+
+
 PINS = [
     pin_rope_d2_closed_form,
     pin_rope_complex_form,
@@ -306,4 +347,6 @@ PINS = [
     pin_importance_bruteforce_and_mass,
     pin_importance_closed_forms,
     pin_compact_identity_and_masked,
+    pin_reconstruct_cache_identity,
+    pin_dense_baseline_identity_and_full_selection,
 ]

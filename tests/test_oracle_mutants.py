@@ -47,6 +47,12 @@ MUTANTS = [
      "return np.asarray(X, dtype=np.float64) @ np.asarray(P, dtype=np.float64).T", "projection transposed"),
     ("sals.py", "    e = np.exp(logits - m)\n    return e / e.sum()", "    e = np.exp(logits - m)\n    return e",
      "softmax not normalised"),
+    ("sals.py", "pos = np.arange(t0, t0 + T)", "pos = np.arange(T)", "rebuilt keys rotated relative to t0"),
+    ("sals.py", "out[g] = rope(rows, pos, base) if base is not None else rows",
+     "out[g] = rope(rows, pos, base if base is not None else 10000.0)", "rebuilt values rotated"),
+    ("sals.py", "qh = rope(qf[b, h][None, :], ctx - 1, base)[0]", "qh = qf[b, h]", "baseline query not rotated"),
+    ("sals.py", "V = reconstruct_cache(stored_to_f64(Lv[b, :ctx], dtype), Pvf, 0, ctx, H_kv, None)",
+     "V = reconstruct_cache(stored_to_f64(Lv[b, :ctx], dtype), Pkf, 0, ctx, H_kv, None)", "baseline values from P_k"),
     ("compact.py", "a = _softmax(K[: p + 1] @ Qobs[i] / np.sqrt(d))\n        I[: p + 1] += a",
      "a = _softmax(K[:T] @ Qobs[i] / np.sqrt(d))\n        I[:T] += a", "causal mask dropped"),
     ("compact.py", "p = T - w + i", "p = T - w + i + 1 if i < w - 1 else T - 1", "observation positions shifted"),
