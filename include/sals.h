@@ -213,6 +213,33 @@ sals_status sals_dense_decode(const kvc_shape* c, const void* q, const void* K, 
                               int32_t n, int32_t stride_tokens, float* out, void* ws,
                               size_t ws_bytes, sals_stream_t stream);
 
+/*
+ * sals_reconstruct_kv - full reconstruction of latent cache rows into a plain post-RoPE KV cache:
+ * the dense baseline SALS replaces (SALS 问题定义 and abstract: the whole low-rank cache must be
+ * rebuilt before RoPE can be applied; 技术框架 stage 3 rebuilds only the selected rows).
+ *   K[b, g, t, :] = RoPE_t(L_k[b, t, :] . P_k[g]^T),  V[b, g, t, :] = L_v[b, t, :] . P_v[g]^T
+ *   for t in [t0, t0 + T), every KV head g; RoPE (rotate-half, theta_i = base^(-2i/d)) at the
+ *   absolute position t. With q given, also q_rot[b, h] = RoPE_{q_pos}(q[b, h]).
+ *   sals_dense_decode over K, V and q_rot then gives attention over the whole rebuilt cache.
+ * Args
+ *   s             shape; dtype must be SALS_BF16, d = 128, H_kv even, r in {128, 256, 384, 512}.
+ *   rope_base     RoPE base (e.g. 10000).
+ *   Lk, Lv        [B, ctx_cap, r] bf16, rows [t0, t0 + T) read. Lv may be NULL (then Pv and V
+ *                 must be NULL too: K only).
+ *   Pk, Pv        [H_kv * d, r] bf16, read.
+ *   K, V          [B, H_kv, stride_tokens, d] bf16; rows [t0, t0 + T) written, others untouched.
+ *   q, q_rot      [B, H_q, d] bf16, pre-RoPE query read and rotated query written; both NULL to
+ *                 skip. q_pos >= 0 is the query's position.
+ * Arithmetic: bf16 products, fp32 sums, rotation in fp32 with the angle reduced in fp64, one
+ * rounding to bf16 (nearest even) per output element.
+ * Errors: NULL (K side or the q pair incomplete), DTYPE (not bf16), SHAPE, RANGE (T < 1, t0 < 0,
+ * t0 + T > ctx_cap or > stride_tokens, q_pos < 0), ALIGN, HIP on launch failure.
+ */
+sals_status sals_reconstruct_kv(const sals_shape* s, float rope_base, const void* Lk,
+                               const void* Lv, const void* Pk, const void* Pv, int32_t ctx_cap,
+                               int32_t t0, int32_t T, void* K, void* V, int32_t stride_tokens,
+                               const void* q, void* q_rot, int32_t q_pos, sals_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,4 +16,5 @@ from .binding import (  # noqa: F401
     sals_dense_decode,
     sals_dense_decode_workspace_bytes,
     sals_project_kv,
+    sals_reconstruct_kv,
 )

@@ -217,3 +217,20 @@ def sals_dense_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, *, n: O
         ctypes.byref(c), _ptr(q), _ptr(K), _ptr(V), n, stride, _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+# ---- full reconstruction (the dense baseline) -------------------------------------------------
+
+def sals_reconstruct_kv(Lk: torch.Tensor, Pk: torch.Tensor, K: torch.Tensor, *, t0: int, T: int, d: int,
+                        rope_base: float = 10000.0, Lv: Optional[torch.Tensor] = None,
+                        Pv: Optional[torch.Tensor] = None, V: Optional[torch.Tensor] = None,
+                        q: Optional[torch.Tensor] = None, q_rot: Optional[torch.Tensor] = None,
+                        q_pos: int = 0, stream=None) -> None:
+    """K[:, :, t0:t0+T] = RoPE_t(L_k . P_k^T) (and V without RoPE); with q, q_rot = RoPE_{q_pos}(q).
+    Lk/Lv [B, ctx_cap, r]; Pk/Pv [H_kv*d, r]; K/V [B, H_kv, stride_tokens, d]; q/q_rot [B, H_q, d]."""
+    B, H_kv, stride, _ = K.shape
+    H_q = q.shape[1] if q is not None else H_kv
+    s = SalsShape(B, H_q, H_kv, d, Pk.shape[1], _dtype(Lk, Pk, K, Lv, Pv, V, q, q_rot))
+    _check("sals_reconstruct_kv", lib().sals_reconstruct_kv(
+        ctypes.byref(s), ctypes.c_float(rope_base), _ptr(Lk), _ptr(Lv), _ptr(Pk), _ptr(Pv), Lk.shape[1],
+        t0, T, _ptr(K), _ptr(V), stride, _ptr(q), _ptr(q_rot), q_pos, _stream(stream)))

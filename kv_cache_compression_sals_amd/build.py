@@ -34,6 +34,7 @@ SOURCES = [
     "kernels/select_attend_f32_d64.hip",
     "kernels/value.hip",
     "kernels/select_shared.hip",
+    "kernels/reconstruct.hip",
     "kernels/project.hip",
     "kernels/compact.hip",
 ]

@@ -59,6 +59,17 @@ hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, con
                               int ctx_cap, int ctx, int n_sel, int n_splits, float rope_base,
                               hipStream_t st);
 
+// Full reconstruction of cache rows [t0, t0 + T) into a post-RoPE KV cache [B, H_kv,
+// stride_tokens, d] (bf16, d = 128, an even H_kv, r in {128, 256, 384, 512}); V (and Lv, Pv)
+// may be null. launch_rope_query rotates rows of q ([rows, d], bf16) at one position.
+bool reconstruct_supported(int dtype, int H_kv, int d, int r);
+long reconstruct_grid(int B, int H_kv, int T, bool with_v);
+hipError_t launch_reconstruct(const void* Lk, const void* Lv, const void* Pk, const void* Pv, void* K,
+                              void* V, int B, int H_kv, int r, int ctx_cap, int t0, int T,
+                              int stride_tokens, float rope_base, hipStream_t st);
+hipError_t launch_rope_query(const void* q, void* q_rot, int rows, int pos, float rope_base,
+                             hipStream_t st);
+
 // Value side for selection groups shared by several KV heads (the group's rows are read once
 // per column block instead of once per KV head):
 //   zpart[c][b][h][j] = w[b][h][split(c)] sum_{t in chunk c} pbuf[b][h][t] L_v[b][sel[t]][j]

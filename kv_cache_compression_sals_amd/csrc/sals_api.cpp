@@ -296,6 +296,33 @@ sals_status sals_project_kv(const sals_shape* s, const void* Xk, const void* Xv,
   return e == hipSuccess ? SALS_OK : hip_fail(e);
 }
 
+sals_status sals_reconstruct_kv(const sals_shape* s, float rope_base, const void* Lk,
+                               const void* Lv, const void* Pk, const void* Pv, int32_t ctx_cap,
+                               int32_t t0, int32_t T, void* K, void* V, int32_t stride_tokens,
+                               const void* q, void* q_rot, int32_t q_pos, sals_stream_t stream) {
+  if (!s || !Lk || !Pk || !K) return SALS_ERR_NULL;
+  const bool with_v = Lv != nullptr;
+  if (with_v != (Pv != nullptr) || with_v != (V != nullptr)) return SALS_ERR_NULL;
+  if ((q != nullptr) != (q_rot != nullptr)) return SALS_ERR_NULL;
+  sals_status st = check_layer_shape(s);
+  if (st != SALS_OK) return st;
+  if (s->dtype != SALS_BF16) return SALS_ERR_DTYPE;
+  if (!sals::reconstruct_supported(s->dtype, s->H_kv, s->d, s->r)) return SALS_ERR_SHAPE;
+  if (T < 1 || t0 < 0 || ctx_cap < 1 || (long)t0 + T > ctx_cap || (long)t0 + T > stride_tokens ||
+      T > (1 << 26) || (q && q_pos < 0))
+    return SALS_ERR_RANGE;
+  if (sals::reconstruct_grid(s->B, s->H_kv, T, with_v) > 0x7fffffffL) return SALS_ERR_RANGE;
+  if (misaligned(Lk) || misaligned(Lv) || misaligned(Pk) || misaligned(Pv) || misaligned(K) ||
+      misaligned(V) || misaligned(q) || misaligned(q_rot))
+    return SALS_ERR_ALIGN;
+  if ((st = device_ready()) != SALS_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = sals::launch_reconstruct(Lk, Lv, Pk, Pv, K, V, s->B, s->H_kv, s->r, ctx_cap, t0, T,
+                                          stride_tokens, rope_base, hs);
+  if (e == hipSuccess && q) e = sals::launch_rope_query(q, q_rot, s->B * s->H_q, q_pos, rope_base, hs);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
 sals_status sals_decode_workspace_bytes(const sals_shape* s, const sals_select* sel, int32_t ctx,
                                         size_t* bytes) {
   if (!bytes) return SALS_ERR_NULL;

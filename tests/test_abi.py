@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     L = lib()
     for n in names:
         assert hasattr(L, n), n
@@ -149,6 +149,28 @@ def test_dense_decode_argument_errors():
     assert L.sals_dense_decode(ctypes.byref(c), P, P, None, 10, 10, P, P, 1 << 20, None) == NULL
     assert L.sals_dense_decode(ctypes.byref(c), P, P, P, 11, 10, P, P, 1 << 20, None) == RANGE
     assert L.sals_dense_decode(ctypes.byref(c), P, P, P, 0, 10, P, P, 1 << 20, None) == RANGE
+
+
+def test_reconstruct_argument_errors():
+    L = lib()
+
+    def call(s=SalsShape(2, 8, 4, 128, 256, 1), Lk=P, Lv=P, Pv=P, V=P, cap=100, t0=0, T=100, stride=100,
+             q=None, q_rot=None, q_pos=0):
+        return L.sals_reconstruct_kv(ctypes.byref(s), ctypes.c_float(10000.0), Lk, Lv, P, Pv, cap, t0, T, P, V,
+                                     stride, q, q_rot, q_pos, None)
+
+    assert call(Lk=None) == NULL
+    assert call(V=None) == NULL  # V pointers must be all NULL or all set
+    assert call(q=P) == NULL     # q and q_rot come together
+    assert call(s=SalsShape(2, 8, 4, 128, 256, 0)) == DTYPE
+    assert call(s=SalsShape(2, 8, 4, 64, 256, 1)) == SHAPE
+    assert call(s=SalsShape(2, 6, 3, 128, 256, 1)) == SHAPE   # odd number of KV heads
+    assert call(s=SalsShape(2, 8, 4, 128, 64, 1)) == SHAPE
+    assert call(T=0) == RANGE
+    assert call(t0=1) == RANGE
+    assert call(stride=99) == RANGE
+    assert call(q=P, q_rot=P, q_pos=-1) == RANGE
+    assert call(Lv=P + 8) == ALIGN
 
 
 def _gpu_present():
