@@ -222,7 +222,57 @@ def run_workload(cfg, steps, warmup, label):
     event_step_us = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(steps)) / steps * 1e3
     del graph, copies
     torch.cuda.empty_cache()
-    return dict(case=case, us=us_step, stage_us=stage_us, event_step_us=event_step_us, eager_us=eager_us)
+    comp = run_comparators(cfg, base, ctx, steps, warmup) if cfg.dtype == "bf16" else None
+    return dict(case=case, us=us_step, stage_us=stage_us, event_step_us=event_step_us, eager_us=eager_us,
+                comparators=comp)
+
+
+def run_comparators(cfg, base, ctx, steps, warmup):
+    """The dense baselines on the same layer: (a) sals_dense_decode over the whole post-RoPE bf16
+    KV cache (flash-decode, split over the context); (b) the full rebuild the selection avoids,
+    sals_reconstruct_kv of every token (K rotated, V, the rotated query) followed by (a). Each is
+    timed as `steps` back-to-back calls between two HIP events; the rebuilt cache (2 x 268 MB at
+    these shapes) is larger than the MALL, so every call reads it from HBM."""
+    import torch
+
+    import kv_cache_compression_sals_amd as sals
+
+    q, Lk, Lv, Pk, Pv = (base[n] for n in ("q", "Lk", "Lv", "Pk", "Pv"))
+    B, H_q, d = q.shape
+    H_kv, r = cfg.H_kv, cfg.r
+    K = torch.empty((B, H_kv, ctx, d), dtype=q.dtype, device="cuda")
+    V, q_rot = torch.empty_like(K), torch.empty_like(q)
+    out = torch.empty((B, H_q, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sals.sals_dense_decode_workspace_bytes(q_rot, K, n=ctx), dtype=torch.uint8, device="cuda")
+    rebuild = lambda: sals.sals_reconstruct_kv(Lk, Pk, K, t0=0, T=ctx, d=d, rope_base=cfg.base, Lv=Lv, Pv=Pv,
+                                               V=V, q=q, q_rot=q_rot, q_pos=ctx - 1)
+    dense = lambda: sals.sals_dense_decode(q_rot, K, V, n=ctx, out=out, workspace=ws)
+
+    def both():
+        rebuild()
+        dense()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    rebuild_us, dense_us, naive_us = timed(rebuild), timed(dense), timed(both)
+    kv_bytes = 2 * B * H_kv * ctx * d * 2
+    rebuild_flops = 2 * 2 * B * ctx * r * H_kv * d
+    del K, V, ws
+    torch.cuda.empty_cache()
+    return dict(dense_full_kv_us=round(dense_us, 2), dense_full_kv_gbps=round(kv_bytes / (dense_us * 1e-6) / 1e9, 1),
+                full_rebuild_us=round(rebuild_us, 2),
+                full_rebuild_tflops=round(rebuild_flops / (rebuild_us * 1e-6) / 1e12, 1),
+                full_rebuild_then_dense_us=round(naive_us, 2), kv_bytes=kv_bytes, rebuild_flops=rebuild_flops)
 
 
 def run_compact_workload(cfg, steps, warmup, label):
@@ -398,7 +448,10 @@ def summary(cfg, r, label):
         k_rebuild_tflops=round(alg["k_rebuild_flops"] / (r["stage_us"]["select_attend"] * 1e-6) / 1e12, 1),
         compulsory_bytes=alg["compulsory"],
         roofline=rl,
-    )
+    ) | ({} if not r.get("comparators") else dict(comparators=dict(
+        r["comparators"],
+        speedup_vs_dense_full_kv=round(r["comparators"]["dense_full_kv_us"] / r["us"], 2),
+        speedup_vs_full_rebuild=round(r["comparators"]["full_rebuild_then_dense_us"] / r["us"], 2))))
 
 
 def main():

@@ -249,41 +249,67 @@ __global__ void gather_rows_kernel(const u32x4* __restrict__ K, const u32x4* __r
   Vc[e] = V[src];
 }
 
-// Dense flash-decode over a contiguous cache, one query head per workgroup and split.
-// Lane l of a wave reads token l/4, columns (l%4)*DH/4 .. : 4 lanes share one row.
+// Dense flash-decode over a contiguous cache. A workgroup takes one split of one KV head for NG
+// of its query heads (NG = 4, 2 or 1, dividing the query heads per KV head): wave w computes
+// head w % NG over token phase w / NG, so with NG > 1 the waves of a CU read the same K/V rows
+// at about the same time and all but the first find them in L1. Four lanes share one token row:
+// load instruction i of lane l reads 16-byte piece 4i + l%4 of row l/4, so the four lanes of a
+// row read 64 contiguous bytes per instruction. Each wave takes 16 tokens per step and issues the
+// next step's rows before it computes on the current ones. Grid: one dimension, XCD-aware order
+// with the head groups of one KV head fastest, then the split: the workgroups that read the same
+// rows run on one XCD at about the same time.
 template <class T, int DH>
 __global__ __launch_bounds__(kThreads) void dense_decode_kernel(
     const typename T::elem* __restrict__ q, const typename T::elem* __restrict__ K,
     const typename T::elem* __restrict__ V, float* __restrict__ out, float* __restrict__ part,
     int H_q, int H_kv, int n, int stride, int split_len, int n_splits) {
-  constexpr int CW = DH / 4;  // columns per lane
-  __shared__ float qsh[DH];
+  using elem = typename T::elem;
+  constexpr int CW = DH / 4;                     // columns per lane
+  constexpr int EPP = 16 / (int)sizeof(elem);    // elements per 16-byte piece
+  constexpr int NP = CW / EPP;                   // pieces per lane and row
+  __shared__ float qsh[4][DH];
   __shared__ float red[4][DH + 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (H_q / H_kv);
+  const int nqh = H_q / H_kv;
+  const int NG = dense_heads_per_group(nqh), NPH = 4 / NG, ngr = nqh / NG;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int gr = wg % ngr, sp = (wg / ngr) % n_splits, g = (wg / (ngr * n_splits)) % H_kv;
+  const int b = wg / (ngr * n_splits * H_kv);
+  const int myh = wave % NG, phase = wave / NG;
   const float scale = 1.0f / sqrtf((float)DH);
-  for (int c = tid; c < DH; c += kThreads) qsh[c] = T::to_f32(q[((size_t)b * H_q + h) * DH + c]) * scale;
+  for (int c = tid; c < NG * DH; c += kThreads)
+    qsh[c / DH][c % DH] = T::to_f32(q[((size_t)b * H_q + g * nqh + gr * NG + c / DH) * DH + c % DH]) * scale;
   __syncthreads();
-  const int cb = (lane & 3) * CW;
+  const int lq = lane & 3;
+  auto col = [&](int j) { return ((j / EPP) * 4 + lq) * EPP + j % EPP; };  // column of element j
   float qv[CW];
 #pragma unroll
-  for (int j = 0; j < CW; ++j) qv[j] = qsh[cb + j];
-  const typename T::elem* Kh = K + ((size_t)b * H_kv + g) * stride * DH;
-  const typename T::elem* Vh = V + ((size_t)b * H_kv + g) * stride * DH;
+  for (int j = 0; j < CW; ++j) qv[j] = qsh[myh][col(j)];
+  const elem* Kh = K + ((size_t)b * H_kv + g) * stride * DH;
+  const elem* Vh = V + ((size_t)b * H_kv + g) * stride * DH;
   const int jbeg = sp * split_len, jend = min(n, jbeg + split_len);
   float m = -INFINITY, l = 0.f;
   float o[CW];
 #pragma unroll
   for (int j = 0; j < CW; ++j) o[j] = 0.f;
-  for (int t0 = jbeg + wave * 16; t0 < jend; t0 += 64) {
-    const int t = t0 + (lane >> 2);
-    const bool ok = t < jend;
-    const int tt = ok ? t : jend - 1;
-    float x = 0.f;
-    const typename T::elem* kr = Kh + (size_t)tt * DH + cb;
+  auto load = [&](int t0, u32x4 (&kr)[NP], u32x4 (&vr)[NP]) {
+    const int tt = min(t0 + (lane >> 2), jend - 1);
 #pragma unroll
-    for (int j = 0; j < CW; ++j) x = fmaf(qv[j], T::to_f32(kr[j]), x);
+    for (int i = 0; i < NP; ++i) {
+      kr[i] = *(const u32x4*)(Kh + (size_t)tt * DH + (4 * i + lq) * EPP);
+      vr[i] = *(const u32x4*)(Vh + (size_t)tt * DH + (4 * i + lq) * EPP);
+    }
+  };
+  auto value = [&](const u32x4 (&r)[NP], int j) {
+    const uint32_t w = r[j / EPP][(j % EPP) * (int)sizeof(elem) / 4];
+    if constexpr (sizeof(elem) == 2) return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+    else return __uint_as_float(w);
+  };
+  auto step = [&](int t0, const u32x4 (&kr)[NP], const u32x4 (&vr)[NP]) {
+    const bool ok = t0 + (lane >> 2) < jend;
+    float x = 0.f;
+#pragma unroll
+    for (int j = 0; j < CW; ++j) x = fmaf(qv[j], value(kr, j), x);
     x += __shfl_xor(x, 1);
     x += __shfl_xor(x, 2);
     if (!ok) x = -INFINITY;
@@ -298,9 +324,19 @@ __global__ __launch_bounds__(kThreads) void dense_decode_kernel(
     ps += __shfl_xor(ps, 32);
     l = l * corr + ps;
     m = mn;
-    const typename T::elem* vr = Vh + (size_t)tt * DH + cb;
 #pragma unroll
-    for (int j = 0; j < CW; ++j) o[j] = fmaf(p, T::to_f32(vr[j]), o[j] * corr);
+    for (int j = 0; j < CW; ++j) o[j] = fmaf(p, value(vr, j), o[j] * corr);
+  };
+  u32x4 k0[NP], v0[NP], k1[NP], v1[NP];
+  const int tstep = 16 * NPH;
+  int t0 = jbeg + phase * 16;
+  if (t0 < jend) load(t0, k0, v0);
+  for (; t0 < jend; t0 += 2 * tstep) {
+    if (t0 + tstep < jend) load(t0 + tstep, k1, v1);
+    step(t0, k0, v0);
+    if (t0 + tstep >= jend) break;
+    if (t0 + 2 * tstep < jend) load(t0 + 2 * tstep, k0, v0);
+    step(t0 + tstep, k1, v1);
   }
   // reduce o over the 16 tokens of the wave (lanes with equal lane%4)
 #pragma unroll
@@ -314,27 +350,30 @@ __global__ __launch_bounds__(kThreads) void dense_decode_kernel(
   }
   if (lane < 4) {
 #pragma unroll
-    for (int j = 0; j < CW; ++j) red[wave][cb + j] = o[j];
+    for (int j = 0; j < CW; ++j) red[wave][col(j)] = o[j];
   }
   if (lane == 0) {
     red[wave][DH] = m;
     red[wave][DH + 1] = l;
   }
   __syncthreads();
-  float M = -INFINITY;
-  for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, red[wv][DH]);
-  float wgt[4], L = 0.f;
-  for (int wv = 0; wv < 4; ++wv) {
-    wgt[wv] = red[wv][DH] == -INFINITY ? 0.f : expf(red[wv][DH] - M);
-    L += red[wv][DH + 1] * wgt[wv];
-  }
-  for (int c = tid; c < DH; c += kThreads) {
-    float oc = 0.f;
-    for (int wv = 0; wv < 4; ++wv) oc += red[wv][c] * wgt[wv];
+  // head e of the group: waves e, e + NG, ... (its token phases), merged in phase order
+  for (int c2 = tid; c2 < NG * DH; c2 += kThreads) {
+    const int e = c2 / DH, c = c2 % DH;
+    float M = -INFINITY;
+    for (int ph = 0; ph < NPH; ++ph) M = fmaxf(M, red[ph * NG + e][DH]);
+    float L = 0.f, oc = 0.f;
+    for (int ph = 0; ph < NPH; ++ph) {
+      const int wv = ph * NG + e;
+      const float wgt = red[wv][DH] == -INFINITY ? 0.f : expf(red[wv][DH] - M);
+      L += red[wv][DH + 1] * wgt;
+      oc += red[wv][c] * wgt;
+    }
+    const int hq = g * nqh + gr * NG + e;
     if (n_splits == 1) {
-      out[((size_t)b * H_q + h) * DH + c] = oc / L;
+      out[((size_t)b * H_q + hq) * DH + c] = oc / L;
     } else {
-      float* pp = part + (((size_t)b * H_q + h) * n_splits + sp) * (DH + 2);
+      float* pp = part + (((size_t)b * H_q + hq) * n_splits + sp) * (DH + 2);
       pp[2 + c] = oc;
       if (c == 0) {
         pp[0] = M;
@@ -410,7 +449,7 @@ hipError_t launch_gather_rows(int dtype, const void* K, const void* V, const int
 hipError_t launch_dense_decode(int dtype, const void* q, const void* K, const void* V, float* out,
                                float* part, int B, int H_q, int H_kv, int d, int n, int stride,
                                int split_len, int n_splits, hipStream_t st) {
-  dim3 grid(n_splits, H_q, B);
+  dim3 grid(n_splits * (H_q / dense_heads_per_group(H_q / H_kv)) * B);
   SALS_KVC_DISPATCH(dtype, d,
                     (dense_decode_kernel<TT, DD><<<grid, kThreads, 0, st>>>(
                         (const TT::elem*)q, (const TT::elem*)K, (const TT::elem*)V, out, part, H_q,

@@ -123,6 +123,8 @@ hipError_t launch_gather_rows(int dtype, const void* K, const void* V, const int
                               hipStream_t st);
 
 // Flash-decode over a contiguous cache: partials per split, or out directly (n_splits == 1).
+// Query heads of one KV head that a dense-decode workgroup serves together: 4, 2 or 1.
+__host__ __device__ inline int dense_heads_per_group(int nqh) { return nqh % 4 == 0 ? 4 : nqh % 2 == 0 ? 2 : 1; }
 hipError_t launch_dense_decode(int dtype, const void* q, const void* K, const void* V, float* out,
                                float* part, int B, int H_q, int H_kv, int d, int n, int stride,
                                int split_len, int n_splits, hipStream_t st);

@@ -173,12 +173,15 @@ sals_status make_dense_plan(const kvc_shape* c, int32_t n, DensePlan* p) {
   if (st != SALS_OK) return st;
   if (n < 1 || n > (1 << 26)) return SALS_ERR_RANGE;
   const long heads = (long)c->B * c->H_q;
-  const int desired = (int)((1024 + heads - 1) / heads);
+  const long groups = heads / sals::dense_heads_per_group(c->H_q / c->H_kv);  // workgroups per split
+  // about 4096 workgroups (16 per CU), so that each one's serial pass over its split stays short
+  const int desired = (int)((4096 + groups - 1) / groups);
   int split = (n + desired - 1) / desired;
   split = (split + 63) / 64 * 64;
   if (split < 256) split = 256;
   p->split_len = split;
   p->n_splits = (n + split - 1) / split;
+  if (heads * p->n_splits > 0x7fffffffL) return SALS_ERR_RANGE;  // 1-D grid
   p->total = p->n_splits > 1 ? align_up((size_t)heads * p->n_splits * (c->d + 2) * 4) : 0;
   return SALS_OK;
 }

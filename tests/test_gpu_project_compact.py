@@ -152,3 +152,37 @@ def test_dense_decode_full_cache_matches_oracle():
     out = sals.sals_dense_decode(q, K, V, n=2999).cpu().numpy()
     ref = oracle.dense_decode(case["q"], case["K"], case["V"], n=2999, H_kv=4, dtype="bf16")
     assert np.abs(out - ref).max() <= 2e-2
+
+
+def _bf16_bits(x):
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+DENSE = [
+    # B, H_q, H_kv, d, n, stride, dtype: query heads per KV head 4, 2, 8, 3 and 1; one token
+    (2, 16, 4, 128, 5000, 5003, "bf16"),
+    (1, 16, 8, 64, 3001, 3001, "bf16"),
+    (2, 32, 4, 128, 1000, 1000, "bf16"),
+    (1, 12, 4, 128, 777, 800, "bf16"),
+    (3, 4, 4, 64, 1, 4, "bf16"),
+    (1, 8, 2, 128, 2000, 2000, "f32"),
+    (2, 6, 6, 64, 300, 310, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,H_q,H_kv,d,n,stride,dt", DENSE, ids=[f"nqh{c[1] // c[2]}_n{c[4]}_{c[6]}" for c in DENSE])
+def test_dense_decode_grouped_heads(B, H_q, H_kv, d, n, stride, dt):
+    """Every query head against the oracle at fp32 accuracy: the inputs are exact on both sides."""
+    print(f"dense B={B} H_q={H_q} H_kv={H_kv} d={d} n={n} stride={stride} {dt}", flush=True)
+    rs = np.random.default_rng(B * 1000 + H_q * 10 + n)
+    q = rs.standard_normal((B, H_q, d)).astype(np.float32)
+    K = rs.standard_normal((B, H_kv, stride, d)).astype(np.float32) * 1.5
+    V = rs.standard_normal((B, H_kv, stride, d)).astype(np.float32)
+    if dt == "bf16":
+        q, K, V = _bf16_bits(q), _bf16_bits(K), _bf16_bits(V)
+    out = sals.sals_dense_decode(to_device(q, dt), to_device(K, dt), to_device(V, dt), n=n).cpu().numpy()
+    ref = oracle.dense_decode(q, K, V, n=n, H_kv=H_kv, dtype=dt)
+    err = np.abs(out - ref).max()
+    print(f"   max err {err:.2e}", flush=True)
+    assert err <= 1e-4
