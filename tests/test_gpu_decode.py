@@ -54,6 +54,10 @@ SMALL = [
     ("shared_r384_nqh2", C3, dict(H_q=16, H_kv=8, d=128, r=384, G=2, k=120, w=16, rank=200, calib_tokens=512), 2, 1300, 1333),
     ("shared_hs24_splits", C3, dict(H_q=24, H_kv=12, d=64, r=128, G=1, k=300, w=20, rank=48, calib_tokens=256), 2, 2000, 2100),
     ("shared_hs128", C3, dict(H_q=128, H_kv=16, d=64, r=64, G=1, k=150, w=16, rank=32, calib_tokens=256), 1, 1000, 1000),
+    # the two-head key tile kernel (bf16, d = 128): r = 128 with 4 query heads per KV head over three
+    # splits (the last ragged), and r = 256 whose second split holds one token
+    ("skeys_r128_nqh4_ragged", C3, dict(H_q=32, H_kv=8, d=128, r=128, G=1, k=650, w=50, rank=64, calib_tokens=256), 1, 2000, 2000),
+    ("skeys_r256_one_token_split", C3, dict(H_q=8, H_kv=8, d=128, r=256, G=2, k=280, w=9, rank=100, calib_tokens=256), 2, 1500, 1500),
 ]
 
 
