@@ -16,9 +16,14 @@ W untimed eager steps run first. The K steps are then captured once as a HIP gra
 loop runs its decode step), replayed once untimed (upload), and the timed region is exactly one
 replay of the K steps between two device synchronisations: that is the value. Right after it,
 the same K steps are issued eagerly through sals_decode_step_traced, which records HIP events on
-the launch stream at every stage boundary; the events give each kernel's average duration
-(stage_us, and the roofline's avg_launch_us), and the host clock around that pass gives
-eager_us_per_step. One JSON line goes to stdout; progress goes to stderr.
+the launch stream at every stage boundary; the events give each stage's average duration
+(stage_us), and the host clock around that pass gives eager_us_per_step. The attention stage
+(select_attend, the dominant kernel) is bounded by events that the runtime records at its
+kernel's own start and end, so its figure (the roofline's avg_launch_us) is the kernel's duration
+without the launch gap before it; the other stages include that gap. Each step is also followed,
+outside the timed replay, by the dense baselines (comparators): flash-decode over the whole KV
+cache, and the full rebuild of the cache followed by it. One JSON line goes to stdout; progress
+goes to stderr.
 
 --calib-copy-mib M first copies an M MiB buffer with torch (a plain copy kernel of known size),
 so that a counter run can scale FETCH_SIZE / WRITE_SIZE to bytes.

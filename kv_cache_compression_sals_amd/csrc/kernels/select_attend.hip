@@ -19,9 +19,11 @@ hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const 
                                 const void* Pk, const void* Pv, const int32_t* sel, float* out,
                                 float* part, float* pbuf, float* pstat, int B, int H_q,
                                 int H_kv, int d, int r, int G, int ctx_cap, int ctx, int n_sel,
-                                int split_len, int n_splits, float rope_base, hipStream_t st) {
+                                int split_len, int n_splits, float rope_base, hipStream_t st,
+                                hipEvent_t t_start, hipEvent_t t_stop) {
   const sa::SAArgs a{q,     Lk,   Lv, Pk,      Pv,  sel,   out,       part,     pbuf,     pstat,
-                     B,     H_q,  H_kv, G,     ctx_cap, ctx, n_sel, split_len, n_splits, rope_base};
+                     B,     H_q,  H_kv, G,     ctx_cap, ctx, n_sel, split_len, n_splits, rope_base,
+                     t_start, t_stop};
   bool ok = false;
   if (dtype == 1 && d == 128) ok = sa::bf16_d128_launch(r, a, st);
   else if (dtype == 1 && d == 64) ok = sa::bf16_d64_launch(r, a, st);

@@ -280,20 +280,25 @@ int shared_keys_split() { return kTOK; }
 hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, const int32_t* sel,
                               float* pbuf, float* pstat, int B, int H_q, int H_kv, int G, int r,
                               int ctx_cap, int ctx, int n_sel, int n_splits, float rope_base,
-                              hipStream_t st) {
+                              hipStream_t st, hipEvent_t t_start, hipEvent_t t_stop) {
   const dim3 grid(n_splits * (H_kv / kNH) * B);
   const int nqh = H_q / H_kv;
   const auto* qq = (const uint16_t*)q;
   const auto* lk = (const uint16_t*)Lk;
   const auto* pk = (const uint16_t*)Pk;
-#define SALS_SK(RR, QQ)                                                                             \
-  shared_keys_kernel<RR, QQ><<<grid, kNT, 0, st>>>(qq, lk, pk, sel, pbuf, pstat, H_q, H_kv, G, ctx_cap, \
-                                                   ctx, n_sel, n_splits, rope_base)
-#define SALS_SK_R(RR)      \
-  if (nqh <= 1)            \
-    SALS_SK(RR, 1);        \
-  else                     \
-    SALS_SK(RR, 4);
+#define SALS_SK(RR, QQ)                                                                              \
+  if (t_start)                                                                                       \
+    hipExtLaunchKernelGGL(shared_keys_kernel<RR, QQ>, grid, dim3(kNT), 0, st, t_start, t_stop, 0, qq, lk, \
+                          pk, sel, pbuf, pstat, H_q, H_kv, G, ctx_cap, ctx, n_sel, n_splits, rope_base);  \
+  else                                                                                               \
+    shared_keys_kernel<RR, QQ><<<grid, kNT, 0, st>>>(qq, lk, pk, sel, pbuf, pstat, H_q, H_kv, G,       \
+                                                     ctx_cap, ctx, n_sel, n_splits, rope_base)
+#define SALS_SK_R(RR) \
+  if (nqh <= 1) {     \
+    SALS_SK(RR, 1);   \
+  } else {            \
+    SALS_SK(RR, 4);   \
+  }
   switch (r) {
     case 128: SALS_SK_R(128) break;
     case 256: SALS_SK_R(256) break;

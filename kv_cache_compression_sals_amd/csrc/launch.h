@@ -3,6 +3,7 @@
 // Shapes were validated by the C ABI layer before any of these is called.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -45,7 +46,8 @@ hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const 
                                 const void* Pk, const void* Pv, const int32_t* sel, float* out,
                                 float* part, float* pbuf, float* pstat, int B, int H_q, int H_kv,
                                 int d, int r, int G, int ctx_cap, int ctx, int n_sel,
-                                int split_len, int n_splits, float rope_base, hipStream_t st);
+                                int split_len, int n_splits, float rope_base, hipStream_t st,
+                                hipEvent_t t_start = nullptr, hipEvent_t t_stop = nullptr);
 
 // Key side when one selection serves several KV heads (bf16, d = 128, an even number of KV heads
 // per group, at most 4 query heads per KV head, r in {128, 256, 384, 512}): the K rebuild of two
@@ -57,7 +59,7 @@ int shared_keys_split();
 hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, const int32_t* sel,
                               float* pbuf, float* pstat, int B, int H_q, int H_kv, int G, int r,
                               int ctx_cap, int ctx, int n_sel, int n_splits, float rope_base,
-                              hipStream_t st);
+                              hipStream_t st, hipEvent_t t_start = nullptr, hipEvent_t t_stop = nullptr);
 
 // Full reconstruction of cache rows [t0, t0 + T) into a post-RoPE KV cache [B, H_kv,
 // stride_tokens, d] (bf16, d = 128, an even H_kv, r in {128, 256, 384, 512}); V (and Lv, Pv)

@@ -231,15 +231,16 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   if (e == hipSuccess)
     e = sals::launch_topk_window(S, p.ldS, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel,
                                  (int32_t*)(w + p.off_cand), hs);
-  mark(3);
+  // the attention kernel's own start and end (recorded by the runtime around the kernel) bound
+  // its stage, so that the traced time of the dominant kernel excludes the launch gap
+  hipEvent_t k0 = events ? (hipEvent_t)events[3] : nullptr, k1 = events ? (hipEvent_t)events[4] : nullptr;
   if (e == hipSuccess && p.skeys)
     e = sals::launch_shared_keys(q, Lk, Pk, selb, pbuf, pstat, s->B, s->H_q, s->H_kv, G, s->r,
-                                 ctx_cap, ctx, p.n_sel, p.n_splits, rope_base, hs);
+                                 ctx_cap, ctx, p.n_sel, p.n_splits, rope_base, hs, k0, k1);
   else if (e == hipSuccess)
     e = sals::launch_select_attend(s->dtype, q, Lk, Lv, Pk, Pv, selb, out, part, pbuf, pstat,
                                    s->B, s->H_q, s->H_kv, s->d, s->r, G, ctx_cap, ctx, p.n_sel,
-                                   p.split_len, p.n_splits, rope_base, hs);
-  mark(4);
+                                   p.split_len, p.n_splits, rope_base, hs, k0, k1);
   if (p.shared) {
     if (e == hipSuccess)
       e = sals::launch_value_sum(s->dtype, p.vp, pbuf, pstat, selb, Lv, zpart, s->B, s->H_q, G,

@@ -163,3 +163,29 @@ def test_graph_capture_replays_match_eager():
         # eager work between replays
         sals.sals_decode_step(q, Lk, Lv, Pk, Pv, **kw)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,cfg,ov,B,ctx", [
+    ("shared_keys", C2, dict(calib_tokens=1024), 2, 1200),
+    ("select_attend", C3, dict(calib_tokens=512), 2, 3001),
+], ids=["shared_keys", "select_attend"])
+def test_traced_step_matches_and_times(name, cfg, ov, B, ctx):
+    """The traced entry point gives the same bytes as the plain one, and its six events are
+    ordered with a positive duration for the attention kernel (timed by its own start and end)."""
+    case = decode_case(cfg.with_(**ov), B=B, ctx=ctx, ctx_cap=ctx)
+    print(f"traced {name} B={B} ctx={ctx}", flush=True)
+    dt = case["dtype"]
+    q, Lk, Lv, Pk, Pv = (to_device(case[n], dt) for n in ("q", "Lk", "Lv", "Pk", "Pv"))
+    kw = dict(ctx=ctx, k=case["k"], w=case["w"], G=case["G"], rope_base=case["base"], want_sel=True)
+    out0, sel0 = sals.sals_decode_step(q, Lk, Lv, Pk, Pv, **kw)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    out1, sel1 = sals.sals_decode_step_traced(q, Lk, Lv, Pk, Pv, evs, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(sel0, sel1)
+    t = [evs[0].elapsed_time(e) for e in evs]
+    print("   event times (ms):", [round(x, 4) for x in t], flush=True)
+    assert all(t[i] <= t[i + 1] for i in range(5))
+    assert evs[3].elapsed_time(evs[4]) > 0
