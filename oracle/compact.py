@@ -80,6 +80,23 @@ def kv_compact(K, V, Qobs, *, ctx: int, k_keep: int, H_kv: int, dtype: str = "bf
     return dict(importance=I, kept=kept, Kc=Kc, Vc=Vc)
 
 
+def compact_from_importance(K, V, importance, *, k_keep: int, pairs=None) -> Dict[str, object]:
+    """Selection and gather from a given importance (the PureKV abstract: importance measured on a
+    lower layer ranks the cache tokens of higher layers). importance[B, H_kv, >= T] (float), K, V
+    stored [B, H_kv, ctx_cap, d]; the first T = importance.shape[2] positions are ranked.
+    Returns ``kept[B, H_kv, k_keep]`` (ascending int64) and ``Kc, Vc`` (stored rows)."""
+    B, H_kv, T = importance.shape
+    d = K.shape[3]
+    kept = np.full((B, H_kv, k_keep), -1, dtype=np.int64)
+    Kc = np.zeros((B, H_kv, k_keep, d), dtype=K.dtype)
+    Vc = np.zeros_like(Kc)
+    todo = [(b, g) for b in range(B) for g in range(H_kv)] if pairs is None else pairs
+    for b, g in todo:
+        kept[b, g] = topk_lowest_index(np.asarray(importance[b, g], dtype=np.float64), k_keep)
+        Kc[b, g], Vc[b, g] = K[b, g, kept[b, g]], V[b, g, kept[b, g]]
+    return dict(kept=kept, Kc=Kc, Vc=Vc)
+
+
 def dense_decode(q, K, V, *, n: int, H_kv: int, dtype: str = "bf16", pairs=None) -> np.ndarray:
     """o[b, h] = softmax(q[b, h] . K[b, kv(h), :n]^T / sqrt(d)) . V[b, kv(h), :n].
 

@@ -333,6 +333,27 @@ def pin_dense_baseline_identity_and_full_selection():
         assert np.allclose(base_out, sals_out, atol=TOL, rtol=0), (H_q, H_kv, G, d)
 
 
+def pin_compact_from_importance():
+    """Against Python's sorted() on (-I, t) keys with ties and signed zeros; with the importance
+    kv_compact computed for the same cache it keeps the same rows."""
+    rs = np.random.default_rng(41)
+    B, H, T, d, k = 2, 3, 40, 4, 11
+    I = np.round(rs.standard_normal((B, H, T)), 1)  # many ties
+    I[0, 0, :5] = [0.0, -0.0, 0.0, -0.0, 0.0]
+    K = rs.standard_normal((B, H, T + 3, d))
+    V = rs.standard_normal((B, H, T + 3, d))
+    res = OC.compact_from_importance(K, V, I, k_keep=k)
+    for b in range(B):
+        for g in range(H):
+            ref = sorted(sorted(range(T), key=lambda t: (-float(I[b, g, t]) + 0.0, t))[:k])
+            assert list(res["kept"][b, g]) == ref, (b, g)
+            assert np.array_equal(res["Kc"][b, g], K[b, g, ref]) and np.array_equal(res["Vc"][b, g], V[b, g, ref])
+    Q = rs.standard_normal((B, 2 * H, 5, d))
+    full = OC.kv_compact(K, V, Q, ctx=T, k_keep=k, H_kv=H, dtype="f64")
+    again = OC.compact_from_importance(K, V, full["importance"], k_keep=k)
+    assert np.array_equal(full["kept"], again["kept"]) and np.array_equal(full["Kc"], again["Kc"])
+
+
 PINS = [
     pin_rope_d2_closed_form,
     pin_rope_complex_form,
@@ -349,4 +370,5 @@ PINS = [
     pin_compact_identity_and_masked,
     pin_reconstruct_cache_identity,
     pin_dense_baseline_identity_and_full_selection,
+    pin_compact_from_importance,
 ]

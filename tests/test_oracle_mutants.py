@@ -53,6 +53,11 @@ MUTANTS = [
     ("sals.py", "qh = rope(qf[b, h][None, :], ctx - 1, base)[0]", "qh = qf[b, h]", "baseline query not rotated"),
     ("sals.py", "V = reconstruct_cache(stored_to_f64(Lv[b, :ctx], dtype), Pvf, 0, ctx, H_kv, None)",
      "V = reconstruct_cache(stored_to_f64(Lv[b, :ctx], dtype), Pkf, 0, ctx, H_kv, None)", "baseline values from P_k"),
+    ("compact.py", "topk_lowest_index(np.asarray(importance[b, g], dtype=np.float64), k_keep)",
+     "topk_lowest_index(-np.asarray(importance[b, g], dtype=np.float64), k_keep)",
+     "given importance ranked upside down"),
+    ("compact.py", "Kc[b, g], Vc[b, g] = K[b, g, kept[b, g]], V[b, g, kept[b, g]]",
+     "Kc[b, g], Vc[b, g] = K[b, g, kept[b, g]], K[b, g, kept[b, g]]", "given-importance values gathered from K"),
     ("compact.py", "a = _softmax(K[: p + 1] @ Qobs[i] / np.sqrt(d))\n        I[: p + 1] += a",
      "a = _softmax(K[:T] @ Qobs[i] / np.sqrt(d))\n        I[:T] += a", "causal mask dropped"),
     ("compact.py", "p = T - w + i", "p = T - w + i + 1 if i < w - 1 else T - 1", "observation positions shifted"),
