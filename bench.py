@@ -281,8 +281,9 @@ def run_comparators(cfg, base, ctx, steps, warmup):
 
 
 def run_compact_workload(cfg, steps, warmup, label):
-    """kv_compact on the full compaction workload, then sals_dense_decode over the compact cache;
-    each timed as `steps` back-to-back calls between two HIP events."""
+    """kv_compact on the full compaction workload, then sals_dense_decode over the compact cache,
+    and kv_compact_from_importance (selection and gather from a given importance, as a higher
+    layer reusing this layer's); each timed as `steps` back-to-back calls between two HIP events."""
     import numpy as np
     import torch
 
@@ -302,8 +303,12 @@ def run_compact_workload(cfg, steps, warmup, label):
     out = torch.empty((B, Qobs.shape[1], d), dtype=torch.float32, device="cuda")
     ws_c = torch.empty(sals.kv_compact_workspace_bytes(K, Qobs, ctx=ctx, k_keep=kk), dtype=torch.uint8, device="cuda")
     ws_d = torch.empty(sals.sals_dense_decode_workspace_bytes(q, Kc, n=kk), dtype=torch.uint8, device="cuda")
-    compact = lambda: sals.kv_compact(K, V, Qobs, ctx=ctx, k_keep=kk, Kc=Kc, Vc=Vc, kept=kept, workspace=ws_c)
+    imp = torch.empty((B, H_kv, ctx), dtype=torch.float32, device="cuda")
+    compact = lambda: sals.kv_compact(K, V, Qobs, ctx=ctx, k_keep=kk, Kc=Kc, Vc=Vc, kept=kept, importance=imp,
+                                      workspace=ws_c)
     decode = lambda: sals.sals_dense_decode(q, Kc, Vc, n=kk, out=out, workspace=ws_d)
+    # a higher layer compacted by this layer's importance (the same cache stands in for it)
+    reuse = lambda: sals.kv_compact_from_importance(K, V, imp, k_keep=kk, Kc=Kc, Vc=Vc, kept=kept)
 
     def timed(fn):
         for _ in range(warmup):
@@ -317,20 +322,22 @@ def run_compact_workload(cfg, steps, warmup, label):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps * 1e3
 
-    c_us, d_us = timed(compact), timed(decode)
+    c_us, d_us, r_us = timed(compact), timed(decode), timed(reuse)
     s = 2
     # compaction: K once for the importance (its second pass is recomputation), the kept K and V
     # rows read and written once, the observation queries; decode: the compact cache once
     c_bytes = B * H_kv * ctx * d * s + 4 * B * H_kv * kk * d * s + Qobs.numel() * s
     d_bytes = 2 * B * H_kv * kk * d * s
+    r_bytes = B * H_kv * ctx * 4 + 4 * B * H_kv * kk * d * s
     H_q = Qobs.shape[1]
-    del K, V, Qobs, Kc, Vc, ws_c, ws_d
+    del K, V, Qobs, Kc, Vc, ws_c, ws_d, imp
     torch.cuda.empty_cache()
     return dict(workload=f"{label}: B={B} H_q={H_q} H_kv={H_kv} d={d} ctx={ctx} w={cfg.w} "
                          f"k_keep={kk}, bf16",
                 compact_us=round(c_us, 1), compact_gbps=round(c_bytes / (c_us * 1e-6) / 1e9, 1),
                 decode_us=round(d_us, 2), decode_gbps=round(d_bytes / (d_us * 1e-6) / 1e9, 1),
-                compact_bytes=c_bytes, decode_bytes=d_bytes)
+                from_importance_us=round(r_us, 2), from_importance_gbps=round(r_bytes / (r_us * 1e-6) / 1e9, 1),
+                compact_bytes=c_bytes, decode_bytes=d_bytes, from_importance_bytes=r_bytes)
 
 
 def _layer_inputs(layer):

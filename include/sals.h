@@ -195,6 +195,26 @@ sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const v
                        sals_stream_t stream);
 
 /*
+ * kv_compact_from_importance - the selection and gather of kv_compact from an importance the
+ * caller supplies (PureKV abstract: attention measured on a lower layer estimates the importance
+ * of the tokens of higher layers, so those layers need no attention scores of their own).
+ *   kept   = the k_keep largest importance[b, g, :ctx] (ties to the lowest index), ascending
+ *   Kc, Vc = K[b, g, kept], V[b, g, kept]   (bit-exact copies)
+ * Args
+ *   c             shape (H_q unused); K and V use c->dtype.
+ *   K, V          [B, H_kv, ctx_cap, d], rows [0, ctx) read.
+ *   importance    [B, H_kv, ctx] fp32 (e.g. the importance output of kv_compact on another
+ *                 layer), finite values; read.
+ *   ctx_cap, ctx  1 <= ctx <= ctx_cap; 1 <= k_keep <= ctx.
+ *   Kc, Vc        [B, H_kv, k_keep, d] written.   kept [B, H_kv, k_keep] int32 written.
+ * No workspace. Errors: NULL/ALIGN/SHAPE/DTYPE/RANGE as for kv_compact, HIP on launch failure.
+ */
+sals_status kv_compact_from_importance(const kvc_shape* c, const void* K, const void* V,
+                                      const float* importance, int32_t ctx_cap, int32_t ctx,
+                                      int32_t k_keep, void* Kc, void* Vc, int32_t* kept,
+                                      sals_stream_t stream);
+
+/*
  * sals_dense_decode_workspace_bytes - exact workspace size of sals_dense_decode for (c, n).
  */
 sals_status sals_dense_decode_workspace_bytes(const kvc_shape* c, int32_t n, size_t* bytes);

@@ -8,6 +8,7 @@ loading the library happens on first use and fails loudly if it has not been bui
 from .binding import (  # noqa: F401
     SalsError,
     kv_compact,
+    kv_compact_from_importance,
     kv_compact_workspace_bytes,
     n_selected,
     sals_decode_step,

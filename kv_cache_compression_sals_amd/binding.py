@@ -234,3 +234,27 @@ def sals_reconstruct_kv(Lk: torch.Tensor, Pk: torch.Tensor, K: torch.Tensor, *, 
     _check("sals_reconstruct_kv", lib().sals_reconstruct_kv(
         ctypes.byref(s), ctypes.c_float(rope_base), _ptr(Lk), _ptr(Lv), _ptr(Pk), _ptr(Pv), Lk.shape[1],
         t0, T, _ptr(K), _ptr(V), stride, _ptr(q), _ptr(q_rot), q_pos, _stream(stream)))
+
+
+def kv_compact_from_importance(K: torch.Tensor, V: torch.Tensor, importance: torch.Tensor, *, k_keep: int,
+                               ctx: Optional[int] = None, Kc: Optional[torch.Tensor] = None,
+                               Vc: Optional[torch.Tensor] = None, kept: Optional[torch.Tensor] = None,
+                               stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Keep the k_keep most important rows per (sequence, KV head) by a given importance
+    [B, H_kv, ctx] fp32 (e.g. another layer's kv_compact importance). K, V [B, H_kv, ctx_cap, d].
+    Returns (Kc, Vc [B, H_kv, k_keep, d], kept [B, H_kv, k_keep] int32)."""
+    B, H_kv, cap, d = K.shape
+    ctx = importance.shape[2] if ctx is None else ctx
+    if importance.dtype != torch.float32:
+        raise ValueError("importance must be float32")
+    c = KvcShape(B, H_kv, H_kv, d, _dtype(K, V))
+    if Kc is None:
+        Kc = torch.empty((B, H_kv, k_keep, d), dtype=K.dtype, device=K.device)
+    if Vc is None:
+        Vc = torch.empty_like(Kc)
+    if kept is None:
+        kept = torch.empty((B, H_kv, k_keep), dtype=torch.int32, device=K.device)
+    _check("kv_compact_from_importance", lib().kv_compact_from_importance(
+        ctypes.byref(c), _ptr(K), _ptr(V), _ptr(importance), cap, ctx, k_keep, _ptr(Kc), _ptr(Vc),
+        _ptr(kept), _stream(stream)))
+    return Kc, Vc, kept

@@ -398,6 +398,27 @@ sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const v
   return e == hipSuccess ? SALS_OK : hip_fail(e);
 }
 
+sals_status kv_compact_from_importance(const kvc_shape* c, const void* K, const void* V,
+                                      const float* importance, int32_t ctx_cap, int32_t ctx,
+                                      int32_t k_keep, void* Kc, void* Vc, int32_t* kept,
+                                      sals_stream_t stream) {
+  if (!c || !K || !V || !importance || !Kc || !Vc || !kept) return SALS_ERR_NULL;
+  sals_status st = check_kvc_shape(c);
+  if (st != SALS_OK) return st;
+  if (ctx < 1 || ctx > (1 << 26) || ctx > ctx_cap || k_keep < 1 || k_keep > ctx) return SALS_ERR_RANGE;
+  if (misaligned(K) || misaligned(V) || misaligned(importance) || misaligned(Kc) || misaligned(Vc) ||
+      misaligned(kept))
+    return SALS_ERR_ALIGN;
+  if ((st = device_ready()) != SALS_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = sals::launch_topk_window(importance, ctx, kept, c->B * c->H_kv, ctx, k_keep, ctx,
+                                          k_keep, nullptr, hs);
+  if (e == hipSuccess)
+    e = sals::launch_gather_rows(c->dtype, K, V, kept, Kc, Vc, c->B * c->H_kv, c->d, ctx_cap,
+                                 k_keep, hs);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
 sals_status sals_dense_decode_workspace_bytes(const kvc_shape* c, int32_t n, size_t* bytes) {
   if (!bytes) return SALS_ERR_NULL;
   DensePlan p;

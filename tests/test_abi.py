@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     L = lib()
     for n in names:
         assert hasattr(L, n), n
@@ -149,6 +149,22 @@ def test_dense_decode_argument_errors():
     assert L.sals_dense_decode(ctypes.byref(c), P, P, None, 10, 10, P, P, 1 << 20, None) == NULL
     assert L.sals_dense_decode(ctypes.byref(c), P, P, P, 11, 10, P, P, 1 << 20, None) == RANGE
     assert L.sals_dense_decode(ctypes.byref(c), P, P, P, 0, 10, P, P, 1 << 20, None) == RANGE
+
+
+def test_compact_from_importance_argument_errors():
+    L = lib()
+
+    def call(c=KvcShape(2, 4, 4, 128, 1), K=P, imp=P, cap=100, ctx=100, k=10):
+        return L.kv_compact_from_importance(ctypes.byref(c), K, P, imp, cap, ctx, k, P, P, P, None)
+
+    assert call(imp=None) == NULL
+    assert call(K=None) == NULL
+    assert call(ctx=101) == RANGE
+    assert call(k=0) == RANGE
+    assert call(k=101) == RANGE
+    assert call(c=KvcShape(2, 4, 4, 96, 1)) == SHAPE
+    assert call(c=KvcShape(2, 4, 4, 128, 7)) == DTYPE
+    assert call(imp=P + 4) == ALIGN
 
 
 def test_reconstruct_argument_errors():

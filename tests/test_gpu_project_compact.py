@@ -186,3 +186,52 @@ def test_dense_decode_grouped_heads(B, H_q, H_kv, d, n, stride, dt):
     err = np.abs(out - ref).max()
     print(f"   max err {err:.2e}", flush=True)
     assert err <= 1e-4
+
+
+# ---- compaction from a given importance -------------------------------------------------------
+
+FROM_IMP = [
+    # B, H_kv, d, ctx, ctx_cap, k_keep, dtype (a row past 32768 positions takes the global path)
+    (2, 4, 128, 3000, 3100, 300, "bf16"),
+    (1, 2, 64, 40000, 40000, 4000, "bf16"),
+    (2, 3, 64, 777, 800, 777, "f32"),
+    (1, 1, 128, 5, 8, 1, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,H_kv,d,ctx,cap,k_keep,dt", FROM_IMP,
+                         ids=[f"ctx{c[3]}_k{c[5]}_{c[6]}" for c in FROM_IMP])
+def test_compact_from_importance_matches_oracle(B, H_kv, d, ctx, cap, k_keep, dt):
+    """Heavily tied importance (multiples of 0.1, signed zeros): kept sets exact, rows bit-exact."""
+    print(f"from_importance B={B} H_kv={H_kv} d={d} ctx={ctx} k_keep={k_keep} {dt}", flush=True)
+    rs = np.random.default_rng(ctx + k_keep)
+    imp = (np.round(rs.standard_normal((B, H_kv, ctx)) * 10) / 10).astype(np.float32)
+    imp[0, 0, : min(4, ctx)] = np.array([0.0, -0.0, 0.0, -0.0], dtype=np.float32)[: min(4, ctx)]
+    K = rs.standard_normal((B, H_kv, cap, d)).astype(np.float32)
+    V = rs.standard_normal((B, H_kv, cap, d)).astype(np.float32)
+    if dt == "bf16":
+        K, V = _bf16_bits(K), _bf16_bits(V)
+    Kc, Vc, kept = sals.kv_compact_from_importance(to_device(K, dt), to_device(V, dt),
+                                                   torch.from_numpy(imp).cuda(), k_keep=k_keep)
+    torch.cuda.synchronize()
+    ref = oracle.compact_from_importance(K, V, imp, k_keep=k_keep)
+    assert np.array_equal(kept.cpu().numpy(), ref["kept"])
+    raw = (lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)) if dt == "bf16" else (lambda t: t.cpu().numpy())
+    assert np.array_equal(raw(Kc), ref["Kc"]) and np.array_equal(raw(Vc), ref["Vc"])
+
+
+def test_compact_higher_layer_from_lower_layer_importance():
+    """The lower layer's kv_compact importance ranks a higher layer's cache (same selection rule)."""
+    cfg = C4.with_(B=2, H_q=8, H_kv=4, ctx=3000, w=32, n_visual=2000, grid_h=40, grid_w=50, clusters_h=4,
+                   clusters_w=5)
+    low = compact_case(cfg, ctx=3000)
+    high = compact_case(cfg.with_(cfg_id=cfg.cfg_id + 1000), ctx=3000)  # another layer's draw
+    dt = low["dtype"]
+    _, _, _, imp = sals.kv_compact(to_device(low["K"], dt), to_device(low["V"], dt), to_device(low["Qobs"], dt),
+                                   ctx=3000, k_keep=300, want_importance=True)
+    Kc, Vc, kept = sals.kv_compact_from_importance(to_device(high["K"], dt), to_device(high["V"], dt), imp,
+                                                   k_keep=300)
+    torch.cuda.synchronize()
+    ref = oracle.compact_from_importance(high["K"], high["V"], imp.cpu().numpy(), k_keep=300)
+    assert np.array_equal(kept.cpu().numpy(), ref["kept"])
+    assert np.array_equal(Kc.view(torch.int16).cpu().numpy().view(np.uint16), ref["Kc"])
