@@ -49,17 +49,24 @@ __device__ __forceinline__ void load_q_frags(const typename T::elem* __restrict_
   }
 }
 
-// logits[nb][i] = K[t0 + q4*4 + i] . Qobs[qg*64 + nb*16 + n16]   (unscaled)
+// K rows of one 16-token tile in the MFMA operand layout: lane (n16, q4) holds row t0 + n16
+// (clamped to the last valid row), head-dimension segment q4.
 template <class T, int DH>
-__device__ __forceinline__ void logit_tile(const typename T::elem* __restrict__ Kh, int t0, int ctx,
-                                           int lane, const Frags<T, DH>& f, f32x4* acc) {
+__device__ __forceinline__ void load_k_tile(const typename T::elem* __restrict__ Kh, int t0, int ctx,
+                                            int lane, u32x4 (&ch)[Seg<T, DH>::NCH]) {
   using SG = Seg<T, DH>;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int t = min(t0 + n16, ctx - 1);
-  u32x4 ch[SG::NCH];
   const u32x4* p = (const u32x4*)(Kh + (size_t)t * DH + q4 * SG::SEG);
 #pragma unroll
   for (int c = 0; c < SG::NCH; ++c) ch[c] = p[c];
+}
+
+// logits[nb][i] = K[t0 + q4*4 + i] . Qobs[qg*64 + nb*16 + n16]   (unscaled)
+template <class T, int DH>
+__device__ __forceinline__ void logit_tile(const u32x4 (&ch)[Seg<T, DH>::NCH], const Frags<T, DH>& f,
+                                           f32x4* acc) {
+  using SG = Seg<T, DH>;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -67,6 +74,31 @@ __device__ __forceinline__ void logit_tile(const typename T::elem* __restrict__ 
     const typename T::frag a = frag_at<T>(ch, kb);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] = T::mma(a, f.q[nb][kb], acc[nb]);
+  }
+}
+
+// A wave's tiles t = t_begin, t_begin + stride, ... < t_end with the K rows of the next D - 1
+// tiles in flight while one is computed (D buffers, indexed by compile-time constants).
+template <class T, int DH>
+constexpr int kKDepth = sizeof(typename T::elem) == 2 ? 4 : 2;
+
+template <class T, int DH, class StepF>
+__device__ __forceinline__ void for_k_tiles(const typename T::elem* __restrict__ Kh, int ctx, int lane,
+                                            int t_begin, int t_end, int stride, StepF step) {
+  constexpr int D = kKDepth<T, DH>;
+  u32x4 buf[D][Seg<T, DH>::NCH];
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (t_begin + j * stride < t_end) load_k_tile<T, DH>(Kh, t_begin + j * stride, ctx, lane, buf[j]);
+  for (int t0 = t_begin; t0 < t_end; t0 += D * stride) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int t = t0 + j * stride;
+      if (t < t_end) {
+        step(t, buf[j]);
+        if (t + D * stride < t_end) load_k_tile<T, DH>(Kh, t + D * stride, ctx, lane, buf[j]);
+      }
+    }
   }
 }
 
@@ -93,28 +125,33 @@ __global__ __launch_bounds__(kThreads) void imp_stats_kernel(const typename T::e
     s[nb] = 0.f;
   }
   const int cbeg = c * kChunk, cend = min(ctx, cbeg + kChunk);
-  for (int t0 = cbeg + wave * 16; t0 < cend; t0 += 64) {
+  // online (max, sum) per lane over its 4 tokens of each tile: the tile's own maximum first, then
+  // one rescale, so that every lane takes the same path
+  for_k_tiles<T, DH>(Kh, ctx, lane, cbeg + wave * 16, cend, 64, [&](int t0, const u32x4 (&ch)[Seg<T, DH>::NCH]) {
     f32x4 acc[4];
-    logit_tile<T, DH>(Kh, t0, ctx, lane, f, acc);
+    logit_tile<T, DH>(ch, f, acc);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int qi = qg * kQG + nb * 16 + n16;
       const int lim = ctx - w + qi;  // last visible position of query qi
+      float x[4];
+      float tm = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + q4 * 4 + i;
-        if (t < cend && t <= lim && qi < w) {
-          const float x = acc[nb][i] * scale;
-          if (x > m[nb]) {
-            s[nb] = s[nb] * expf(m[nb] - x) + 1.0f;
-            m[nb] = x;
-          } else {
-            s[nb] += expf(x - m[nb]);
-          }
-        }
+        x[i] = (t < cend && t <= lim && qi < w) ? acc[nb][i] * scale : -INFINITY;
+        tm = fmaxf(tm, x[i]);
+      }
+      const float mn = fmaxf(m[nb], tm);
+      if (mn != -INFINITY) {
+        float add = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) add += expf(x[i] - mn);
+        s[nb] = s[nb] * expf(m[nb] - mn) + add;
+        m[nb] = mn;
       }
     }
-  }
+  });
   // merge the 4 lane groups (same query), then the 4 waves
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
@@ -197,9 +234,9 @@ __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::e
           invS[nb] = 0.f;
         }
       }
-      for (int t0 = cbeg + wave * 16; t0 < cend; t0 += 64) {
+      for_k_tiles<T, DH>(Kh, ctx, lane, cbeg + wave * 16, cend, 64, [&](int t0, const u32x4 (&ch)[Seg<T, DH>::NCH]) {
         f32x4 acc[4];
-        logit_tile<T, DH>(Kh, t0, ctx, lane, f, acc);
+        logit_tile<T, DH>(ch, f, acc);
         float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
@@ -227,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::e
             if (t < cend) acc_lds[t - cbeg] += part[i];
           }
         }
-      }
+      });
     }
   }
   __syncthreads();
