@@ -7,7 +7,10 @@
 //   I[t] = sum_{h of g} sum_{i < w} exp(l_{h,i,t} - m_{h,i}) / s_{h,i},   t <= p_i = ctx - w + i
 // with l = Qobs . K / sqrt(d) and (m, s) the row max and softmax denominator of query (h, i).
 // Pass 1 computes (m, s) per token chunk with an online update and merges the chunks; pass 2
-// recomputes the logits and accumulates I. Both passes are MFMA tiles of 16 tokens (A operand,
+// recomputes the logits and accumulates I. Logits are kept in base-2 units (scaled by
+// log2(e) / sqrt(d)) so that every exponential is one hardware exp2; m and the merged maxima are
+// in the same units. Tiles that lie wholly inside every query's causal window (all but the last
+// w tokens) skip the per-element masks. Both passes are MFMA tiles of 16 tokens (A operand,
 // streamed from HBM) x 16 queries (B operand, in registers), so only the last w query rows are
 // ever formed, never the n x n attention matrix.
 #include "../common.h"
@@ -19,6 +22,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 1024;  // tokens per workgroup
 constexpr int kQG = 64;       // observation queries per workgroup (4 MFMA column blocks)
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <class T, int DH>
 struct Frags {
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void imp_stats_kernel(const typename T::e
   const int n16 = lane & 15, q4 = lane >> 4;
   const int c = blockIdx.x, h = blockIdx.y / n_qg, qg = blockIdx.y % n_qg, b = blockIdx.z;
   const int g = h / (H_q / H_kv);
-  const float scale = 1.0f / sqrtf((float)DH);
+  const float scale = kLog2e / sqrtf((float)DH);
   const typename T::elem* Kh = K + ((size_t)b * H_kv + g) * ctx_cap * DH;
   Frags<T, DH> f;
   load_q_frags<T, DH>(Q + ((size_t)b * H_q + h) * w * DH, w, qg, lane, f);
@@ -130,6 +134,8 @@ __global__ __launch_bounds__(kThreads) void imp_stats_kernel(const typename T::e
   for_k_tiles<T, DH>(Kh, ctx, lane, cbeg + wave * 16, cend, 64, [&](int t0, const u32x4 (&ch)[Seg<T, DH>::NCH]) {
     f32x4 acc[4];
     logit_tile<T, DH>(ch, f, acc);
+    // the whole tile is visible to every query of the group (and they all exist)
+    const bool full = t0 + 16 <= cend && t0 + 15 <= ctx - w + qg * kQG && (qg + 1) * kQG <= w;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int qi = qg * kQG + nb * 16 + n16;
@@ -139,15 +145,15 @@ __global__ __launch_bounds__(kThreads) void imp_stats_kernel(const typename T::e
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + q4 * 4 + i;
-        x[i] = (t < cend && t <= lim && qi < w) ? acc[nb][i] * scale : -INFINITY;
+        x[i] = (full || (t < cend && t <= lim && qi < w)) ? acc[nb][i] * scale : -INFINITY;
         tm = fmaxf(tm, x[i]);
       }
       const float mn = fmaxf(m[nb], tm);
       if (mn != -INFINITY) {
         float add = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) add += expf(x[i] - mn);
-        s[nb] = s[nb] * expf(m[nb] - mn) + add;
+        for (int i = 0; i < 4; ++i) add += __builtin_amdgcn_exp2f(x[i] - mn);
+        s[nb] = s[nb] * __builtin_amdgcn_exp2f(m[nb] - mn) + add;
         m[nb] = mn;
       }
     }
@@ -159,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void imp_stats_kernel(const typename T::e
     for (int msk = 16; msk <= 32; msk <<= 1) {
       const float mo = __shfl_xor(m[nb], msk), so = __shfl_xor(s[nb], msk);
       const float mn = fmaxf(m[nb], mo);
-      s[nb] = (mn == -INFINITY) ? 0.f : s[nb] * expf(m[nb] - mn) + so * expf(mo - mn);
+      s[nb] = (mn == -INFINITY) ? 0.f : s[nb] * __builtin_amdgcn_exp2f(m[nb] - mn) + so * __builtin_amdgcn_exp2f(mo - mn);
       m[nb] = mn;
     }
     if (lane < 16) {
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void imp_stats_kernel(const typename T::e
     for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, red[wv][tid][0]);
     float S = 0.f;
     if (M != -INFINITY)
-      for (int wv = 0; wv < 4; ++wv) S += red[wv][tid][1] * expf(red[wv][tid][0] - M);
+      for (int wv = 0; wv < 4; ++wv) S += red[wv][tid][1] * __builtin_amdgcn_exp2f(red[wv][tid][0] - M);
     if (qi < w) {
       float* p = part + ((((size_t)b * H_q + h) * w + qi) * n_chunks + c) * 2;
       p[0] = M;
@@ -193,7 +199,7 @@ __global__ void imp_merge_kernel(const float* __restrict__ part, float* __restri
   for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, p[2 * c]);
   float S = 0.f;
   for (int c = 0; c < n_chunks; ++c)
-    if (p[2 * c] != -INFINITY) S += p[2 * c + 1] * expf(p[2 * c] - M);
+    if (p[2 * c] != -INFINITY) S += p[2 * c + 1] * __builtin_amdgcn_exp2f(p[2 * c] - M);
   stats[2 * (size_t)e] = M;
   stats[2 * (size_t)e + 1] = S;
 }
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::e
   const int n16 = lane & 15, q4 = lane >> 4;
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int nqh = H_q / H_kv;
-  const float scale = 1.0f / sqrtf((float)DH);
+  const float scale = kLog2e / sqrtf((float)DH);
   const typename T::elem* Kh = K + ((size_t)b * H_kv + g) * ctx_cap * DH;
   const int cbeg = c * kChunk, cend = min(ctx, cbeg + kChunk);
   for (int j = tid; j < kChunk; j += kThreads) acc_lds[j] = 0.f;
@@ -238,6 +244,7 @@ __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::e
         f32x4 acc[4];
         logit_tile<T, DH>(ch, f, acc);
         float part[4] = {0.f, 0.f, 0.f, 0.f};
+        const bool full = t0 + 15 <= ctx - w + qg * kQG && (qg + 1) * kQG <= w;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const int qi = qg * kQG + nb * 16 + n16;
@@ -245,7 +252,8 @@ __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::e
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = t0 + q4 * 4 + i;
-            if (qi < w && t <= lim) part[i] += expf(acc[nb][i] * scale - M[nb]) * invS[nb];
+            const float e = __builtin_amdgcn_exp2f(acc[nb][i] * scale - M[nb]) * invS[nb];
+            part[i] += (full || (qi < w && t <= lim)) ? e : 0.f;
           }
         }
 #pragma unroll
