@@ -365,8 +365,9 @@ def run_layers_workload(cfg, steps, warmup, label, n_layers=32):
     t0 = time.time()
     layers = [None] * n_layers
     with mp.get_context("spawn").Pool(min(16, os.cpu_count() or 1)) as pool:
-        for l, arrs in pool.imap_unordered(_layer_inputs, range(n_layers)):
+        for i, (l, arrs) in enumerate(pool.imap_unordered(_layer_inputs, range(n_layers))):
             layers[l] = {n: dev(a) for n, a in arrs.items()}
+            log(f"[{label}] layer {l} resident ({i + 1}/{n_layers}, {time.time() - t0:.0f}s)")
     log(f"[{label}] generated and uploaded {n_layers} layers in {time.time() - t0:.1f}s")
     ctx = cfg.ctx
     kw = dict(ctx=ctx, k=cfg.k, w=cfg.w, G=cfg.G, rope_base=cfg.base)
