@@ -256,15 +256,9 @@ __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::e
             part[i] += (full || (qi < w && t <= lim)) ? e : 0.f;
           }
         }
+        // sum over the 16 queries of the row (DPP, no LDS crossbar)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = part[i];
-          v += __shfl_xor(v, 1);
-          v += __shfl_xor(v, 2);
-          v += __shfl_xor(v, 4);
-          v += __shfl_xor(v, 8);
-          part[i] = v;
-        }
+        for (int i = 0; i < 4; ++i) part[i] = row16_sum(part[i]);
         if (n16 == 0) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
