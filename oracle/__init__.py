@@ -33,4 +33,4 @@ from .sals import (  # noqa: F401
     stored_to_f64,
     topk_lowest_index,
 )
-from .compact import compact_from_importance, dense_decode, importance, kv_compact  # noqa: F401
+from .compact import compact_from_importance, dense_decode, importance, kv_compact, layer_budgets, sparsity  # noqa: F401

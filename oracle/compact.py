@@ -80,6 +80,42 @@ def kv_compact(K, V, Qobs, *, ctx: int, k_keep: int, H_kv: int, dtype: str = "bf
     return dict(importance=I, kept=kept, Kc=Kc, Vc=Vc)
 
 
+def sparsity(Qobs: np.ndarray, K: np.ndarray, T: int, p: float):
+    """Sparsity of one query head's post-vision attention (VL-Cache responses: reviewer X8F2
+    question 1 - Gamma holds a sparsity per head and layer; reviewer KiPr weakness 5 - it is
+    computed on the post-vision attention rows; KiPr weakness 3 - a threshold p, from 1e-4 to
+    0.1). Reading: the fraction of the causal entries a[i, t] (t <= p_i = T - w + i) of the w
+    observation rows whose probability is below p.
+    Qobs[w, d], K[>=T, d] (fp64). Returns (Gamma, below, total, near), near = entries within
+    a relative 1e-5 of p (their side of the threshold depends on rounding)."""
+    w, d = Qobs.shape
+    below = near = total = 0
+    for i in range(w):
+        pi = T - w + i
+        a = _softmax(K[: pi + 1] @ Qobs[i] / np.sqrt(d))
+        below += int(np.count_nonzero(a < p))
+        near += int(np.count_nonzero(np.abs(a - p) <= 1e-5 * p))
+        total += pi + 1
+    return below / total, below, total, near
+
+
+def layer_budgets(nonsparse, total: int, ctx: int) -> np.ndarray:
+    """Cache budget per layer from the non-sparse ratios nu_l = 1 - Gamma_l (VL-Cache responses:
+    reviewer X8F2 question 1 - Z is the sum of the non-sparse ratios over the layers, the
+    normaliser of the budget; reviewer XVzL weakness 1 - the budget is layer-wise). Reading:
+    k_l = floor(total * nu_l / Z), clamped to [1, ctx]; every layer gets floor(total / L) when
+    Z = 0. (The pages name the allocation "skewed" without its formula; this is the plain
+    proportional split.)"""
+    nu = np.asarray(nonsparse, dtype=np.float64)
+    L = len(nu)
+    Z = float(nu.sum())
+    k = np.empty(L, dtype=np.int64)
+    for l in range(L):
+        share = total * nu[l] / Z if Z > 0 else total / L
+        k[l] = min(max(int(np.floor(share)), 1), ctx)
+    return k
+
+
 def compact_from_importance(K, V, importance, *, k_keep: int, pairs=None) -> Dict[str, object]:
     """Selection and gather from a given importance (the PureKV abstract: importance measured on a
     lower layer ranks the cache tokens of higher layers). importance[B, H_kv, >= T] (float), K, V

@@ -354,6 +354,48 @@ def pin_compact_from_importance():
     assert np.array_equal(full["kept"], again["kept"]) and np.array_equal(full["Kc"], again["Kc"])
 
 
+def pin_sparsity_bruteforce_and_closed_form():
+    """Below-threshold counts against explicit loops with math.exp; q = 0 gives a[i, t] =
+    1/(p_i + 1), so an entry counts exactly when p_i + 1 > 1/p; p above every probability counts
+    all causal entries and p = 0 none."""
+    rs = np.random.default_rng(53)
+    T, w, d = 19, 6, 4
+    Q = rs.standard_normal((w, d)) * 2.0
+    K = rs.standard_normal((T + 2, d))
+    for p in (0.01, 0.05, 0.2):
+        G, below, total, _ = OC.sparsity(Q, K, T, p)
+        cnt = tot = 0
+        for i in range(w):
+            pi = T - w + i
+            logits = [sum(Q[i][c] * K[t][c] for c in range(d)) / math.sqrt(d) for t in range(pi + 1)]
+            m = max(logits)
+            e = [math.exp(v - m) for v in logits]
+            z = sum(e)
+            cnt += sum(1 for v in e if v / z < p)
+            tot += pi + 1
+        assert below == cnt and total == tot and abs(G - cnt / tot) < 1e-15, p
+    G0, below0, total0, _ = OC.sparsity(np.zeros((w, d)), K, T, 0.07)
+    ref = sum(T - w + i + 1 for i in range(w) if T - w + i + 1 > 1 / 0.07)
+    assert below0 == ref and total0 == sum(T - w + i + 1 for i in range(w))
+    assert OC.sparsity(Q, K, T, 1.5)[1] == total0 and OC.sparsity(Q, K, T, 0.0)[1] == 0
+    # a probability exactly at the threshold (1/16 for the row of 16 positions) is not below it
+    ref16 = sum(T - w + i + 1 for i in range(w) if T - w + i + 1 > 16)
+    assert OC.sparsity(np.zeros((w, d)), K, T, 1.0 / 16)[1] == ref16
+
+
+def pin_layer_budgets():
+    """Proportional split: equal ratios give equal shares; shares follow the ratios and never
+    exceed the total; the clamps hold; a zero normaliser splits evenly."""
+    k = OC.layer_budgets([0.5, 0.5, 0.5, 0.5], 400, 1000)
+    assert list(k) == [100, 100, 100, 100]
+    k = OC.layer_budgets([0.1, 0.3, 0.6], 1000, 10_000)
+    assert list(k) == [100, 300, 600]
+    k = OC.layer_budgets([0.2, 0.7, 0.05], 777, 10_000)
+    assert sum(k) <= 777 and list(k) == [int(777 * 0.2 / 0.95), int(777 * 0.7 / 0.95), int(777 * 0.05 / 0.95)]
+    assert list(OC.layer_budgets([0.0, 1.0], 5000, 300)) == [1, 300]
+    assert list(OC.layer_budgets([0.0, 0.0, 0.0], 90, 1000)) == [30, 30, 30]
+
+
 PINS = [
     pin_rope_d2_closed_form,
     pin_rope_complex_form,
@@ -371,4 +413,6 @@ PINS = [
     pin_reconstruct_cache_identity,
     pin_dense_baseline_identity_and_full_selection,
     pin_compact_from_importance,
+    pin_sparsity_bruteforce_and_closed_form,
+    pin_layer_budgets,
 ]

@@ -58,6 +58,13 @@ MUTANTS = [
      "given importance ranked upside down"),
     ("compact.py", "Kc[b, g], Vc[b, g] = K[b, g, kept[b, g]], V[b, g, kept[b, g]]",
      "Kc[b, g], Vc[b, g] = K[b, g, kept[b, g]], K[b, g, kept[b, g]]", "given-importance values gathered from K"),
+    ("compact.py", "below += int(np.count_nonzero(a < p))", "below += int(np.count_nonzero(a <= p))",
+     "sparsity counts entries equal to p"),
+    ("compact.py", "total += pi + 1", "total += pi", "sparsity total misses the diagonal"),
+    ("compact.py", "a = _softmax(K[: pi + 1] @ Qobs[i] / np.sqrt(d))", "a = _softmax(K[:T] @ Qobs[i] / np.sqrt(d))",
+     "sparsity ignores the causal mask"),
+    ("compact.py", "share = total * nu[l] / Z if Z > 0 else total / L", "share = total * nu[l] / L if Z > 0 else total / L",
+     "budgets not normalised by Z"),
     ("compact.py", "a = _softmax(K[: p + 1] @ Qobs[i] / np.sqrt(d))\n        I[: p + 1] += a",
      "a = _softmax(K[:T] @ Qobs[i] / np.sqrt(d))\n        I[:T] += a", "causal mask dropped"),
     ("compact.py", "p = T - w + i", "p = T - w + i + 1 if i < w - 1 else T - 1", "observation positions shifted"),
