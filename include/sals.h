@@ -195,6 +195,44 @@ sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const v
                        sals_stream_t stream);
 
 /*
+ * kv_importance_sparsity_workspace_bytes - workspace size of kv_importance_sparsity.
+ */
+sals_status kv_importance_sparsity_workspace_bytes(const kvc_shape* c, int32_t ctx, int32_t w,
+                                                 size_t* bytes);
+
+/*
+ * kv_importance_sparsity - the importance of kv_compact plus the post-vision sparsity per query
+ * head (VL-Cache responses: reviewer X8F2 question 1 - a sparsity Gamma per head and layer;
+ * KiPr weakness 5 - taken on the post-vision attention rows; KiPr weakness 3 - a threshold p):
+ *   importance[b, g, t] as in kv_compact;
+ *   sparsity[b, h] = #{(i, t): t <= p_i, a_h[i, t] < p_thresh} / #{(i, t): t <= p_i},
+ *   a_h[i, .] = softmax_{t <= p_i}(Qobs[b, h, i] . K[b, g, :] / sqrt(d)), p_i = ctx - w + i.
+ * Args
+ *   c, K, Qobs, w, ctx_cap, ctx   as for kv_compact.
+ *   p_thresh       probability threshold in [0, 1].
+ *   importance     [B, H_kv, ctx] fp32 written.   sparsity [B, H_q] fp32 written.
+ *   ws, ws_bytes   workspace of at least kv_importance_sparsity_workspace_bytes(c, ctx, w).
+ * Errors: NULL/ALIGN/SHAPE/DTYPE/RANGE/WORKSPACE as for kv_compact, RANGE for p_thresh outside
+ * [0, 1], HIP on launch failure.
+ */
+sals_status kv_importance_sparsity(const kvc_shape* c, const void* K, const void* Qobs, int32_t w,
+                                  int32_t ctx_cap, int32_t ctx, float p_thresh, float* importance,
+                                  float* sparsity, void* ws, size_t ws_bytes, sals_stream_t stream);
+
+/*
+ * kv_layer_budgets - cache budgets of L layers from their non-sparse ratios nu_l = 1 - Gamma_l
+ * (VL-Cache responses: reviewer X8F2 question 1 - Z, the sum of the non-sparse ratios over the
+ * layers, normalises the budget; XVzL weakness 1 - the budget is layer-wise):
+ *   budgets[l] = clamp(floor(total * nu_l / Z), 1, ctx),  or floor(total / L) for every layer
+ *   when Z = 0. Host arithmetic in double; no GPU call.
+ * Args: nonsparse [L] host floats in [0, 1]; total >= 0 tokens over all layers; ctx >= 1;
+ *   budgets [L] host int32 written.
+ * Errors: NULL, RANGE (L < 1, total < 0, ctx < 1, a ratio outside [0, 1]).
+ */
+sals_status kv_layer_budgets(const float* nonsparse, int32_t L, int64_t total, int32_t ctx,
+                             int32_t* budgets);
+
+/*
  * kv_compact_from_importance - the selection and gather of kv_compact from an importance the
  * caller supplies (PureKV abstract: attention measured on a lower layer estimates the importance
  * of the tokens of higher layers, so those layers need no attention scores of their own).

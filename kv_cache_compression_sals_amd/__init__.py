@@ -9,6 +9,8 @@ from .binding import (  # noqa: F401
     SalsError,
     kv_compact,
     kv_compact_from_importance,
+    kv_importance_sparsity,
+    kv_layer_budgets,
     kv_compact_workspace_bytes,
     n_selected,
     sals_decode_step,

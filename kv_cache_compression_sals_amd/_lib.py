@@ -53,6 +53,10 @@ PROTOTYPES = {
     "kv_compact": (_I, [ctypes.POINTER(KvcShape), _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _S, _P]),
     "sals_dense_decode_workspace_bytes": (_I, [ctypes.POINTER(KvcShape), _I, _SP]),
     "sals_dense_decode": (_I, [ctypes.POINTER(KvcShape), _P, _P, _P, _I, _I, _P, _P, _S, _P]),
+    "kv_importance_sparsity_workspace_bytes": (_I, [ctypes.POINTER(KvcShape), _I, _I, _SP]),
+    "kv_importance_sparsity": (_I, [ctypes.POINTER(KvcShape), _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _S,
+                                    _P]),
+    "kv_layer_budgets": (_I, [_P, _I, ctypes.c_int64, _I, _P]),
     "kv_compact_from_importance": (_I, [ctypes.POINTER(KvcShape), _P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
     "sals_reconstruct_kv": (_I, [ctypes.POINTER(SalsShape), ctypes.c_float, _P, _P, _P, _P, _I, _I, _I,
                                  _P, _P, _I, _P, _P, _I, _P]),

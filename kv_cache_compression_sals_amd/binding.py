@@ -258,3 +258,37 @@ def kv_compact_from_importance(K: torch.Tensor, V: torch.Tensor, importance: tor
         ctypes.byref(c), _ptr(K), _ptr(V), _ptr(importance), cap, ctx, k_keep, _ptr(Kc), _ptr(Vc),
         _ptr(kept), _stream(stream)))
     return Kc, Vc, kept
+
+
+def kv_importance_sparsity(K: torch.Tensor, Qobs: torch.Tensor, *, ctx: int, p: float,
+                           importance: Optional[torch.Tensor] = None, sparsity: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """kv_compact's importance [B, H_kv, ctx] plus the post-vision sparsity [B, H_q] at threshold p.
+    K [B, H_kv, ctx_cap, d]; Qobs [B, H_q, w, d]. Returns (importance, sparsity)."""
+    B, H_kv, ctx_cap, d = K.shape
+    H_q, w = Qobs.shape[1], Qobs.shape[2]
+    c = KvcShape(B, H_q, H_kv, d, _dtype(K, Qobs))
+    if importance is None:
+        importance = torch.empty((B, H_kv, ctx), dtype=torch.float32, device=K.device)
+    if sparsity is None:
+        sparsity = torch.empty((B, H_q), dtype=torch.float32, device=K.device)
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _check("kv_importance_sparsity_workspace_bytes",
+               lib().kv_importance_sparsity_workspace_bytes(ctypes.byref(c), ctx, w, ctypes.byref(n)))
+        workspace = _ws(n.value, K.device, None)
+    _check("kv_importance_sparsity", lib().kv_importance_sparsity(
+        ctypes.byref(c), _ptr(K), _ptr(Qobs), w, ctx_cap, ctx, ctypes.c_float(p), _ptr(importance),
+        _ptr(sparsity), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return importance, sparsity
+
+
+def kv_layer_budgets(nonsparse, *, total: int, ctx: int):
+    """Layer budgets floor(total * nu_l / sum(nu)) clamped to [1, ctx] (host arithmetic)."""
+    import array
+    nu = array.array("f", [float(x) for x in nonsparse])
+    out = array.array("i", [0] * len(nu))
+    nu_addr, _ = nu.buffer_info()
+    out_addr, _ = out.buffer_info()
+    _check("kv_layer_budgets", lib().kv_layer_budgets(nu_addr, len(nu), int(total), ctx, out_addr))
+    return list(out)

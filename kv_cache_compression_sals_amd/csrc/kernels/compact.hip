@@ -204,14 +204,18 @@ __global__ void imp_merge_kernel(const float* __restrict__ part, float* __restri
   stats[2 * (size_t)e + 1] = S;
 }
 
-// Pass 2: I[b][g][t]. grid (n_chunks, H_kv, B).
+// Pass 2: I[b][g][t]. grid (n_chunks, H_kv, B). With cnt, it also counts per query head the
+// causal entries of this chunk whose probability is below p_thresh (the post-vision sparsity):
+// cnt[(b * H_q + h) * n_chunks + c], exact as float sums of whole numbers below 2^24.
 template <class T, int DH>
 __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::elem* __restrict__ K,
                                                              const typename T::elem* __restrict__ Q,
                                                              const float* __restrict__ stats,
                                                              float* __restrict__ I, int H_q,
-                                                             int H_kv, int w, int ctx_cap, int ctx) {
+                                                             int H_kv, int w, int ctx_cap, int ctx,
+                                                             float p_thresh, float* __restrict__ cnt) {
   __shared__ float acc_lds[kChunk];
+  __shared__ float cnt_red[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -222,8 +226,10 @@ __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::e
   for (int j = tid; j < kChunk; j += kThreads) acc_lds[j] = 0.f;
   __syncthreads();
   const int n_qg = ceil_div(w, kQG);
+  const int n_chunks = gridDim.x;
   for (int hh = 0; hh < nqh; ++hh) {
     const int h = g * nqh + hh;
+    float below = 0.f;  // this lane's entries under the threshold, for head h
     for (int qg = 0; qg < n_qg; ++qg) {
       Frags<T, DH> f;
       load_q_frags<T, DH>(Q + ((size_t)b * H_q + h) * w * DH, w, qg, lane, f);
@@ -253,7 +259,9 @@ __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::e
           for (int i = 0; i < 4; ++i) {
             const int t = t0 + q4 * 4 + i;
             const float e = __builtin_amdgcn_exp2f(acc[nb][i] * scale - M[nb]) * invS[nb];
-            part[i] += (full || (qi < w && t <= lim)) ? e : 0.f;
+            const bool valid = full || (qi < w && t <= lim);
+            part[i] += valid ? e : 0.f;
+            if (cnt) below += (valid && e < p_thresh) ? 1.f : 0.f;
           }
         }
         // sum over the 16 queries of the row (DPP, no LDS crossbar)
@@ -267,6 +275,13 @@ __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::e
           }
         }
       });
+    }
+    if (cnt) {  // workgroup total for head h (waves in order)
+      below = wave_sum(below);
+      if (lane == 0) cnt_red[wave] = below;
+      __syncthreads();
+      if (tid == 0) cnt[((size_t)b * H_q + h) * n_chunks + c] = ((cnt_red[0] + cnt_red[1]) + cnt_red[2]) + cnt_red[3];
+      __syncthreads();
     }
   }
   __syncthreads();
@@ -463,14 +478,30 @@ hipError_t launch_importance_stats(int dtype, const void* K, const void* Qobs, f
   return hipGetLastError();
 }
 
+// Sparsity[b][h] = (sum over chunks of cnt) / (number of causal entries of the w rows).
+__global__ void sparsity_kernel(const float* __restrict__ cnt, float* __restrict__ sparsity, int n,
+                                int n_chunks, double total) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  double s = 0.0;
+  for (int c = 0; c < n_chunks; ++c) s += cnt[(size_t)e * n_chunks + c];
+  sparsity[e] = (float)(s / total);
+}
+
 hipError_t launch_importance_accum(int dtype, const void* K, const void* Qobs,
                                    const float* stats, float* I, int B, int H_q, int H_kv, int d,
-                                   int w, int ctx_cap, int ctx, hipStream_t st) {
+                                   int w, int ctx_cap, int ctx, hipStream_t st, float p_thresh,
+                                   float* cnt, float* sparsity) {
   dim3 grid(ceil_div(ctx, kChunk), H_kv, B);
   SALS_KVC_DISPATCH(dtype, d,
                     (imp_accum_kernel<TT, DD><<<grid, kThreads, 0, st>>>(
                         (const TT::elem*)K, (const TT::elem*)Qobs, stats, I, H_q, H_kv, w, ctx_cap,
-                        ctx)));
+                        ctx, p_thresh, cnt)));
+  if (cnt && sparsity) {
+    const int n = B * H_q;
+    const double total = (double)w * (ctx - w) + (double)w * (w + 1) / 2;
+    sparsity_kernel<<<ceil_div(n, 256), 256, 0, st>>>(cnt, sparsity, n, (int)grid.x, total);
+  }
   return hipGetLastError();
 }
 

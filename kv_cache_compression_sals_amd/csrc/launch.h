@@ -117,7 +117,8 @@ hipError_t launch_importance_stats(int dtype, const void* K, const void* Qobs, f
 // I[b][g][t] from the stats (second pass over K).
 hipError_t launch_importance_accum(int dtype, const void* K, const void* Qobs,
                                    const float* stats, float* I, int B, int H_q, int H_kv, int d,
-                                   int w, int ctx_cap, int ctx, hipStream_t st);
+                                   int w, int ctx_cap, int ctx, hipStream_t st,
+                                   float p_thresh = 0.f, float* cnt = nullptr, float* sparsity = nullptr);
 
 // Kc/Vc[b][g][j] = K/V[b][g][kept[b][g][j]].
 hipError_t launch_gather_rows(int dtype, const void* K, const void* V, const int32_t* kept,

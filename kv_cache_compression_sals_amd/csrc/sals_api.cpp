@@ -398,6 +398,61 @@ sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const v
   return e == hipSuccess ? SALS_OK : hip_fail(e);
 }
 
+sals_status kv_importance_sparsity_workspace_bytes(const kvc_shape* c, int32_t ctx, int32_t w,
+                                                 size_t* bytes) {
+  if (!bytes) return SALS_ERR_NULL;
+  CompactPlan p;
+  sals_status st = make_compact_plan(c, ctx, w, 1, &p);
+  if (st != SALS_OK) return st;
+  const size_t n_chunks = (ctx + kImpChunk - 1) / kImpChunk;
+  *bytes = p.off_I + align_up((size_t)c->B * c->H_q * n_chunks * 4);  // stats, then the counts
+  return SALS_OK;
+}
+
+sals_status kv_importance_sparsity(const kvc_shape* c, const void* K, const void* Qobs, int32_t w,
+                                  int32_t ctx_cap, int32_t ctx, float p_thresh, float* importance,
+                                  float* sparsity, void* ws, size_t ws_bytes, sals_stream_t stream) {
+  if (!c || !K || !Qobs || !importance || !sparsity) return SALS_ERR_NULL;
+  CompactPlan p;
+  sals_status st = make_compact_plan(c, ctx, w, 1, &p);
+  if (st != SALS_OK) return st;
+  if (ctx > ctx_cap || !(p_thresh >= 0.f && p_thresh <= 1.f)) return SALS_ERR_RANGE;
+  if (misaligned(K) || misaligned(Qobs) || misaligned(importance) || misaligned(sparsity) || misaligned(ws))
+    return SALS_ERR_ALIGN;
+  size_t need = 0;
+  if ((st = kv_importance_sparsity_workspace_bytes(c, ctx, w, &need)) != SALS_OK) return st;
+  if (!ws || ws_bytes < need) return SALS_ERR_WORKSPACE;
+  if ((st = device_ready()) != SALS_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  float* stats = (float*)((char*)ws + p.off_stats);
+  float* cnt = (float*)((char*)ws + p.off_I);
+  hipError_t e = sals::launch_importance_stats(c->dtype, K, Qobs, stats, c->B, c->H_q, c->H_kv,
+                                               c->d, w, ctx_cap, ctx, hs);
+  if (e == hipSuccess)
+    e = sals::launch_importance_accum(c->dtype, K, Qobs, stats, importance, c->B, c->H_q, c->H_kv,
+                                      c->d, w, ctx_cap, ctx, hs, p_thresh, cnt, sparsity);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
+sals_status kv_layer_budgets(const float* nonsparse, int32_t L, int64_t total, int32_t ctx,
+                             int32_t* budgets) {
+  if (!nonsparse || !budgets) return SALS_ERR_NULL;
+  if (L < 1 || total < 0 || ctx < 1) return SALS_ERR_RANGE;
+  double Z = 0.0;
+  for (int l = 0; l < L; ++l) {
+    if (!(nonsparse[l] >= 0.f && nonsparse[l] <= 1.f)) return SALS_ERR_RANGE;
+    Z += (double)nonsparse[l];
+  }
+  for (int l = 0; l < L; ++l) {
+    const double share = Z > 0.0 ? (double)total * (double)nonsparse[l] / Z : (double)total / L;
+    double k = floor(share);
+    if (k < 1.0) k = 1.0;
+    if (k > ctx) k = ctx;
+    budgets[l] = (int32_t)k;
+  }
+  return SALS_OK;
+}
+
 sals_status kv_compact_from_importance(const kvc_shape* c, const void* K, const void* V,
                                       const float* importance, int32_t ctx_cap, int32_t ctx,
                                       int32_t k_keep, void* Kc, void* Vc, int32_t* kept,

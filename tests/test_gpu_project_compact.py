@@ -235,3 +235,41 @@ def test_compact_higher_layer_from_lower_layer_importance():
     ref = oracle.compact_from_importance(high["K"], high["V"], imp.cpu().numpy(), k_keep=300)
     assert np.array_equal(kept.cpu().numpy(), ref["kept"])
     assert np.array_equal(Kc.view(torch.int16).cpu().numpy().view(np.uint16), ref["Kc"])
+
+
+# ---- post-vision sparsity and layer budgets ---------------------------------------------------
+
+SPARSE = [
+    # cfg overrides, ctx, ctx_cap, p, heads checked ((b, h) pairs, None = all)
+    (dict(B=2, H_q=8, H_kv=4, ctx=2000, w=24, n_visual=1500, grid_h=30, grid_w=50, clusters_h=3, clusters_w=5),
+     2000, 2100, 1e-3, None),
+    (dict(B=1, H_q=4, H_kv=4, ctx=1500, w=80, n_visual=1200, grid_h=30, grid_w=40, clusters_h=3, clusters_w=4),
+     1500, 1500, 1e-2, None),
+    ({}, 16384, 16384, 1e-3, [(0, 0), (7, 13), (15, 31)]),
+]
+
+
+@pytest.mark.parametrize("ov,ctx,cap,p,pairs", SPARSE, ids=["gqa_w24", "w80_p1e-2", "c4_full_sampled"])
+def test_importance_sparsity_matches_oracle(ov, ctx, cap, p, pairs):
+    """Below-threshold counts per query head within the entries the oracle finds at p (relative
+    1e-5), and the importance identical to kv_compact's."""
+    cfg = C4.with_(**ov)
+    case = compact_case(cfg, ctx=ctx, ctx_cap=cap, threads=16)
+    print(f"sparsity B={case['K'].shape[0]} H_q={case['H_q']} H_kv={case['H_kv']} ctx={ctx} p={p}", flush=True)
+    dt = case["dtype"]
+    K, V, Q = to_device(case["K"], dt), to_device(case["V"], dt), to_device(case["Qobs"], dt)
+    imp, sp = sals.kv_importance_sparsity(K, Q, ctx=ctx, p=p)
+    _, _, _, imp2 = sals.kv_compact(K, V, Q, ctx=ctx, k_keep=max(1, ctx // 10), want_importance=True)
+    torch.cuda.synchronize()
+    assert torch.equal(imp, imp2)
+    sp = sp.cpu().numpy()
+    H_q, H_kv = case["H_q"], case["H_kv"]
+    B = case["K"].shape[0]
+    todo = [(b, h) for b in range(B) for h in range(H_q)] if pairs is None else pairs
+    Qf = oracle.stored_to_f64(case["Qobs"], dt)
+    for b, h in todo:
+        g = oracle.kv_head_of(h, H_q, H_kv)
+        G, below, total, near = oracle.sparsity(Qf[b, h], oracle.stored_to_f64(case["K"][b, g, :ctx], dt), ctx, p)
+        err = abs(float(sp[b, h]) * total - below)
+        assert err <= near + 0.5 + 1e-6 * total, (b, h, float(sp[b, h]), G, near)
+    print(f"   sparsity range {sp.min():.4f} .. {sp.max():.4f}", flush=True)
