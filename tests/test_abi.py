@@ -241,3 +241,24 @@ def _gpu_present():
 def test_valid_call_without_device_reports_hip_error():
     assert _step() == HIP
     assert lib().sals_last_hip_error() != 0
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/sals.h compiles as C99 with warnings as errors, and a C program that calls every
+    declared function by address links against the built library."""
+    import shutil
+    import subprocess
+
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    names = declared_functions()
+    lib_dir = os.path.join(ROOT, "kv_cache_compression_sals_amd")
+    src = tmp_path / "abi.c"
+    src.write_text('#include "sals.h"\ntypedef void (*fn)(void);\nint main(void) {\n  fn f[] = {'
+                   + ", ".join(f"(fn)&{n}" for n in names)
+                   + '};\n  for (unsigned i = 0; i < sizeof f / sizeof f[0]; ++i) if (!f[i]) return 1;\n'
+                   '  return sals_abi_version() == 1 ? 0 : 2;\n}\n')
+    exe = tmp_path / "abi"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-L", lib_dir, "-lsals", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], check=True)
+    assert subprocess.run([str(exe)]).returncode == 0
