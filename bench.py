@@ -311,11 +311,8 @@ def run_compact_workload(cfg, steps, warmup, label):
     reuse = lambda: sals.kv_compact_from_importance(K, V, imp, k_keep=kk, Kc=Kc, Vc=Vc, kept=kept)
     # importance plus the post-vision sparsity per head at p = 1e-3 (the input of layer budgets)
     spars = torch.empty((B, Qobs.shape[1]), dtype=torch.float32, device="cuda")
-    n_ws = ctypes.c_size_t(0)
-    from kv_cache_compression_sals_amd._lib import KvcShape, lib
-    lib().kv_importance_sparsity_workspace_bytes(ctypes.byref(KvcShape(B, Qobs.shape[1], H_kv, d, 1)), ctx,
-                                                 Qobs.shape[2], ctypes.byref(n_ws))
-    ws_s = torch.empty(n_ws.value, dtype=torch.uint8, device="cuda")
+    ws_s = torch.empty(sals.kv_importance_sparsity_workspace_bytes(K, Qobs, ctx=ctx), dtype=torch.uint8,
+                       device="cuda")
     sparse = lambda: sals.kv_importance_sparsity(K, Qobs, ctx=ctx, p=1e-3, importance=imp, sparsity=spars,
                                                  workspace=ws_s)
 

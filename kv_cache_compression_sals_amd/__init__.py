@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     kv_compact,
     kv_compact_from_importance,
     kv_importance_sparsity,
+    kv_importance_sparsity_workspace_bytes,
     kv_layer_budgets,
     kv_compact_workspace_bytes,
     n_selected,

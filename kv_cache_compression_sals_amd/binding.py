@@ -260,6 +260,15 @@ def kv_compact_from_importance(K: torch.Tensor, V: torch.Tensor, importance: tor
     return Kc, Vc, kept
 
 
+def kv_importance_sparsity_workspace_bytes(K: torch.Tensor, Qobs: torch.Tensor, *, ctx: int) -> int:
+    B, H_kv, _, d = K.shape
+    c = KvcShape(B, Qobs.shape[1], H_kv, d, _dtype(K, Qobs))
+    n = ctypes.c_size_t(0)
+    _check("kv_importance_sparsity_workspace_bytes",
+           lib().kv_importance_sparsity_workspace_bytes(ctypes.byref(c), ctx, Qobs.shape[2], ctypes.byref(n)))
+    return n.value
+
+
 def kv_importance_sparsity(K: torch.Tensor, Qobs: torch.Tensor, *, ctx: int, p: float,
                            importance: Optional[torch.Tensor] = None, sparsity: Optional[torch.Tensor] = None,
                            workspace: Optional[torch.Tensor] = None, stream=None):
@@ -273,10 +282,7 @@ def kv_importance_sparsity(K: torch.Tensor, Qobs: torch.Tensor, *, ctx: int, p: 
     if sparsity is None:
         sparsity = torch.empty((B, H_q), dtype=torch.float32, device=K.device)
     if workspace is None:
-        n = ctypes.c_size_t(0)
-        _check("kv_importance_sparsity_workspace_bytes",
-               lib().kv_importance_sparsity_workspace_bytes(ctypes.byref(c), ctx, w, ctypes.byref(n)))
-        workspace = _ws(n.value, K.device, None)
+        workspace = _ws(kv_importance_sparsity_workspace_bytes(K, Qobs, ctx=ctx), K.device, None)
     _check("kv_importance_sparsity", lib().kv_importance_sparsity(
         ctypes.byref(c), _ptr(K), _ptr(Qobs), w, ctx_cap, ctx, ctypes.c_float(p), _ptr(importance),
         _ptr(sparsity), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
