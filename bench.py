@@ -348,31 +348,33 @@ def run_compact_workload(cfg, steps, warmup, label):
 
 
 def _layer_inputs(layer):
-    """One layer of the 128K-context workload, generated in a worker process."""
-    from threadpoolctl import threadpool_limits
-
+    """One layer of the 128K-context workload (NumPy releases the GIL in its bulk work, so the
+    layers are generated by threads of this process: no child process ever exists)."""
     from workloads import CONFIGS, decode_case
 
-    with threadpool_limits(1):
-        c = decode_case(CONFIGS["c5"], layer=layer)
+    c = decode_case(CONFIGS["c5"], layer=layer)
     return layer, {n: c[n] for n in ("q", "Lk", "Lv", "Pk", "Pv")}
 
 
 def run_layers_workload(cfg, steps, warmup, label, n_layers=32):
     """One decode step through n_layers independent layers (all resident): `steps` steps captured
     as one HIP graph, one upload replay, then one timed replay."""
-    import multiprocessing as mp
+    from concurrent.futures import ThreadPoolExecutor, as_completed
 
     import numpy as np
     import torch
+    from threadpoolctl import threadpool_limits
 
     import kv_cache_compression_sals_amd as sals
 
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
     t0 = time.time()
     layers = [None] * n_layers
-    with mp.get_context("spawn").Pool(min(16, os.cpu_count() or 1)) as pool:
-        for i, (l, arrs) in enumerate(pool.imap_unordered(_layer_inputs, range(n_layers))):
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        futs = [ex.submit(_layer_inputs, l) for l in range(n_layers)]
+        for i, fut in enumerate(as_completed(futs)):
+            l, arrs = fut.result()
             layers[l] = {n: dev(a) for n, a in arrs.items()}
             log(f"[{label}] layer {l} resident ({i + 1}/{n_layers}, {time.time() - t0:.0f}s)")
     log(f"[{label}] generated and uploaded {n_layers} layers in {time.time() - t0:.1f}s")

@@ -65,14 +65,52 @@ def _ws(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+def _expect(t: Optional[torch.Tensor], name: str, shape, dtype=None) -> None:
+    """ValueError unless t has exactly this shape (and dtype). The C ABI sees only pointers, so a
+    tensor of the wrong size would be read or written out of bounds on the device."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+
+
+def _check_decode_args(q, Lk, Lv, Pk, Pv, ctx):
+    """Shapes of one decode step's inputs: q [B, H_q, d], Pk and Pv [H_kv d, r], Lk and Lv
+    [B, ctx_cap, r] with ctx <= ctx_cap."""
+    if q.dim() != 3 or Pk.dim() != 2 or Lk.dim() != 3:
+        raise ValueError("q must be [B, H_q, d], Pk [H_kv*d, r], Lk [B, ctx_cap, r]")
+    B, H_q, d = q.shape
+    D, r = Pk.shape
+    if D % d != 0 or D // d < 1:
+        raise ValueError(f"Pk rows {D} are not a multiple of d = {d}")
+    _expect(Pv, "Pv", (D, r))
+    _expect(Lk, "Lk", (B, Lk.shape[1], r))
+    _expect(Lv, "Lv", tuple(Lk.shape))
+    if not 1 <= ctx <= Lk.shape[1]:
+        raise ValueError(f"ctx = {ctx} outside [1, ctx_cap = {Lk.shape[1]}]")
+
+
 # ---- projection -----------------------------------------------------------------------------
 
 def sals_project_kv(Xk: torch.Tensor, Pk: torch.Tensor, Lk: torch.Tensor, t0: int, *, d: int,
                     Xv: Optional[torch.Tensor] = None, Pv: Optional[torch.Tensor] = None,
                     Lv: Optional[torch.Tensor] = None, stream=None) -> None:
     """L[:, t0:t0+T] = X . P for K (and V). X [B, T, H_kv*d], P [H_kv*d, r], L [B, ctx_cap, r]."""
+    if Xk.dim() != 3 or Pk.dim() != 2 or Lk.dim() != 3:
+        raise ValueError("Xk must be [B, T, H_kv*d], Pk [H_kv*d, r], Lk [B, ctx_cap, r]")
     B, T, D = Xk.shape
     r = Pk.shape[1]
+    if D % d != 0:
+        raise ValueError(f"row width {D} is not a multiple of d = {d}")
+    _expect(Pk, "Pk", (D, r))
+    _expect(Lk, "Lk", (B, Lk.shape[1], r))
+    _expect(Xv, "Xv", tuple(Xk.shape))
+    _expect(Pv, "Pv", tuple(Pk.shape))
+    _expect(Lv, "Lv", tuple(Lk.shape))
+    if t0 < 0 or t0 + T > Lk.shape[1]:
+        raise ValueError(f"rows [{t0}, {t0 + T}) do not fit ctx_cap = {Lk.shape[1]}")
     s = SalsShape(B, 1, D // d, d, r, _dtype(Xk, Pk, Lk, Xv, Pv, Lv))
     _check("sals_project_kv", lib().sals_project_kv(
         ctypes.byref(s), _ptr(Xk), _ptr(Xv), _ptr(Pk), _ptr(Pv), _ptr(Lk), _ptr(Lv), Lk.shape[1], t0, T,
@@ -108,8 +146,11 @@ def sals_decode_step(q: torch.Tensor, Lk: torch.Tensor, Lv: torch.Tensor, Pk: to
     """One SALS decode step. q [B, H_q, d] pre-RoPE; Lk/Lv [B, ctx_cap, r]; Pk/Pv [H_kv*d, r].
     Returns (out [B, H_q, d] fp32, sel [B, G, n_sel] int32 or None)."""
     dt = _dtype(q, Lk, Lv, Pk, Pv)
+    _check_decode_args(q, Lk, Lv, Pk, Pv, ctx)
     B, H_q, d = q.shape
     s, sel = _decode_structs(q, Pk, Pk.shape[1], k, w, G, dt)
+    _expect(out, "out", (B, H_q, d), torch.float32)
+    _expect(sel_out, "sel_out", (B, G, n_selected(ctx, k, w)), torch.int32)
     if out is None:
         out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
     if sel_out is None and want_sel:
@@ -136,8 +177,11 @@ def sals_decode_step_traced(q: torch.Tensor, Lk: torch.Tensor, Lv: torch.Tensor,
     if len(events) != 6:
         raise ValueError("sals_decode_step_traced needs exactly 6 events")
     dt = _dtype(q, Lk, Lv, Pk, Pv)
+    _check_decode_args(q, Lk, Lv, Pk, Pv, ctx)
     B, H_q, d = q.shape
     s, sel = _decode_structs(q, Pk, Pk.shape[1], k, w, G, dt)
+    _expect(out, "out", (B, H_q, d), torch.float32)
+    _expect(sel_out, "sel_out", (B, G, n_selected(ctx, k, w)), torch.int32)
     if out is None:
         out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
     if sel_out is None and want_sel:
@@ -171,8 +215,18 @@ def kv_compact(K: torch.Tensor, V: torch.Tensor, Qobs: torch.Tensor, *, ctx: int
                want_importance: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
     """K, V [B, H_kv, ctx_cap, d] post-RoPE; Qobs [B, H_q, w, d].
     Returns (Kc, Vc [B, H_kv, k_keep, d], kept [B, H_kv, k_keep] int32, importance or None)."""
+    if K.dim() != 4 or Qobs.dim() != 4:
+        raise ValueError("K, V must be [B, H_kv, ctx_cap, d] and Qobs [B, H_q, w, d]")
     B, H_kv, ctx_cap, d = K.shape
     w = Qobs.shape[2]
+    _expect(V, "V", tuple(K.shape))
+    _expect(Qobs, "Qobs", (B, Qobs.shape[1], w, d))
+    _expect(Kc, "Kc", (B, H_kv, k_keep, d), K.dtype)
+    _expect(Vc, "Vc", (B, H_kv, k_keep, d), K.dtype)
+    _expect(kept, "kept", (B, H_kv, k_keep), torch.int32)
+    _expect(importance, "importance", (B, H_kv, ctx), torch.float32)
+    if not 1 <= ctx <= ctx_cap:
+        raise ValueError(f"ctx = {ctx} outside [1, ctx_cap = {ctx_cap}]")
     c = KvcShape(B, Qobs.shape[1], H_kv, d, _dtype(K, V, Qobs))
     dev = K.device
     if Kc is None:
@@ -205,9 +259,16 @@ def sals_dense_decode(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, *, n: O
                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                       stream=None) -> torch.Tensor:
     """q [B, H_q, d] post-RoPE; K, V [B, H_kv, stride, d]; attends over rows [0, n)."""
+    if q.dim() != 3 or K.dim() != 4:
+        raise ValueError("q must be [B, H_q, d] and K, V [B, H_kv, stride, d]")
     B, H_q, d = q.shape
     stride = K.shape[2]
     n = stride if n is None else n
+    _expect(K, "K", (B, K.shape[1], stride, d))
+    _expect(V, "V", tuple(K.shape))
+    _expect(out, "out", (B, H_q, d), torch.float32)
+    if not 1 <= n <= stride:
+        raise ValueError(f"n = {n} outside [1, stride = {stride}]")
     c = KvcShape(B, H_q, K.shape[1], d, _dtype(q, K, V))
     if out is None:
         out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
@@ -228,8 +289,22 @@ def sals_reconstruct_kv(Lk: torch.Tensor, Pk: torch.Tensor, K: torch.Tensor, *, 
                         q_pos: int = 0, stream=None) -> None:
     """K[:, :, t0:t0+T] = RoPE_t(L_k . P_k^T) (and V without RoPE); with q, q_rot = RoPE_{q_pos}(q).
     Lk/Lv [B, ctx_cap, r]; Pk/Pv [H_kv*d, r]; K/V [B, H_kv, stride_tokens, d]; q/q_rot [B, H_q, d]."""
+    if K.dim() != 4 or Lk.dim() != 3 or Pk.dim() != 2:
+        raise ValueError("Lk must be [B, ctx_cap, r], Pk [H_kv*d, r], K [B, H_kv, stride, d]")
     B, H_kv, stride, _ = K.shape
     H_q = q.shape[1] if q is not None else H_kv
+    r = Pk.shape[1]
+    _expect(Pk, "Pk", (H_kv * d, r))
+    _expect(K, "K", (B, H_kv, stride, d))
+    _expect(Lk, "Lk", (B, Lk.shape[1], r))
+    _expect(Lv, "Lv", tuple(Lk.shape))
+    _expect(Pv, "Pv", tuple(Pk.shape))
+    _expect(V, "V", tuple(K.shape))
+    if q is not None:
+        _expect(q, "q", (B, H_q, d))
+        _expect(q_rot, "q_rot", tuple(q.shape))
+    if t0 < 0 or t0 + T > min(Lk.shape[1], stride):
+        raise ValueError(f"rows [{t0}, {t0 + T}) do not fit ctx_cap = {Lk.shape[1]} and stride = {stride}")
     s = SalsShape(B, H_q, H_kv, d, Pk.shape[1], _dtype(Lk, Pk, K, Lv, Pv, V, q, q_rot))
     _check("sals_reconstruct_kv", lib().sals_reconstruct_kv(
         ctypes.byref(s), ctypes.c_float(rope_base), _ptr(Lk), _ptr(Lv), _ptr(Pk), _ptr(Pv), Lk.shape[1],
@@ -243,10 +318,22 @@ def kv_compact_from_importance(K: torch.Tensor, V: torch.Tensor, importance: tor
     """Keep the k_keep most important rows per (sequence, KV head) by a given importance
     [B, H_kv, ctx] fp32 (e.g. another layer's kv_compact importance). K, V [B, H_kv, ctx_cap, d].
     Returns (Kc, Vc [B, H_kv, k_keep, d], kept [B, H_kv, k_keep] int32)."""
+    if K.dim() != 4 or importance.dim() != 3:
+        raise ValueError("K, V must be [B, H_kv, ctx_cap, d] and importance [B, H_kv, ctx]")
     B, H_kv, cap, d = K.shape
     ctx = importance.shape[2] if ctx is None else ctx
     if importance.dtype != torch.float32:
         raise ValueError("importance must be float32")
+    if importance.shape[0] != B or importance.shape[1] != H_kv or importance.shape[2] < ctx:
+        raise ValueError(f"importance: shape {tuple(importance.shape)}, expected ({B}, {H_kv}, >= {ctx})")
+    if not importance.is_contiguous() or importance.shape[2] != ctx:
+        importance = importance[:, :, :ctx].contiguous()
+    _expect(V, "V", tuple(K.shape))
+    _expect(Kc, "Kc", (B, H_kv, k_keep, d), K.dtype)
+    _expect(Vc, "Vc", (B, H_kv, k_keep, d), K.dtype)
+    _expect(kept, "kept", (B, H_kv, k_keep), torch.int32)
+    if not 1 <= ctx <= cap:
+        raise ValueError(f"ctx = {ctx} outside [1, ctx_cap = {cap}]")
     c = KvcShape(B, H_kv, H_kv, d, _dtype(K, V))
     if Kc is None:
         Kc = torch.empty((B, H_kv, k_keep, d), dtype=K.dtype, device=K.device)
@@ -274,8 +361,15 @@ def kv_importance_sparsity(K: torch.Tensor, Qobs: torch.Tensor, *, ctx: int, p: 
                            workspace: Optional[torch.Tensor] = None, stream=None):
     """kv_compact's importance [B, H_kv, ctx] plus the post-vision sparsity [B, H_q] at threshold p.
     K [B, H_kv, ctx_cap, d]; Qobs [B, H_q, w, d]. Returns (importance, sparsity)."""
+    if K.dim() != 4 or Qobs.dim() != 4:
+        raise ValueError("K must be [B, H_kv, ctx_cap, d] and Qobs [B, H_q, w, d]")
     B, H_kv, ctx_cap, d = K.shape
     H_q, w = Qobs.shape[1], Qobs.shape[2]
+    _expect(Qobs, "Qobs", (B, H_q, w, d))
+    _expect(importance, "importance", (B, H_kv, ctx), torch.float32)
+    _expect(sparsity, "sparsity", (B, H_q), torch.float32)
+    if not 1 <= ctx <= ctx_cap:
+        raise ValueError(f"ctx = {ctx} outside [1, ctx_cap = {ctx_cap}]")
     c = KvcShape(B, H_q, H_kv, d, _dtype(K, Qobs))
     if importance is None:
         importance = torch.empty((B, H_kv, ctx), dtype=torch.float32, device=K.device)

@@ -6,7 +6,13 @@ to the lowest index. The window is always kept, the set has exactly n_sel entrie
 strictly ascending.
 
 Outputs: the GPU output is compared with the oracle's attention over the GPU's own selected
-set (so an exempt swap cannot inflate the error), max-abs <= 1e-4 for fp32, 2e-2 for bf16.
+set (so an exempt swap cannot inflate the error). Two bounds are asserted:
+  * the stated tolerance, max-abs <= 1e-4 for fp32 and 2e-2 for bf16 caches;
+  * a tight bound, max-abs <= 1e-4 for every cache type. The stored inputs are exact on both
+    sides (bf16 widens to fp32 exactly) and every sum on the GPU is fp32; the fp32 vectors that
+    enter bf16 MFMAs as high + low bf16 parts carry about 2^-16 relative error. An output is a
+    convex combination of value rows of magnitude O(1) to O(10), so the accumulated error stays
+    near 1e-6; the bf16 tolerance alone would let a 1e-3 angle or value-side slip through.
 """
 
 from __future__ import annotations
@@ -16,6 +22,7 @@ import numpy as np
 import oracle
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+TIGHT = 1e-4
 EXEMPT_REL = 1e-4
 
 
@@ -68,6 +75,7 @@ def decode_parity(case: dict, out_gpu: np.ndarray, sel_gpu: np.ndarray, batches=
     Pk, Pv = oracle.stored_to_f64(case["Pk"], dt), oracle.stored_to_f64(case["Pv"], dt)
     max_err = 0.0
     max_err_vs_ora_set = 0.0
+    sq_err = sq_ref = 0.0
     exempt = 0
     for b in batches:
         for s in range(G):
@@ -78,6 +86,10 @@ def decode_parity(case: dict, out_gpu: np.ndarray, sel_gpu: np.ndarray, batches=
                                         case["base"], H_kv, G)
         err = np.abs(out_gpu[b] - ref).max()
         max_err = max(max_err, err)
+        sq_err += float(((out_gpu[b] - ref) ** 2).sum())
+        sq_ref += float((ref ** 2).sum())
         max_err_vs_ora_set = max(max_err_vs_ora_set, np.abs(out_gpu[b] - ora["out"][b]).max())
     assert max_err <= tol, f"max-abs error {max_err:.3e} > {tol:.1e}"
-    return dict(max_err=max_err, max_err_vs_oracle_set=max_err_vs_ora_set, exempt=exempt)
+    assert max_err <= TIGHT, f"max-abs error {max_err:.3e} > tight bound {TIGHT:.1e}"
+    rel_rms = (sq_err / sq_ref) ** 0.5 if sq_ref > 0 else 0.0
+    return dict(max_err=max_err, rel_rms=rel_rms, max_err_vs_oracle_set=max_err_vs_ora_set, exempt=exempt)

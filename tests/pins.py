@@ -34,6 +34,47 @@ def _run_decode(q, Lk, Lv, Pk, Pv, T, k, w, G, H_kv, base=10000.0):
 
 
 # ---------------------------------------------------------------------------------------------
+# storage decode
+# ---------------------------------------------------------------------------------------------
+
+def _ieee_value(bits: int, exp_bits: int, man_bits: int) -> float:
+    """Value of a finite IEEE binary pattern from the format's definition: sign, biased exponent,
+    fraction; a zero exponent field is subnormal (no implicit leading one)."""
+    bias = (1 << (exp_bits - 1)) - 1
+    sign = -1.0 if (bits >> (exp_bits + man_bits)) & 1 else 1.0
+    e = (bits >> man_bits) & ((1 << exp_bits) - 1)
+    m = bits & ((1 << man_bits) - 1)
+    if e == 0:
+        return sign * math.ldexp(m, 1 - bias - man_bits)
+    return sign * math.ldexp((1 << man_bits) + m, e - bias - man_bits)
+
+
+def pin_stored_decode():
+    """bf16 bit patterns decode to the IEEE binary16-brain values (1 sign, 8 exponent, 7 fraction
+    bits): named patterns, then every finite pattern against the definition; fp32 values decode
+    unchanged, checked on named and random finite bit patterns."""
+    named = {0x3F80: 1.0, 0xC000: -2.0, 0x0000: 0.0, 0x4049: 3.140625, 0x3EAB: 0.333984375,
+             0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126,
+             0x807F: -(127 * 2.0 ** -133)}
+    got = OS.stored_to_f64(np.array(list(named), dtype=np.uint16), "bf16")
+    assert got.dtype == np.float64
+    assert list(got) == list(named.values()), got
+    neg0 = OS.stored_to_f64(np.array([0x8000], dtype=np.uint16), "bf16")[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) == -1.0
+    pats = np.array([b for b in range(1 << 16) if (b >> 7) & 0xFF != 0xFF], dtype=np.uint16)
+    ref = np.array([_ieee_value(int(b), 8, 7) for b in pats])
+    assert np.array_equal(OS.stored_to_f64(pats.reshape(-1, 16), "bf16").ravel(), ref)
+    rs = np.random.default_rng(11)
+    u = rs.integers(0, 1 << 32, size=4000, dtype=np.uint64).astype(np.uint32)
+    u = u[((u >> 23) & 0xFF) != 0xFF]
+    u = np.concatenate([u, np.array([0x00000001, 0x7F7FFFFF, 0x3F800001, 0x80000000], dtype=np.uint32)])
+    f = u.view(np.float32)
+    ref32 = np.array([_ieee_value(int(b), 8, 23) for b in u])
+    assert np.array_equal(OS.stored_to_f64(f, "f32"), ref32)
+    assert np.array_equal(OS.stored_to_f64(np.array([1.5, -0.25]), "f64"), [1.5, -0.25])
+
+
+# ---------------------------------------------------------------------------------------------
 # RoPE
 # ---------------------------------------------------------------------------------------------
 
@@ -397,6 +438,7 @@ def pin_layer_budgets():
 
 
 PINS = [
+    pin_stored_decode,
     pin_rope_d2_closed_form,
     pin_rope_complex_form,
     pin_rope_invariants,

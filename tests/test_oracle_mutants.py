@@ -18,6 +18,14 @@ ORACLE_DIR = os.path.dirname(OS.__file__)
 
 MUTANTS = [
     # (file, original snippet, mutated snippet, what the mistake is)
+    ("sals.py", "return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16)",
+     "return ((np.asarray(a, dtype=np.uint16) << 16).astype(np.uint32))", "bf16 bits shifted before widening"),
+    ("sals.py", "return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16)",
+     "return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 15)", "bf16 bits shifted by 15"),
+    ("sals.py", "return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)",
+     "return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)", "bf16 bits read as IEEE half"),
+    ("sals.py", "return np.asarray(a, dtype=np.float32).astype(np.float64)",
+     "return np.asarray(a, dtype=np.float16).astype(np.float64)", "fp32 decoded through half precision"),
     ("sals.py", "return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=1)",
      "return np.concatenate([x1 * c + x2 * s, x2 * c - x1 * s], axis=1)", "RoPE rotates the wrong way"),
     ("sals.py", "** (-(2.0 * i) / d)", "** (-(1.0 * i) / d)", "RoPE frequency exponent"),
