@@ -16,9 +16,10 @@
  *   - Arrays are device pointers, row-major and contiguous, in the layout stated per argument.
  *     "dtype" arrays hold SALS_F32 (IEEE fp32) or SALS_BF16 (bfloat16) elements.
  *   - Every pointer must be 16-byte aligned (SALS_ERR_ALIGN otherwise).
- *   - The caller owns every buffer, workspaces included. The library never allocates, frees or
- *     synchronises; all work is enqueued on `stream` (NULL = the null stream) and returns
- *     asynchronously. Buffers must stay valid until that work completes.
+ *   - The caller owns every buffer, workspaces included (the one exception is
+ *     sals_decode_step_noalloc, whose workspace is a fixed array the library holds per GPU). The
+ *     library never allocates, frees or synchronises; all work is enqueued on `stream` (NULL = the
+ *     null stream) and returns asynchronously. Buffers must stay valid until that work completes.
  *   - Inputs are never written. Outputs are fully overwritten. Inputs, outputs and workspace
  *     must not overlap.
  *   - All argument checks run before any HIP call, so they cost nothing on the GPU and can be
@@ -147,6 +148,27 @@ sals_status sals_decode_step(const sals_shape* s, const sals_select* sel, float 
                              const void* q, const void* Lk, const void* Lv, const void* Pk,
                              const void* Pv, int32_t ctx_cap, int32_t ctx, float* out,
                              int32_t* sel_out, void* ws, size_t ws_bytes, sals_stream_t stream);
+
+/*
+ * sals_decode_step_noalloc - sals_decode_step for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. It takes no
+ * workspace: the library keeps one SALS_NOALLOC_SCRATCH_BYTES array of device memory per GPU (a
+ * static device symbol, held from the first use on that GPU until the process ends) and runs the
+ * same kernels as sals_decode_step with that array as their workspace, so the results are
+ * bit-identical. It calls no hipMalloc, hipFree or other allocating routine.
+ * Args: as sals_decode_step without ws / ws_bytes. The call runs on the current device.
+ * Limit: the workspace sals_decode_workspace_bytes reports for (s, sel, ctx) must not exceed
+ *   SALS_NOALLOC_SCRATCH_BYTES, else SALS_ERR_WORKSPACE (checked before any HIP call).
+ * Concurrency: every call on one GPU shares that GPU's array, so calls that may overlap on one GPU
+ *   (on different streams, or from different threads without stream ordering) race and must not
+ *   be issued; calls ordered on one stream are safe. Nothing in the array must start at zero.
+ * Errors: as sals_decode_step; SALS_ERR_HIP if the array's device address cannot be looked up.
+ */
+#define SALS_NOALLOC_SCRATCH_BYTES (16u << 20)
+sals_status sals_decode_step_noalloc(const sals_shape* s, const sals_select* sel, float rope_base,
+                                     const void* q, const void* Lk, const void* Lv, const void* Pk,
+                                     const void* Pv, int32_t ctx_cap, int32_t ctx, float* out,
+                                     int32_t* sel_out, sals_stream_t stream);
 
 /*
  * sals_decode_step_traced - sals_decode_step that also records caller-created HIP events on

@@ -164,6 +164,28 @@ def sals_decode_step(q: torch.Tensor, Lk: torch.Tensor, Lv: torch.Tensor, Pk: to
     return out, sel_out
 
 
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def sals_decode_step_noalloc(q: torch.Tensor, Lk: torch.Tensor, Lv: torch.Tensor, Pk: torch.Tensor,
+                             Pv: torch.Tensor, *, ctx: int, k: int, w: int, G: int, out: torch.Tensor,
+                             sel_out: Optional[torch.Tensor] = None, rope_base: float = 10000.0,
+                             stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """sals_decode_step without a workspace: the library's own per-GPU scratch array serves as the
+    workspace (for callers that cannot allocate). out [B, H_q, d] fp32 and sel_out (optional,
+    [B, G, n_sel] int32) must be given; nothing is allocated here or in the library."""
+    dt = _dtype(q, Lk, Lv, Pk, Pv)
+    _check_decode_args(q, Lk, Lv, Pk, Pv, ctx)
+    B, H_q, d = q.shape
+    s, sel = _decode_structs(q, Pk, Pk.shape[1], k, w, G, dt)
+    _expect(out, "out", (B, H_q, d), torch.float32)
+    _expect(sel_out, "sel_out", (B, G, n_selected(ctx, k, w)), torch.int32)
+    _check("sals_decode_step_noalloc", lib().sals_decode_step_noalloc(
+        ctypes.byref(s), ctypes.byref(sel), ctypes.c_float(rope_base), _ptr(q), _ptr(Lk), _ptr(Lv),
+        _ptr(Pk), _ptr(Pv), Lk.shape[1], ctx, _ptr(out), _ptr(sel_out), _stream(stream)))
+    return out, sel_out
+
+
 def sals_decode_step_traced(q: torch.Tensor, Lk: torch.Tensor, Lv: torch.Tensor, Pk: torch.Tensor,
                             Pv: torch.Tensor, events, *, ctx: int, k: int, w: int, G: int,
                             rope_base: float = 10000.0, out: Optional[torch.Tensor] = None,
@@ -392,3 +414,4 @@ def kv_layer_budgets(nonsparse, *, total: int, ctx: int):
     out_addr, _ = out.buffer_info()
     _check("kv_layer_budgets", lib().kv_layer_budgets(nu_addr, len(nu), int(total), ctx, out_addr))
     return list(out)
+

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/sals.h"
 #include "launch.h"
 
@@ -255,6 +257,37 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   return e == hipSuccess ? SALS_OK : hip_fail(e);
 }
 
+// ---- library-owned scratch for callers that cannot allocate ----------------------------------
+
+// The decode workspace of sals_decode_step_noalloc lives here: one array per GPU, held from the
+// library's first use on that GPU until the process ends. In host code `scratch` is a host-side
+// stand-in for the device symbol, not a device address; the device address is looked up once per
+// device with hipGetSymbolAddress and only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[SALS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first call per device,
+// with that device current).
+sals_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!ptr || ((uintptr_t)ptr & 255u) != 0) return hip_fail(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SALS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -343,6 +376,29 @@ sals_status sals_decode_step(const sals_shape* s, const sals_select* sel, float 
                              int32_t* sel_out, void* ws, size_t ws_bytes, sals_stream_t stream) {
   return decode_impl(s, sel, rope_base, q, Lk, Lv, Pk, Pv, ctx_cap, ctx, out, sel_out, ws,
                      ws_bytes, stream, nullptr);
+}
+
+sals_status sals_decode_step_noalloc(const sals_shape* s, const sals_select* sel, float rope_base,
+                                     const void* q, const void* Lk, const void* Lv, const void* Pk,
+                                     const void* Pv, int32_t ctx_cap, int32_t ctx, float* out,
+                                     int32_t* sel_out, sals_stream_t stream) {
+  if (!s || !sel || !q || !Lk || !Lv || !Pk || !Pv || !out) return SALS_ERR_NULL;
+  DecodePlan p;
+  sals_status st = make_decode_plan(s, sel, ctx, &p);
+  if (st != SALS_OK) return st;
+  // the size limit is checked before any HIP call
+  if (p.total > (size_t)SALS_NOALLOC_SCRATCH_BYTES) return SALS_ERR_WORKSPACE;
+  if (ctx > ctx_cap || !(rope_base > 1.0f) || !isfinite(rope_base)) return SALS_ERR_RANGE;
+  if (misaligned(q) || misaligned(Lk) || misaligned(Lv) || misaligned(Pk) || misaligned(Pv) ||
+      misaligned(out) || misaligned(sel_out))
+    return SALS_ERR_ALIGN;
+  if ((st = device_ready()) != SALS_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != SALS_OK) return st;
+  // no kernel of the decode path reads workspace bytes it has not written in the same call, so
+  // the array needs no clearing between calls
+  return decode_impl(s, sel, rope_base, q, Lk, Lv, Pk, Pv, ctx_cap, ctx, out, sel_out, ws,
+                     (size_t)SALS_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 sals_status sals_decode_step_traced(const sals_shape* s, const sals_select* sel, float rope_base,

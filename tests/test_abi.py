@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     L = lib()
     for n in names:
         assert hasattr(L, n), n
@@ -262,3 +262,25 @@ def test_header_is_plain_c_and_links(tmp_path):
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
                     str(src), "-L", lib_dir, "-lsals", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], check=True)
     assert subprocess.run([str(exe)]).returncode == 0
+
+
+def test_noalloc_decode_checks_before_any_hip_call():
+    """The no-allocation decode entry point rejects a workspace need above its fixed array, and
+    every argument error, before touching HIP."""
+    L = lib()
+    fn = L.sals_decode_step_noalloc
+    sel = SalsSelect(2048, 128, 8)
+    s = _shape(B=4, H_q=32, H_kv=8, d=128, r=256)
+    args = lambda s, sel, ctx, out=P: (ctypes.byref(s), ctypes.byref(sel), ctypes.c_float(10000.0), P, P, P, P,
+                                       P, 1 << 20, ctx, out, None, None)
+    assert fn(*args(s, sel, 32768, out=None)) == NULL
+    # a workspace above 16 MiB: 64 sequences of 128K-token score rows
+    big = _shape(B=64, H_q=32, H_kv=8, d=128, r=256)
+    st, need = _ws_bytes(big, sel, 131072)
+    assert st == OK and need > (16 << 20)
+    assert fn(*args(big, sel, 131072)) == WORKSPACE
+    assert fn(*args(_shape(d=96), sel, 1000)) == SHAPE
+    assert fn(*args(s, SalsSelect(-1, 4, 8), 1000)) == RANGE
+    bad = (ctypes.byref(s), ctypes.byref(sel), ctypes.c_float(10000.0), P + 4, P, P, P, P, 1 << 20, 1000, P,
+           None, None)
+    assert fn(*bad) == ALIGN
