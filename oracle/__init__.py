@@ -34,3 +34,4 @@ from .sals import (  # noqa: F401
     topk_lowest_index,
 )
 from .compact import compact_from_importance, dense_decode, importance, kv_compact, layer_budgets, sparsity  # noqa: F401
+from .outlier import dct_basis, deviation_energy, lowpass, outlier_compact, outlier_importance  # noqa: F401

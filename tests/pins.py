@@ -13,6 +13,7 @@ import scipy.special
 
 import brute
 import oracle.compact as OC
+import oracle.outlier as OO
 import oracle.sals as OS
 
 TOL = 1e-11
@@ -437,6 +438,84 @@ def pin_layer_budgets():
     assert list(OC.layer_budgets([0.0, 0.0, 0.0], 90, 1000)) == [30, 30, 30]
 
 
+# ---------------------------------------------------------------------------------------------
+# frequency-domain outlier importance
+# ---------------------------------------------------------------------------------------------
+
+def pin_dct_basis():
+    """The basis is the orthonormal DCT-II: C^T x equals scipy's dct(x, type 2, norm 'ortho'), and
+    C^T C = I; a hand value: T = 2 gives [[1, 1], [1, -1]] / sqrt(2)."""
+    import scipy.fft
+    for T in (5, 16, 33):
+        C = OO.dct_basis(T, T)
+        x = _rand(T, T, 3)
+        assert np.allclose(C.T @ x, scipy.fft.dct(x, type=2, norm="ortho", axis=0), atol=1e-12, rtol=0), T
+        assert np.allclose(C.T @ C, np.eye(T), atol=1e-12), T
+    assert np.allclose(OO.dct_basis(2, 2), np.array([[1.0, 1.0], [1.0, -1.0]]) / math.sqrt(2.0), atol=1e-15)
+
+
+def pin_outlier_closed_forms():
+    """Closed forms of the deviation energy: zero when every frequency is kept, zero for a
+    constant (DC) signal, zero for a mode below the cutoff and its full energy for one at or above
+    it; the total equals the energy of the dropped coefficients (Parseval); and the explicit
+    per-token loops of the definition on a tiny input."""
+    T, d = 24, 3
+    X = _rand(7, T, d)
+    assert np.abs(OO.deviation_energy(X, T)).max() < 1e-20
+    Xc = np.tile(_rand(8, 1, d), (T, 1))
+    assert np.abs(OO.deviation_energy(Xc, 1)).max() < 1e-20
+    t = np.arange(T)
+    for f0, F in ((3, 4), (3, 3), (10, 2)):
+        col = math.sqrt(2.0 / T) * np.cos(np.pi * (2 * t + 1) * f0 / (2 * T))
+        Xm = np.outer(col, [2.0, -1.0, 0.5])
+        got = OO.deviation_energy(Xm, F)
+        want = np.zeros(T) if f0 < F else (col ** 2) * (4.0 + 1.0 + 0.25)
+        assert np.allclose(got, want, atol=1e-12, rtol=0), (f0, F)
+    for F in (1, 5, 17):
+        import scipy.fft
+        coef = scipy.fft.dct(X, type=2, norm="ortho", axis=0)
+        assert abs(OO.deviation_energy(X, F).sum() - (coef[F:] ** 2).sum()) < 1e-10, F
+    # brute force: explicit loops with math.cos
+    T, F = 9, 3
+    Xs = _rand(9, T, 2)
+    ref = []
+    for tt in range(T):
+        e = 0.0
+        for c in range(2):
+            lp = 0.0
+            for f in range(F):
+                a = math.sqrt((1.0 if f == 0 else 2.0) / T)
+                coef = sum(a * math.cos(math.pi * (2 * u + 1) * f / (2 * T)) * Xs[u, c] for u in range(T))
+                lp += a * math.cos(math.pi * (2 * tt + 1) * f / (2 * T)) * coef
+            e += (Xs[tt, c] - lp) ** 2
+        ref.append(e)
+    assert np.allclose(OO.deviation_energy(Xs, F), ref, atol=1e-12, rtol=0)
+
+
+def pin_outlier_importance_pairs():
+    """The importance of a pair is the deviation energy of its key plus that of its value (a zero
+    value contributes nothing); the kept set is the top-k of it with lowest-index ties, and the
+    gathered rows are the stored rows."""
+    B, H, T, d, F = 2, 3, 40, 4, 6
+    rs = np.random.default_rng(3)
+    K = rs.standard_normal((B, H, T + 2, d))
+    V = rs.standard_normal((B, H, T + 2, d))
+    I = OO.outlier_importance(K, V, ctx=T, n_freq=F, dtype="f64")
+    for b in range(B):
+        for g in range(H):
+            want = OO.deviation_energy(K[b, g, :T], F) + OO.deviation_energy(V[b, g, :T], F)
+            assert np.allclose(I[b, g], want, atol=1e-12)
+    I0 = OO.outlier_importance(K, np.zeros_like(V), ctx=T, n_freq=F, dtype="f64")
+    assert np.allclose(I0[1, 2], OO.deviation_energy(K[1, 2, :T], F), atol=1e-12)
+    r = OO.outlier_compact(K, V, ctx=T, n_freq=F, k_keep=7, dtype="f64")
+    for b in range(B):
+        for g in range(H):
+            order = sorted(range(T), key=lambda t: (-I[b, g, t], t))[:7]
+            assert list(r["kept"][b, g]) == sorted(order)
+            assert np.array_equal(r["Kc"][b, g], K[b, g, r["kept"][b, g]])
+            assert np.array_equal(r["Vc"][b, g], V[b, g, r["kept"][b, g]])
+
+
 PINS = [
     pin_stored_decode,
     pin_rope_d2_closed_form,
@@ -457,4 +536,7 @@ PINS = [
     pin_compact_from_importance,
     pin_sparsity_bruteforce_and_closed_form,
     pin_layer_budgets,
+    pin_dct_basis,
+    pin_outlier_closed_forms,
+    pin_outlier_importance_pairs,
 ]

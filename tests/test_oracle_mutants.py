@@ -11,6 +11,7 @@ import types
 import pytest
 
 import oracle.compact as OC
+import oracle.outlier as OO
 import oracle.sals as OS
 from pins import PINS
 
@@ -18,6 +19,17 @@ ORACLE_DIR = os.path.dirname(OS.__file__)
 
 MUTANTS = [
     # (file, original snippet, mutated snippet, what the mistake is)
+    ("outlier.py", "a = np.where(f == 0, np.sqrt(1.0 / T), np.sqrt(2.0 / T))",
+     "a = np.sqrt(2.0 / T) + 0.0 * f", "DCT DC column not normalised"),
+    ("outlier.py", "np.cos(np.pi * (2.0 * t + 1.0) * f / (2.0 * T))", "np.cos(np.pi * (2.0 * t) * f / (2.0 * T))",
+     "DCT phase: 2t instead of 2t + 1"),
+    ("outlier.py", "C = dct_basis(X.shape[0], n_freq)", "C = dct_basis(X.shape[0], n_freq + 1)",
+     "low-pass keeps one frequency too many"),
+    ("outlier.py", "return (R * R).sum(axis=1)", "return np.abs(R).sum(axis=1)", "deviation measured as an L1 norm"),
+    ("outlier.py", "+ deviation_energy(stored_to_f64(V[b, g, :ctx], dtype), n_freq))",
+     "+ 0.0 * deviation_energy(stored_to_f64(V[b, g, :ctx], dtype), n_freq))", "value deviation dropped"),
+    ("outlier.py", "kept[b, g] = topk_lowest_index(I[b, g], k_keep)", "kept[b, g] = topk_lowest_index(-I[b, g], k_keep)",
+     "keeps the least deviating pairs"),
     ("sals.py", "return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16)",
      "return ((np.asarray(a, dtype=np.uint16) << 16).astype(np.uint32))", "bf16 bits shifted before widening"),
     ("sals.py", "return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16)",
@@ -109,7 +121,7 @@ def _patch(monkeypatch, mod, target):
 def test_some_pin_catches(mutant, monkeypatch):
     fname, old, new, what = mutant
     mod = _load(fname, old, new)
-    _patch(monkeypatch, mod, OS if fname == "sals.py" else OC)
+    _patch(monkeypatch, mod, {"sals.py": OS, "compact.py": OC, "outlier.py": OO}[fname])
     caught = []
     for pin in PINS:
         try:
@@ -121,7 +133,7 @@ def test_some_pin_catches(mutant, monkeypatch):
 
 def test_unmutated_copy_passes(monkeypatch):
     """Loading the sources through the same path without a change passes every pin."""
-    for fname, target in (("sals.py", OS), ("compact.py", OC)):
+    for fname, target in (("sals.py", OS), ("compact.py", OC), ("outlier.py", OO)):
         _patch(monkeypatch, _load(fname, "import numpy as np", "import numpy as np"), target)
     for pin in PINS:
         pin()
