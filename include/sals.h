@@ -275,6 +275,39 @@ sals_status kv_compact_from_importance(const kvc_shape* c, const void* K, const 
                                       sals_stream_t stream);
 
 /*
+ * kv_outlier_importance_workspace_bytes - workspace size of kv_outlier_importance.
+ */
+sals_status kv_outlier_importance_workspace_bytes(const kvc_shape* c, int32_t ctx, int32_t n_freq,
+                                                  size_t* bytes);
+
+/*
+ * kv_outlier_importance - frequency-domain outlier importance of a plain KV cache, computed from
+ * the keys and values alone, with no attention score (FlashCache page, summary and abstract: the
+ * energy of the KV matrices along the tokens sits at low frequencies, a low-pass filter extracts
+ * it, and the KV pairs that deviate most from it are the ones to keep):
+ *   for every sequence b and KV head g, with X = K[b, g, :ctx] or V[b, g, :ctx] ([ctx, d]) and
+ *   C[t, f] = a_f cos(pi (2t + 1) f / (2 ctx)) the orthonormal DCT-II basis along the tokens
+ *   (a_0 = sqrt(1/ctx), a_f = sqrt(2/ctx)), X_lp = C_F C_F^T X keeps the n_freq lowest
+ *   frequencies, and
+ *     importance[b, g, t] = ||K[t] - K_lp[t]||^2 + ||V[t] - V_lp[t]||^2      (fp32)
+ *   kv_compact_from_importance then keeps the k_keep most deviating pairs per (b, g).
+ * Args
+ *   c             shape; dtype must be SALS_BF16 (H_q unused).
+ *   K, V          [B, H_kv, ctx_cap, d] as stored, rows [0, ctx) read.
+ *   ctx_cap, ctx  1 <= ctx <= ctx_cap.
+ *   n_freq        kept frequencies, 1 <= n_freq <= min(64, ctx).
+ *   importance    [B, H_kv, ctx] fp32 written.
+ *   ws, ws_bytes  workspace of at least kv_outlier_importance_workspace_bytes(c, ctx, n_freq).
+ * Arithmetic: bf16 MFMA products with the fp32 basis values and coefficients split into high and
+ * low bf16 parts, fp32 sums; angles reduced exactly in integers before the fp32 cosine.
+ * Errors: NULL/ALIGN/SHAPE/RANGE/WORKSPACE as stated above, DTYPE unless bf16, HIP on launch
+ * failure.
+ */
+sals_status kv_outlier_importance(const kvc_shape* c, const void* K, const void* V, int32_t ctx_cap,
+                                  int32_t ctx, int32_t n_freq, float* importance, void* ws,
+                                  size_t ws_bytes, sals_stream_t stream);
+
+/*
  * sals_dense_decode_workspace_bytes - exact workspace size of sals_dense_decode for (c, n).
  */
 sals_status sals_dense_decode_workspace_bytes(const kvc_shape* c, int32_t n, size_t* bytes);

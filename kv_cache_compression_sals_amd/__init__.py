@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     kv_importance_sparsity,
     kv_importance_sparsity_workspace_bytes,
     kv_layer_budgets,
+    kv_outlier_importance,
+    kv_outlier_importance_workspace_bytes,
     kv_compact_workspace_bytes,
     n_selected,
     sals_decode_step,

@@ -415,3 +415,37 @@ def kv_layer_budgets(nonsparse, *, total: int, ctx: int):
     _check("kv_layer_budgets", lib().kv_layer_budgets(nu_addr, len(nu), int(total), ctx, out_addr))
     return list(out)
 
+
+# ---- frequency-domain outlier importance ------------------------------------------------------
+
+def kv_outlier_importance_workspace_bytes(K: torch.Tensor, *, ctx: int, n_freq: int) -> int:
+    B, H_kv, _, d = K.shape
+    c = KvcShape(B, H_kv, H_kv, d, _dtype(K))
+    n = ctypes.c_size_t(0)
+    _check("kv_outlier_importance_workspace_bytes",
+           lib().kv_outlier_importance_workspace_bytes(ctypes.byref(c), ctx, n_freq, ctypes.byref(n)))
+    return n.value
+
+
+def kv_outlier_importance(K: torch.Tensor, V: torch.Tensor, *, ctx: int, n_freq: int,
+                          importance: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """Deviation energy of each cached (key, value) pair from the low-pass of the cache along the
+    tokens (the n_freq lowest DCT-II frequencies). K, V [B, H_kv, ctx_cap, d] bf16.
+    Returns importance [B, H_kv, ctx] fp32, to rank pairs with kv_compact_from_importance."""
+    if K.dim() != 4:
+        raise ValueError("K, V must be [B, H_kv, ctx_cap, d]")
+    B, H_kv, ctx_cap, d = K.shape
+    _expect(V, "V", tuple(K.shape))
+    _expect(importance, "importance", (B, H_kv, ctx), torch.float32)
+    if not 1 <= ctx <= ctx_cap:
+        raise ValueError(f"ctx = {ctx} outside [1, ctx_cap = {ctx_cap}]")
+    c = KvcShape(B, H_kv, H_kv, d, _dtype(K, V))
+    if importance is None:
+        importance = torch.empty((B, H_kv, ctx), dtype=torch.float32, device=K.device)
+    if workspace is None:
+        workspace = _ws(kv_outlier_importance_workspace_bytes(K, ctx=ctx, n_freq=n_freq), K.device, None)
+    _check("kv_outlier_importance", lib().kv_outlier_importance(
+        ctypes.byref(c), _ptr(K), _ptr(V), ctx_cap, ctx, n_freq, _ptr(importance), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return importance

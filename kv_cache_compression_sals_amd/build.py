@@ -37,6 +37,7 @@ SOURCES = [
     "kernels/reconstruct.hip",
     "kernels/project.hip",
     "kernels/compact.hip",
+    "kernels/outlier.hip",
 ]
 
 

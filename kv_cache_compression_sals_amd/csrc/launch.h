@@ -125,6 +125,14 @@ hipError_t launch_gather_rows(int dtype, const void* K, const void* V, const int
                               void* Kc, void* Vc, int BG, int d, int ctx_cap, int k_keep,
                               hipStream_t st);
 
+// Frequency-domain outlier importance: I[b][g][t] = deviation energy of K and V row t from
+// their low-pass (the n_freq lowest orthonormal DCT-II frequencies along the tokens), bf16 cache.
+// n_freq in [1, 64]; the workspace holds the per-chunk coefficients.
+int outlier_freq_pad(int n_freq);
+size_t outlier_workspace_bytes(int BH, int d, int ctx, int n_freq);
+hipError_t launch_outlier_importance(const void* K, const void* V, void* ws, float* I, int BH, int d,
+                                     int ctx_cap, int ctx, int n_freq, hipStream_t st);
+
 // Flash-decode over a contiguous cache: partials per split, or out directly (n_splits == 1).
 // Query heads of one KV head that a dense-decode workgroup serves together: 4, 2 or 1.
 __host__ __device__ inline int dense_heads_per_group(int nqh) { return nqh % 4 == 0 ? 4 : nqh % 2 == 0 ? 2 : 1; }

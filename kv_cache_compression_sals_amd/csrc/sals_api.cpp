@@ -530,6 +530,45 @@ sals_status kv_compact_from_importance(const kvc_shape* c, const void* K, const 
   return e == hipSuccess ? SALS_OK : hip_fail(e);
 }
 
+namespace {
+
+sals_status check_outlier(const kvc_shape* c, int32_t ctx, int32_t n_freq) {
+  if (!c) return SALS_ERR_NULL;
+  sals_status st = check_kvc_shape(c);
+  if (st != SALS_OK) return st;
+  if (c->dtype != SALS_BF16) return SALS_ERR_DTYPE;
+  if (ctx < 1 || ctx > (1 << 26) || n_freq < 1 || n_freq > 64 || n_freq > ctx) return SALS_ERR_RANGE;
+  if ((long)c->B * c->H_kv * 2 * ((ctx + 4095) / 4096) > 0x7fffffffL) return SALS_ERR_RANGE;
+  return SALS_OK;
+}
+
+}  // namespace
+
+sals_status kv_outlier_importance_workspace_bytes(const kvc_shape* c, int32_t ctx, int32_t n_freq,
+                                                  size_t* bytes) {
+  if (!bytes) return SALS_ERR_NULL;
+  sals_status st = check_outlier(c, ctx, n_freq);
+  if (st != SALS_OK) return st;
+  *bytes = sals::outlier_workspace_bytes(c->B * c->H_kv, c->d, ctx, n_freq);
+  return SALS_OK;
+}
+
+sals_status kv_outlier_importance(const kvc_shape* c, const void* K, const void* V, int32_t ctx_cap,
+                                  int32_t ctx, int32_t n_freq, float* importance, void* ws,
+                                  size_t ws_bytes, sals_stream_t stream) {
+  if (!c || !K || !V || !importance) return SALS_ERR_NULL;
+  sals_status st = check_outlier(c, ctx, n_freq);
+  if (st != SALS_OK) return st;
+  if (ctx > ctx_cap) return SALS_ERR_RANGE;
+  if (misaligned(K) || misaligned(V) || misaligned(importance) || misaligned(ws)) return SALS_ERR_ALIGN;
+  if (!ws || ws_bytes < sals::outlier_workspace_bytes(c->B * c->H_kv, c->d, ctx, n_freq))
+    return SALS_ERR_WORKSPACE;
+  if ((st = device_ready()) != SALS_OK) return st;
+  hipError_t e = sals::launch_outlier_importance(K, V, ws, importance, c->B * c->H_kv, c->d, ctx_cap, ctx,
+                                                 n_freq, (hipStream_t)stream);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
 sals_status sals_dense_decode_workspace_bytes(const kvc_shape* c, int32_t n, size_t* bytes) {
   if (!bytes) return SALS_ERR_NULL;
   DensePlan p;
