@@ -35,3 +35,4 @@ from .sals import (  # noqa: F401
 )
 from .compact import compact_from_importance, dense_decode, importance, kv_compact, layer_budgets, sparsity  # noqa: F401
 from .outlier import dct_basis, deviation_energy, lowpass, outlier_compact, outlier_importance  # noqa: F401
+from .quant import dequantize_rows, mixed_decode, mixed_quantize, mixed_rows, quantize_group, quantize_rows  # noqa: F401

@@ -14,6 +14,7 @@ import scipy.special
 import brute
 import oracle.compact as OC
 import oracle.outlier as OO
+import oracle.quant as OQ
 import oracle.sals as OS
 
 TOL = 1e-11
@@ -516,6 +517,98 @@ def pin_outlier_importance_pairs():
             assert np.array_equal(r["Vc"][b, g], V[b, g, r["kept"][b, g]])
 
 
+# ---------------------------------------------------------------------------------------------
+# mixed-precision cache
+# ---------------------------------------------------------------------------------------------
+
+def pin_quant_group():
+    """Groups whose values sit exactly on the grid decode exactly (4 bits: zero point 0.5, step
+    1/16; 8 bits: zero point -1, step 1/128); a constant group, or one whose span is below 2^-96,
+    has code 0, scale 0 and its minimum as zero point; and for random groups every code is in
+    [0, 2^bits - 1] and within 1/2 step (plus fp32 rounding) of its value."""
+    q4 = np.array([0, 15, 3, 7, 8, 1, 14, 2] * 4)
+    x4 = (0.5 + q4 / 16.0).astype(np.float32)
+    c, sc, z = OQ.quantize_group(x4, 4)
+    assert list(c) == list(q4) and sc == np.float32(1 / 16) and z == np.float32(0.5)
+    q8 = np.array([0, 255, 128, 127, 1, 254, 64, 200] * 4)
+    x8 = (-1.0 + q8 / 128.0).astype(np.float32)
+    c, sc, z = OQ.quantize_group(x8, 8)
+    assert list(c) == list(q8) and sc == np.float32(1 / 128) and z == np.float32(-1.0)
+    assert np.array_equal(OQ.dequantize_rows(c[None], np.array([[[sc, z]]])), x8[None].astype(np.float64))
+    c, sc, z = OQ.quantize_group(np.full(32, 0.75, dtype=np.float32), 8)
+    assert not c.any() and sc == 0.0 and z == np.float32(0.75)
+    tiny = np.zeros(32, dtype=np.float32)
+    tiny[5] = np.float32(2.0 ** -110)
+    c, sc, z = OQ.quantize_group(tiny, 4)
+    assert not c.any() and sc == 0.0 and z == 0.0
+    rs = np.random.default_rng(21)
+    for bits in (4, 8):
+        for _ in range(200):
+            x = (rs.standard_normal(32) * rs.uniform(0.01, 30)).astype(np.float32)
+            c, sc, z = OQ.quantize_group(x, bits)
+            assert c.min() >= 0 and c.max() <= (1 << bits) - 1
+            assert c[np.argmin(x)] == 0 and c[np.argmax(x)] == (1 << bits) - 1
+            xh = float(z) + c * float(sc)
+            step = (float(x.max()) - float(x.min())) / ((1 << bits) - 1)
+            assert np.all(np.abs(xh - x) <= 0.5 * step * (1 + 1e-5) + 2.0 ** -21 * np.abs(x).max()), bits
+
+
+def pin_quant_layout_and_split():
+    """Nibble packing puts the even channel in the low nibble (hand example, round trip); the
+    important set is the top n_hi by (-importance, position), the rest is its complement, both
+    ascending; rows are quantized at 8 and 4 bits in their own sets."""
+    assert OQ.pack_nibbles(np.array([[1, 2, 3, 4]])).tolist() == [[0x21, 0x43]]
+    c = np.random.default_rng(2).integers(0, 16, size=(5, 64))
+    assert np.array_equal(OQ.unpack_nibbles(OQ.pack_nibbles(c)), c)
+    imp = np.array([0.3, 2.0, -1.0, 2.0, 0.0, -0.0, 5.0, 0.3, 1.0])
+    hi, lo = OQ.split_positions(imp, 9, 4)
+    assert list(hi) == [1, 3, 6, 8] and list(lo) == [0, 2, 4, 5, 7]
+    B, H, T, d = 1, 2, 40, 64
+    rs = np.random.default_rng(4)
+    K = rs.standard_normal((B, H, T, d))
+    V = rs.standard_normal((B, H, T, d))
+    I = rs.standard_normal((B, H, T))
+    m = OQ.mixed_quantize(K, V, I, ctx=T, n_hi=7, dtype="f64")
+    for g in range(H):
+        order = sorted(range(T), key=lambda t: (-I[0, g, t], t))
+        assert list(m["pos_hi"][0, g]) == sorted(order[:7]) and list(m["pos_lo"][0, g]) == sorted(order[7:])
+        rows_hi = K[0, g, m["pos_hi"][0, g]].astype(np.float32)
+        c8, p8 = OQ.quantize_rows(rows_hi, 8)
+        assert np.array_equal(m["codes_hi"][0, 0, g], c8) and np.array_equal(m["params_hi"][0, 0, g], p8)
+        rows_lo = V[0, g, m["pos_lo"][0, g]].astype(np.float32)
+        c4, p4 = OQ.quantize_rows(rows_lo, 4)
+        assert np.array_equal(OQ.unpack_nibbles(m["codes_lo"][1, 0, g]), c4)
+        assert np.array_equal(m["params_lo"][1, 0, g], p4)
+
+
+def pin_mixed_decode():
+    """On grid-exact data (every 32-channel group spans -1 .. 127/128 in steps of 1/128) with every
+    position at 8 bits, the decode equals plain attention over the original cache; in general it
+    equals plain attention over the dequantized rows put back at their positions."""
+    B, H_q, H_kv, T, d = 1, 4, 2, 30, 64
+    rs = np.random.default_rng(6)
+    qv = rs.integers(0, 256, size=(2, B, H_kv, T, d))
+    qv[..., 0] = 0
+    qv[..., 32] = 255
+    qv[..., 1] = 255
+    qv[..., 33] = 0
+    K, V = -1.0 + qv[0] / 128.0, -1.0 + qv[1] / 128.0
+    q = rs.standard_normal((B, H_q, d))
+    I = rs.standard_normal((B, H_kv, T))
+    m = OQ.mixed_quantize(K, V, I, ctx=T, n_hi=T, dtype="f64")
+    ref = OC.dense_decode(q, K, V, n=T, H_kv=H_kv, dtype="f64")
+    assert np.allclose(OQ.mixed_decode(q, m, H_kv=H_kv, dtype="f64"), ref, atol=1e-13, rtol=0)
+    K, V = rs.standard_normal((B, H_kv, T, d)), rs.standard_normal((B, H_kv, T, d))
+    for n_hi in (0, 11, T):
+        m = OQ.mixed_quantize(K, V, I, ctx=T, n_hi=n_hi, dtype="f64")
+        Kh, Vh = np.zeros_like(K), np.zeros_like(V)
+        for g in range(H_kv):
+            pos = np.concatenate([m["pos_hi"][0, g], m["pos_lo"][0, g]])
+            Kh[0, g, pos], Vh[0, g, pos] = OQ.mixed_rows(m, 0, 0, g), OQ.mixed_rows(m, 1, 0, g)
+        ref = OC.dense_decode(q, Kh, Vh, n=T, H_kv=H_kv, dtype="f64")
+        assert np.allclose(OQ.mixed_decode(q, m, H_kv=H_kv, dtype="f64"), ref, atol=1e-12, rtol=0), n_hi
+
+
 PINS = [
     pin_stored_decode,
     pin_rope_d2_closed_form,
@@ -539,4 +632,7 @@ PINS = [
     pin_dct_basis,
     pin_outlier_closed_forms,
     pin_outlier_importance_pairs,
+    pin_quant_group,
+    pin_quant_layout_and_split,
+    pin_mixed_decode,
 ]

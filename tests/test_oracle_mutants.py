@@ -12,6 +12,7 @@ import pytest
 
 import oracle.compact as OC
 import oracle.outlier as OO
+import oracle.quant as OQ
 import oracle.sals as OS
 from pins import PINS
 
@@ -19,6 +20,17 @@ ORACLE_DIR = os.path.dirname(OS.__file__)
 
 MUTANTS = [
     # (file, original snippet, mutated snippet, what the mistake is)
+    ("quant.py", "codes = np.floor((u + np.float32(0.5)).astype(np.float32)).astype(np.int64)",
+     "codes = np.floor(u).astype(np.int64)", "codes truncated instead of rounded"),
+    ("quant.py", "levels = np.float32((1 << bits) - 1)", "levels = np.float32(1 << bits)", "2^bits levels"),
+    ("quant.py", "return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)",
+     "return (c[:, 1::2] | (c[:, 0::2] << 4)).astype(np.uint8)", "nibbles swapped"),
+    ("quant.py", "hi = topk_lowest_index(np.asarray(imp_row[:ctx], dtype=np.float64), n_hi)",
+     "hi = topk_lowest_index(-np.asarray(imp_row[:ctx], dtype=np.float64), n_hi)", "least important tokens at 8 bits"),
+    ("quant.py", "return zero + codes * scale", "return codes * scale", "dequantization drops the zero point"),
+    ("quant.py", "HI_BITS, LO_BITS = 8, 4", "HI_BITS, LO_BITS = 4, 8", "bit widths swapped"),
+    ("quant.py", "scale = np.float32(span / levels)", "scale = np.float32(span / (levels + 1))", "step off by one level"),
+    ("quant.py", "out[:, 1::2] = b >> 4", "out[:, 1::2] = b & 0xF", "high nibble lost"),
     ("outlier.py", "a = np.where(f == 0, np.sqrt(1.0 / T), np.sqrt(2.0 / T))",
      "a = np.sqrt(2.0 / T) + 0.0 * f", "DCT DC column not normalised"),
     ("outlier.py", "np.cos(np.pi * (2.0 * t + 1.0) * f / (2.0 * T))", "np.cos(np.pi * (2.0 * t) * f / (2.0 * T))",
@@ -121,7 +133,7 @@ def _patch(monkeypatch, mod, target):
 def test_some_pin_catches(mutant, monkeypatch):
     fname, old, new, what = mutant
     mod = _load(fname, old, new)
-    _patch(monkeypatch, mod, {"sals.py": OS, "compact.py": OC, "outlier.py": OO}[fname])
+    _patch(monkeypatch, mod, {"sals.py": OS, "compact.py": OC, "outlier.py": OO, "quant.py": OQ}[fname])
     caught = []
     for pin in PINS:
         try:
@@ -133,7 +145,7 @@ def test_some_pin_catches(mutant, monkeypatch):
 
 def test_unmutated_copy_passes(monkeypatch):
     """Loading the sources through the same path without a change passes every pin."""
-    for fname, target in (("sals.py", OS), ("compact.py", OC), ("outlier.py", OO)):
+    for fname, target in (("sals.py", OS), ("compact.py", OC), ("outlier.py", OO), ("quant.py", OQ)):
         _patch(monkeypatch, _load(fname, "import numpy as np", "import numpy as np"), target)
     for pin in PINS:
         pin()
