@@ -308,6 +308,61 @@ sals_status kv_outlier_importance(const kvc_shape* c, const void* K, const void*
                                   size_t ws_bytes, sals_stream_t stream);
 
 /*
+ * kv_quantize_mixed - importance-based mixed-precision storage of a plain KV cache (ZipVL
+ * abstract: high-bit quantization for the caches of important tokens, low-bit quantization for
+ * the less important ones, to relieve the memory traffic of decoding).
+ *   For every sequence b and KV head g: pos_hi = the n_hi largest importance[b, g, :ctx] (ties to
+ *   the lowest index), ascending; pos_lo = the other positions of [0, ctx), ascending. The K and V
+ *   rows of pos_hi are stored at 8 bits, those of pos_lo at 4 bits, per token and per group of 32
+ *   channels, asymmetric and uniform: with mn, mx the group's extremes, levels = 2^bits - 1 and
+ *   fp32 steps each rounded to nearest, span = mx - mn, inv = levels / span, scale = span / levels,
+ *   code = clamp(floor((x - mn) * inv + 0.5), 0, levels); a group with span < 2^-96 stores code 0,
+ *   scale 0, zero point mn. A value is read back as mn + code * scale.
+ * Args
+ *   c             shape; dtype must be SALS_BF16 (H_q unused); d in {64, 128}.
+ *   K, V          [B, H_kv, ctx_cap, d] as stored, rows [0, ctx) read.
+ *   importance    [B, H_kv, ctx] fp32, finite (e.g. from kv_compact or kv_outlier_importance).
+ *   ctx_cap, ctx  1 <= ctx <= ctx_cap;  0 <= n_hi <= ctx;  n_lo = ctx - n_hi.
+ *   codes_hi      [2, B, H_kv, n_hi, d] uint8 written (index 0 keys, 1 values).
+ *   params_hi     [2, B, H_kv, n_hi, d / 32, 2] fp32 written: (scale, zero point) per group.
+ *   pos_hi        [B, H_kv, n_hi] int32 written.
+ *   codes_lo      [2, B, H_kv, n_lo, d / 2] uint8 written: two codes per byte, channel 2j in the
+ *                 low nibble of byte j of its row.
+ *   params_lo     [2, B, H_kv, n_lo, d / 32, 2] fp32 written.    pos_lo [B, H_kv, n_lo] written.
+ *   The *_hi pointers may be NULL when n_hi = 0, the *_lo ones when n_lo = 0.
+ * No workspace. Errors: NULL/ALIGN/SHAPE/RANGE as stated above, DTYPE unless bf16, HIP on launch
+ * failure.
+ */
+sals_status kv_quantize_mixed(const kvc_shape* c, const void* K, const void* V, const float* importance,
+                              int32_t ctx_cap, int32_t ctx, int32_t n_hi, uint8_t* codes_hi,
+                              float* params_hi, int32_t* pos_hi, uint8_t* codes_lo, float* params_lo,
+                              int32_t* pos_lo, sals_stream_t stream);
+
+/*
+ * sals_dense_decode_mixed_workspace_bytes - workspace size of sals_dense_decode_mixed.
+ */
+sals_status sals_dense_decode_mixed_workspace_bytes(const kvc_shape* c, int32_t n_hi, int32_t n_lo,
+                                                    size_t* bytes);
+
+/*
+ * sals_dense_decode_mixed - one decode step of plain attention over a mixed-precision cache from
+ * kv_quantize_mixed (every token of both sets; the rows were rotated before quantization, so the
+ * positions play no further part):
+ *   out[b, h] = softmax(q[b, h] . K_hat^T / sqrt(d)) . V_hat,  K_hat, V_hat = the dequantized rows
+ *   (mn + code * scale, one fp32 fused multiply-add per value) of KV head h * H_kv / H_q.
+ * Args
+ *   c             shape; dtype SALS_BF16 (the query's type).
+ *   q             [B, H_q, d] bf16, RoPE already applied.
+ *   codes_*, params_*, n_hi, n_lo   the two sets as kv_quantize_mixed wrote them; n_hi + n_lo >= 1.
+ *   out           [B, H_q, d] fp32 written.
+ *   ws, ws_bytes  workspace of at least sals_dense_decode_mixed_workspace_bytes(c, n_hi, n_lo).
+ */
+sals_status sals_dense_decode_mixed(const kvc_shape* c, const void* q, const uint8_t* codes_hi,
+                                    const float* params_hi, int32_t n_hi, const uint8_t* codes_lo,
+                                    const float* params_lo, int32_t n_lo, float* out, void* ws,
+                                    size_t ws_bytes, sals_stream_t stream);
+
+/*
  * sals_dense_decode_workspace_bytes - exact workspace size of sals_dense_decode for (c, n).
  */
 sals_status sals_dense_decode_workspace_bytes(const kvc_shape* c, int32_t n, size_t* bytes);

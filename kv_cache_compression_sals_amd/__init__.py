@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     kv_layer_budgets,
     kv_outlier_importance,
     kv_outlier_importance_workspace_bytes,
+    kv_quantize_mixed,
     kv_compact_workspace_bytes,
     n_selected,
     sals_decode_step,
@@ -21,6 +22,8 @@ from .binding import (  # noqa: F401
     sals_decode_step_traced,
     sals_decode_workspace_bytes,
     sals_dense_decode,
+    sals_dense_decode_mixed,
+    sals_dense_decode_mixed_workspace_bytes,
     sals_dense_decode_workspace_bytes,
     sals_project_kv,
     sals_reconstruct_kv,

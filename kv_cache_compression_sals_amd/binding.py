@@ -449,3 +449,75 @@ def kv_outlier_importance(K: torch.Tensor, V: torch.Tensor, *, ctx: int, n_freq:
         ctypes.byref(c), _ptr(K), _ptr(V), ctx_cap, ctx, n_freq, _ptr(importance), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return importance
+
+
+# ---- importance-based mixed-precision cache ---------------------------------------------------
+
+def kv_quantize_mixed(K: torch.Tensor, V: torch.Tensor, importance: torch.Tensor, *, n_hi: int,
+                      ctx: Optional[int] = None, out: Optional[dict] = None, stream=None) -> dict:
+    """Stores the n_hi most important rows per (sequence, KV head) at 8 bits and the rest at 4 bits.
+    K, V [B, H_kv, ctx_cap, d] bf16; importance [B, H_kv, ctx] fp32. Returns a dict with codes_hi
+    [2, B, H_kv, n_hi, d] uint8, params_hi [2, B, H_kv, n_hi, d/32, 2] fp32, pos_hi [B, H_kv, n_hi]
+    int32, codes_lo [2, B, H_kv, n_lo, d/2] uint8, params_lo, pos_lo (n_lo = ctx - n_hi)."""
+    if K.dim() != 4 or importance.dim() != 3:
+        raise ValueError("K, V must be [B, H_kv, ctx_cap, d] and importance [B, H_kv, ctx]")
+    B, H_kv, cap, d = K.shape
+    ctx = importance.shape[2] if ctx is None else ctx
+    _expect(V, "V", tuple(K.shape))
+    _expect(importance, "importance", (B, H_kv, ctx), torch.float32)
+    if not 1 <= ctx <= cap or not 0 <= n_hi <= ctx:
+        raise ValueError(f"need 1 <= ctx <= ctx_cap and 0 <= n_hi <= ctx (ctx {ctx}, cap {cap}, n_hi {n_hi})")
+    n_lo = ctx - n_hi
+    dev = K.device
+    shapes = dict(codes_hi=((2, B, H_kv, n_hi, d), torch.uint8), params_hi=((2, B, H_kv, n_hi, d // 32, 2), torch.float32),
+                  pos_hi=((B, H_kv, n_hi), torch.int32), codes_lo=((2, B, H_kv, n_lo, d // 2), torch.uint8),
+                  params_lo=((2, B, H_kv, n_lo, d // 32, 2), torch.float32), pos_lo=((B, H_kv, n_lo), torch.int32))
+    out = {} if out is None else out
+    for name, (shape, dt) in shapes.items():
+        if name in out:
+            _expect(out[name], name, shape, dt)
+        else:
+            out[name] = torch.empty(shape, dtype=dt, device=dev)
+    ptr = lambda name, n: _ptr(out[name]) if n > 0 else None  # noqa: E731
+    c = KvcShape(B, H_kv, H_kv, d, _dtype(K, V))
+    _check("kv_quantize_mixed", lib().kv_quantize_mixed(
+        ctypes.byref(c), _ptr(K), _ptr(V), _ptr(importance), cap, ctx, n_hi, ptr("codes_hi", n_hi),
+        ptr("params_hi", n_hi), ptr("pos_hi", n_hi), ptr("codes_lo", n_lo), ptr("params_lo", n_lo),
+        ptr("pos_lo", n_lo), _stream(stream)))
+    return out
+
+
+def sals_dense_decode_mixed_workspace_bytes(q: torch.Tensor, H_kv: int, *, n_hi: int, n_lo: int) -> int:
+    B, H_q, d = q.shape
+    c = KvcShape(B, H_q, H_kv, d, _dtype(q))
+    nb = ctypes.c_size_t(0)
+    _check("sals_dense_decode_mixed_workspace_bytes",
+           lib().sals_dense_decode_mixed_workspace_bytes(ctypes.byref(c), n_hi, n_lo, ctypes.byref(nb)))
+    return nb.value
+
+
+def sals_dense_decode_mixed(q: torch.Tensor, cache: dict, *, out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Attention of q [B, H_q, d] (bf16, RoPE applied) over a kv_quantize_mixed cache."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H_q, d]")
+    B, H_q, d = q.shape
+    _, Bc, H_kv, n_hi, dc = cache["codes_hi"].shape
+    n_lo = cache["codes_lo"].shape[3]
+    if Bc != B or dc != d:
+        raise ValueError("cache and query disagree on B or d")
+    _expect(cache["params_hi"], "params_hi", (2, B, H_kv, n_hi, d // 32, 2), torch.float32)
+    _expect(cache["codes_lo"], "codes_lo", (2, B, H_kv, n_lo, d // 2), torch.uint8)
+    _expect(cache["params_lo"], "params_lo", (2, B, H_kv, n_lo, d // 32, 2), torch.float32)
+    _expect(out, "out", (B, H_q, d), torch.float32)
+    c = KvcShape(B, H_q, H_kv, d, _dtype(q))
+    if out is None:
+        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _ws(sals_dense_decode_mixed_workspace_bytes(q, H_kv, n_hi=n_hi, n_lo=n_lo), q.device, None)
+    p = lambda name, n: _ptr(cache[name]) if n > 0 else None  # noqa: E731
+    _check("sals_dense_decode_mixed", lib().sals_dense_decode_mixed(
+        ctypes.byref(c), _ptr(q), p("codes_hi", n_hi), p("params_hi", n_hi), n_hi, p("codes_lo", n_lo),
+        p("params_lo", n_lo), n_lo, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out

@@ -38,6 +38,7 @@ SOURCES = [
     "kernels/project.hip",
     "kernels/compact.hip",
     "kernels/outlier.hip",
+    "kernels/quant.hip",
 ]
 
 

@@ -133,6 +133,16 @@ size_t outlier_workspace_bytes(int BH, int d, int ctx, int n_freq);
 hipError_t launch_outlier_importance(const void* K, const void* V, void* ws, float* I, int BH, int d,
                                      int ctx_cap, int ctx, int n_freq, hipStream_t st);
 
+// Mixed-precision cache: rows of K and V quantized per group of 32 channels, at 8 bits for the
+// positions listed in pos_hi (sorted, n_hi per pair) and at 4 bits for the rest (their positions
+// written to pos_lo); bf16 input. Decode: flash-decode over both sets, partials for the combine.
+hipError_t launch_mixed_quant(const void* K, const void* V, const int32_t* pos_hi, uint8_t* codes_hi,
+                              float* params_hi, uint8_t* codes_lo, float* params_lo, int32_t* pos_lo, int BH, int d,
+                              int ctx_cap, int ctx, int n_hi, hipStream_t st);
+hipError_t launch_mixed_decode(const void* q, const uint8_t* codes_hi, const float* params_hi, const uint8_t* codes_lo,
+                               const float* params_lo, float* out, float* part, int B, int H_q, int H_kv, int d,
+                               int n_hi, int n_lo, int split_len, int n_splits, hipStream_t st);
+
 // Flash-decode over a contiguous cache: partials per split, or out directly (n_splits == 1).
 // Query heads of one KV head that a dense-decode workgroup serves together: 4, 2 or 1.
 __host__ __device__ inline int dense_heads_per_group(int nqh) { return nqh % 4 == 0 ? 4 : nqh % 2 == 0 ? 2 : 1; }

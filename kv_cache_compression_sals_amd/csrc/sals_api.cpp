@@ -569,6 +569,69 @@ sals_status kv_outlier_importance(const kvc_shape* c, const void* K, const void*
   return e == hipSuccess ? SALS_OK : hip_fail(e);
 }
 
+sals_status kv_quantize_mixed(const kvc_shape* c, const void* K, const void* V, const float* importance,
+                              int32_t ctx_cap, int32_t ctx, int32_t n_hi, uint8_t* codes_hi,
+                              float* params_hi, int32_t* pos_hi, uint8_t* codes_lo, float* params_lo,
+                              int32_t* pos_lo, sals_stream_t stream) {
+  if (!c || !K || !V || !importance) return SALS_ERR_NULL;
+  sals_status st = check_kvc_shape(c);
+  if (st != SALS_OK) return st;
+  if (c->dtype != SALS_BF16) return SALS_ERR_DTYPE;
+  if (ctx < 1 || ctx > (1 << 26) || ctx > ctx_cap || n_hi < 0 || n_hi > ctx) return SALS_ERR_RANGE;
+  const int n_lo = ctx - n_hi;
+  if (n_hi > 0 && (!codes_hi || !params_hi || !pos_hi)) return SALS_ERR_NULL;
+  if (n_lo > 0 && (!codes_lo || !params_lo || !pos_lo)) return SALS_ERR_NULL;
+  if (misaligned(K) || misaligned(V) || misaligned(importance) || misaligned(codes_hi) ||
+      misaligned(params_hi) || misaligned(pos_hi) || misaligned(codes_lo) || misaligned(params_lo) ||
+      misaligned(pos_lo))
+    return SALS_ERR_ALIGN;
+  if ((st = device_ready()) != SALS_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  const int BH = c->B * c->H_kv;
+  hipError_t e = hipSuccess;
+  if (n_hi > 0)
+    e = sals::launch_topk_window(importance, ctx, pos_hi, BH, ctx, n_hi, ctx, n_hi, nullptr, hs);
+  if (e == hipSuccess)
+    e = sals::launch_mixed_quant(K, V, pos_hi, codes_hi, params_hi, codes_lo, params_lo, pos_lo, BH, c->d,
+                                 ctx_cap, ctx, n_hi, hs);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
+sals_status sals_dense_decode_mixed_workspace_bytes(const kvc_shape* c, int32_t n_hi, int32_t n_lo,
+                                                    size_t* bytes) {
+  if (!bytes) return SALS_ERR_NULL;
+  if (n_hi < 0 || n_lo < 0 || (long)n_hi + n_lo > (1 << 26)) return SALS_ERR_RANGE;
+  DensePlan p;
+  sals_status st = make_dense_plan(c, n_hi + n_lo, &p);
+  if (st != SALS_OK) return st;
+  *bytes = p.total;
+  return SALS_OK;
+}
+
+sals_status sals_dense_decode_mixed(const kvc_shape* c, const void* q, const uint8_t* codes_hi,
+                                    const float* params_hi, int32_t n_hi, const uint8_t* codes_lo,
+                                    const float* params_lo, int32_t n_lo, float* out, void* ws,
+                                    size_t ws_bytes, sals_stream_t stream) {
+  if (!c || !q || !out) return SALS_ERR_NULL;
+  if (n_hi < 0 || n_lo < 0 || (long)n_hi + n_lo > (1 << 26)) return SALS_ERR_RANGE;
+  if ((n_hi > 0 && (!codes_hi || !params_hi)) || (n_lo > 0 && (!codes_lo || !params_lo))) return SALS_ERR_NULL;
+  DensePlan p;
+  sals_status st = make_dense_plan(c, n_hi + n_lo, &p);
+  if (st != SALS_OK) return st;
+  if (c->dtype != SALS_BF16) return SALS_ERR_DTYPE;
+  if (misaligned(q) || misaligned(codes_hi) || misaligned(params_hi) || misaligned(codes_lo) ||
+      misaligned(params_lo) || misaligned(out) || misaligned(ws))
+    return SALS_ERR_ALIGN;
+  if (p.total > 0 && (!ws || ws_bytes < p.total)) return SALS_ERR_WORKSPACE;
+  if ((st = device_ready()) != SALS_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  float* part = (float*)ws;
+  hipError_t e = sals::launch_mixed_decode(q, codes_hi, params_hi, codes_lo, params_lo, out, part, c->B, c->H_q,
+                                           c->H_kv, c->d, n_hi, n_lo, p.split_len, p.n_splits, hs);
+  if (e == hipSuccess && p.n_splits > 1) e = sals::launch_combine(part, out, c->B * c->H_q, c->d, p.n_splits, hs);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
 sals_status sals_dense_decode_workspace_bytes(const kvc_shape* c, int32_t n, size_t* bytes) {
   if (!bytes) return SALS_ERR_NULL;
   DensePlan p;
