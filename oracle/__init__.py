@@ -21,6 +21,7 @@ No function here is "parity unpinned".
 from .sals import (  # noqa: F401
     attend_selected,
     decode_step,
+    decode_step_threshold,
     group_of,
     kv_head_of,
     latent_query,
@@ -30,6 +31,7 @@ from .sals import (  # noqa: F401
     rope,
     rope_theta,
     select_tokens,
+    select_tokens_threshold,
     stored_to_f64,
     topk_lowest_index,
 )

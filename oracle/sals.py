@@ -124,6 +124,19 @@ def select_tokens(S_row: np.ndarray, T: int, k: int, w: int) -> np.ndarray:
     return np.concatenate([top, np.arange(T_c, T)]).astype(np.int64)
 
 
+def select_tokens_threshold(S_row: np.ndarray, T: int, k: int, w: int, tau: float) -> np.ndarray:
+    """Threshold selection (SALS, 关键设计 item 4 names threshold selection beside top-k): the
+    candidates of [0, T_c) whose score is at least tau, at most k of them (the k largest by the
+    top-k rule when more pass), plus the window [T_c, T). Ascending, int64; its length varies per
+    row. Reading: tau is an absolute bound on the raw latent score, the same score top-k ranks;
+    k is the capacity of the selection."""
+    T_c = max(0, T - w)
+    S = np.asarray(S_row[:T_c], dtype=np.float64)
+    c = int(np.count_nonzero(S >= tau))
+    top = topk_lowest_index(S, min(k, c))
+    return np.concatenate([top, np.arange(T_c, T)]).astype(np.int64)
+
+
 # ----------------------------------------------------------------------------------------------
 # stage 3: rebuild the selected rows, then RoPE at their true positions
 # ----------------------------------------------------------------------------------------------
@@ -221,6 +234,30 @@ def decode_step(q, Lk, Lv, Pk, Pv, *, ctx: int, k: int, w: int, G: int, H_kv: in
         sel[b] = np.stack(sets)
         out[b], _ = attend_selected(qf[b], Lkb, Lvb, Pkf, Pvf, sets, T, base, H_kv, G)
     return dict(out=out, sel=sel, S=S, T_c=T_c, n_sel=n_sel)
+
+
+def decode_step_threshold(q, Lk, Lv, Pk, Pv, *, ctx: int, k: int, w: int, G: int, H_kv: int, base: float,
+                          tau: float, dtype: str, batches: Optional[list] = None) -> Dict[str, object]:
+    """decode_step with the threshold selection: per group the candidates scoring at least tau
+    (at most k), plus the window. Returns ``out`` [B, H_q, d], ``sel`` (a list per sequence of G
+    index arrays of varying length; None for sequences not computed), ``n_sel`` [B, G] and ``S``."""
+    qf = stored_to_f64(q, dtype)
+    Pkf, Pvf = stored_to_f64(Pk, dtype), stored_to_f64(Pv, dtype)
+    B, H_q, d = qf.shape
+    T = int(ctx)
+    T_c = max(0, T - w)
+    out = np.full((B, H_q, d), np.nan)
+    sel = [None] * B
+    n_sel = np.full((B, G), -1, dtype=np.int64)
+    S = np.full((B, G, T_c), np.nan)
+    for b in (range(B) if batches is None else batches):
+        Lkb = stored_to_f64(Lk[b, :T], dtype)
+        Lvb = stored_to_f64(Lv[b, :T], dtype)
+        S[b] = latent_scores(latent_query(qf[b], Pkf, H_kv, G), Lkb, T_c)
+        sel[b] = [select_tokens_threshold(S[b, s], T, k, w, tau) for s in range(G)]
+        n_sel[b] = [len(x) for x in sel[b]]
+        out[b], _ = attend_selected(qf[b], Lkb, Lvb, Pkf, Pvf, sel[b], T, base, H_kv, G)
+    return dict(out=out, sel=sel, n_sel=n_sel, S=S, T_c=T_c)
 
 
 # ----------------------------------------------------------------------------------------------

@@ -609,6 +609,56 @@ def pin_mixed_decode():
         assert np.allclose(OQ.mixed_decode(q, m, H_kv=H_kv, dtype="f64"), ref, atol=1e-12, rtol=0), n_hi
 
 
+def pin_select_threshold():
+    """Threshold selection, hand-worked on candidates [0.5, 2.0, -1.0, 2.0, 0.3, 2.0, 1.5, 0.0],
+    T = 10, w = 2: tau 1.5, k 4 keeps every score >= 1.5 (1, 3, 5, 6); tau 1.6, k 2 caps three
+    passing 2.0 ties at the lowest two; a score equal to tau passes; tau above every score keeps
+    only the window; tau -inf is plain top-k; k = 0 keeps the window. Random rows: equal to a
+    filter-then-sort written with sorted()."""
+    S = np.array([0.5, 2.0, -1.0, 2.0, 0.3, 2.0, 1.5, 0.0, 9.0, 9.0])
+    f = OS.select_tokens_threshold
+    assert list(f(S, 10, 4, 2, 1.5)) == [1, 3, 5, 6, 8, 9]
+    assert list(f(S, 10, 2, 2, 1.6)) == [1, 3, 8, 9]
+    assert list(f(S, 10, 9, 2, 0.3)) == [0, 1, 3, 4, 5, 6, 8, 9]
+    assert list(f(S, 10, 4, 2, 3.0)) == [8, 9]
+    assert list(f(S, 10, 0, 2, -5.0)) == [8, 9]
+    assert list(f(np.array([0.0, -0.0, 1.0]), 3, 5, 0, -0.0)) == [0, 1, 2]
+    rs = np.random.default_rng(8)
+    for _ in range(100):
+        T = int(rs.integers(1, 60))
+        w = int(rs.integers(0, 5))
+        k = int(rs.integers(0, 40))
+        S = np.round(rs.standard_normal(T) * 3) / 2
+        tau = float(np.round(rs.standard_normal() * 3) / 2)
+        assert list(f(S, T, k, w, -np.inf)) == list(OS.select_tokens(S, T, k, w))
+        T_c = max(0, T - w)
+        passing = [t for t in range(T_c) if S[t] >= tau]
+        keep = sorted(sorted(passing, key=lambda t: (-S[t], t))[:k])
+        assert list(f(S, T, k, w, tau)) == keep + list(range(T_c, T)), (T, w, k, tau)
+
+
+def pin_decode_threshold():
+    """The threshold decode attends over its own ragged sets: equal to attend_selected over them,
+    and to the top-k decode when tau lies below every score."""
+    H_q, H_kv, G, d, r, T = 4, 2, 2, 8, 6, 40
+    rs = np.random.default_rng(14)
+    q = rs.standard_normal((H_q, d))
+    Lk, Lv = rs.standard_normal((T, r)), rs.standard_normal((T, r))
+    Pk, Pv = rs.standard_normal((H_kv * d, r)), rs.standard_normal((H_kv * d, r))
+    kw = dict(ctx=T, k=9, w=3, G=G, H_kv=H_kv, base=10000.0, dtype="f64")
+    th = OS.decode_step_threshold(q[None], Lk[None], Lv[None], Pk, Pv, tau=0.5, **kw)
+    S = th["S"][0]
+    for s in range(G):
+        want = OS.select_tokens_threshold(S[s], T, 9, 3, 0.5)
+        assert np.array_equal(th["sel"][0][s], want) and th["n_sel"][0, s] == len(want)
+    ref, _ = OS.attend_selected(q, Lk, Lv, Pk, Pv, th["sel"][0], T, 10000.0, H_kv, G)
+    assert np.allclose(th["out"][0], ref, atol=1e-12)
+    low = OS.decode_step_threshold(q[None], Lk[None], Lv[None], Pk, Pv, tau=-1e300, **kw)
+    top = OS.decode_step(q[None], Lk[None], Lv[None], Pk, Pv, **kw)
+    assert np.allclose(low["out"], top["out"], atol=1e-12)
+    assert all(np.array_equal(low["sel"][0][s], top["sel"][0, s]) for s in range(G))
+
+
 PINS = [
     pin_stored_decode,
     pin_rope_d2_closed_form,
@@ -635,4 +685,6 @@ PINS = [
     pin_quant_group,
     pin_quant_layout_and_split,
     pin_mixed_decode,
+    pin_select_threshold,
+    pin_decode_threshold,
 ]

@@ -20,6 +20,12 @@ ORACLE_DIR = os.path.dirname(OS.__file__)
 
 MUTANTS = [
     # (file, original snippet, mutated snippet, what the mistake is)
+    ("sals.py", "c = int(np.count_nonzero(S >= tau))", "c = int(np.count_nonzero(S > tau))",
+     "a score equal to the threshold fails it"),
+    ("sals.py", "top = topk_lowest_index(S, min(k, c))", "top = topk_lowest_index(S, c)", "threshold set not capped at k"),
+    ("sals.py", "S = np.asarray(S_row[:T_c], dtype=np.float64)\n    c = int(np.count_nonzero(S >= tau))",
+     "S = np.asarray(S_row[:T_c], dtype=np.float64)\n    c = int(np.count_nonzero(np.asarray(S_row[:T]) >= tau))",
+     "threshold count includes the window"),
     ("quant.py", "codes = np.floor((u + np.float32(0.5)).astype(np.float32)).astype(np.int64)",
      "codes = np.floor(u).astype(np.int64)", "codes truncated instead of rounded"),
     ("quant.py", "levels = np.float32((1 << bits) - 1)", "levels = np.float32(1 << bits)", "2^bits levels"),
