@@ -150,6 +150,28 @@ sals_status sals_decode_step(const sals_shape* s, const sals_select* sel, float 
                              int32_t* sel_out, void* ws, size_t ws_bytes, sals_stream_t stream);
 
 /*
+ * sals_decode_step_threshold - sals_decode_step with threshold selection instead of a fixed
+ * top-k (SALS 关键设计 item 4: top-k or threshold selection of the tokens):
+ *   per sequence b and group: the candidates t < T_c whose score S[t] (the raw latent score of
+ *   sals_decode_step) is at least tau, at most k of them (when more pass, the k largest with ties
+ *   to the lowest index), plus the window [T_c, ctx); ascending. The set's length n varies per
+ *   row; attention runs over exactly its n tokens.
+ * Args: as sals_decode_step (sel->k is the largest number of candidates a row may keep), plus
+ *   tau          the score threshold (finite); scores are compared in fp32.
+ *   sel_out      NULL, or [B, G, n_max] int32 with n_max = min(k, T_c) + (ctx - T_c): row b, g holds
+ *                its n positions, then -1 up to n_max.
+ *   n_sel_out    NULL, or [B, G] int32 written with each row's n.
+ *   ws, ws_bytes workspace of at least sals_decode_workspace_bytes(s, sel, ctx) bytes.
+ * Errors: as sals_decode_step; SALS_ERR_RANGE also when w < 1 (the window keeps every row
+ *   non-empty) or tau is not finite.
+ */
+sals_status sals_decode_step_threshold(const sals_shape* s, const sals_select* sel, float tau,
+                                       float rope_base, const void* q, const void* Lk, const void* Lv,
+                                       const void* Pk, const void* Pv, int32_t ctx_cap, int32_t ctx,
+                                       float* out, int32_t* sel_out, int32_t* n_sel_out, void* ws,
+                                       size_t ws_bytes, sals_stream_t stream);
+
+/*
  * sals_decode_step_noalloc - sals_decode_step for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. It takes no
  * workspace: the library keeps one SALS_NOALLOC_SCRATCH_BYTES array of device memory per GPU (a

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     n_selected,
     sals_decode_step,
     sals_decode_step_noalloc,
+    sals_decode_step_threshold,
     sals_decode_step_traced,
     sals_decode_workspace_bytes,
     sals_dense_decode,

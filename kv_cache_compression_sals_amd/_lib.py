@@ -46,6 +46,8 @@ PROTOTYPES = {
     "sals_decode_workspace_bytes": (_I, [ctypes.POINTER(SalsShape), ctypes.POINTER(SalsSelect), _I, _SP]),
     "sals_decode_step": (_I, [ctypes.POINTER(SalsShape), ctypes.POINTER(SalsSelect), ctypes.c_float,
                               _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _S, _P]),
+    "sals_decode_step_threshold": (_I, [ctypes.POINTER(SalsShape), ctypes.POINTER(SalsSelect), ctypes.c_float,
+                                        ctypes.c_float, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _S, _P]),
     "sals_decode_step_noalloc": (_I, [ctypes.POINTER(SalsShape), ctypes.POINTER(SalsSelect), ctypes.c_float,
                                       _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "sals_decode_step_traced": (_I, [ctypes.POINTER(SalsShape), ctypes.POINTER(SalsSelect), ctypes.c_float,

@@ -164,6 +164,37 @@ def sals_decode_step(q: torch.Tensor, Lk: torch.Tensor, Lv: torch.Tensor, Pk: to
     return out, sel_out
 
 
+def sals_decode_step_threshold(q: torch.Tensor, Lk: torch.Tensor, Lv: torch.Tensor, Pk: torch.Tensor,
+                               Pv: torch.Tensor, *, ctx: int, k: int, w: int, G: int, tau: float,
+                               rope_base: float = 10000.0, out: Optional[torch.Tensor] = None,
+                               sel_out: Optional[torch.Tensor] = None, n_sel_out: Optional[torch.Tensor] = None,
+                               want_sel: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
+    """One SALS decode step with threshold selection: per row the candidates scoring at least tau
+    (at most k), plus the window. Returns (out [B, H_q, d] fp32, sel [B, G, n_max] int32 padded
+    with -1 or None, n_sel [B, G] int32)."""
+    dt = _dtype(q, Lk, Lv, Pk, Pv)
+    _check_decode_args(q, Lk, Lv, Pk, Pv, ctx)
+    B, H_q, d = q.shape
+    s, sel = _decode_structs(q, Pk, Pk.shape[1], k, w, G, dt)
+    n_max = n_selected(ctx, k, w)
+    _expect(out, "out", (B, H_q, d), torch.float32)
+    _expect(sel_out, "sel_out", (B, G, n_max), torch.int32)
+    _expect(n_sel_out, "n_sel_out", (B, G), torch.int32)
+    if out is None:
+        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+    if sel_out is None and want_sel:
+        sel_out = torch.empty((B, G, n_max), dtype=torch.int32, device=q.device)
+    if n_sel_out is None:
+        n_sel_out = torch.empty((B, G), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = _ws(sals_decode_workspace_bytes(q, Pk, ctx=ctx, k=k, w=w, G=G), q.device, None)
+    _check("sals_decode_step_threshold", lib().sals_decode_step_threshold(
+        ctypes.byref(s), ctypes.byref(sel), ctypes.c_float(tau), ctypes.c_float(rope_base), _ptr(q), _ptr(Lk),
+        _ptr(Lv), _ptr(Pk), _ptr(Pv), Lk.shape[1], ctx, _ptr(out), _ptr(sel_out), _ptr(n_sel_out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, sel_out, n_sel_out
+
+
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
 

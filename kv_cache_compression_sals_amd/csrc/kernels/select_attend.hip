@@ -16,12 +16,12 @@ int select_attend_max_split(int dtype, int d, int r, int nqh) {
 }
 
 hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const void* Lv,
-                                const void* Pk, const void* Pv, const int32_t* sel, float* out,
-                                float* part, float* pbuf, float* pstat, int B, int H_q,
+                                const void* Pk, const void* Pv, const int32_t* sel, const int32_t* cnt,
+                                float* out, float* part, float* pbuf, float* pstat, int B, int H_q,
                                 int H_kv, int d, int r, int G, int ctx_cap, int ctx, int n_sel,
                                 int split_len, int n_splits, float rope_base, hipStream_t st,
                                 hipEvent_t t_start, hipEvent_t t_stop) {
-  const sa::SAArgs a{q,     Lk,   Lv, Pk,      Pv,  sel,   out,       part,     pbuf,     pstat,
+  const sa::SAArgs a{q,     Lk,   Lv, Pk,      Pv,  sel,   cnt,   out,       part,     pbuf,     pstat,
                      B,     H_q,  H_kv, G,     ctx_cap, ctx, n_sel, split_len, n_splits, rope_base,
                      t_start, t_stop};
   bool ok = false;

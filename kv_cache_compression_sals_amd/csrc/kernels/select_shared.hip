@@ -76,8 +76,9 @@ __device__ __forceinline__ void rope_sincos(int pos, double frev, float* s, floa
 template <int R, int NQH>
 __global__ __launch_bounds__(kNT) void shared_keys_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ Lk, const uint16_t* __restrict__ Pk,
-    const int32_t* __restrict__ sel, float* __restrict__ pbuf, float* __restrict__ pstat, int H_q,
-    int H_kv, int G, int ctx_cap, int ctx, int n_sel, int n_splits, float rope_base) {
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, float* __restrict__ pbuf,
+    float* __restrict__ pstat, int H_q, int H_kv, int G, int ctx_cap, int ctx, int n_sel, int n_splits,
+    float rope_base) {
   constexpr int NKC = R / kKC;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   int32_t* pos = (int32_t*)(smem + kOffPos);
@@ -93,7 +94,18 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
   const int s = (g0 * G) / H_kv;
   const int nqh = H_q / H_kv;
   const int j0 = sp * kTOK;
-  const int n_tok = min(kTOK, n_sel - j0);
+  // a thresholded (ragged) selection has its own count per row; a split past it holds no token
+  // and leaves neutral split statistics (m = -inf, l = 0)
+  const int n_row = cnt ? cnt[(size_t)b * G + s] : n_sel;
+  const int n_tok = min(kTOK, n_row - j0);
+  if (n_tok <= 0) {
+    if (tid < kNH * nqh) {
+      float* ps = pstat + (((size_t)b * H_q + (g0 + tid / nqh) * nqh + tid % nqh) * n_splits + sp) * 2;
+      ps[0] = -INFINITY;
+      ps[1] = 0.f;
+    }
+    return;
+  }
   const size_t brow = (size_t)b * ctx_cap;
 
   // ---- prologue: positions, RoPE frequencies, rotated and scaled queries ----
@@ -278,7 +290,7 @@ bool shared_keys_supported(int dtype, int H_q, int H_kv, int G, int d, int r) {
 int shared_keys_split() { return kTOK; }
 
 hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, const int32_t* sel,
-                              float* pbuf, float* pstat, int B, int H_q, int H_kv, int G, int r,
+                              const int32_t* cnt, float* pbuf, float* pstat, int B, int H_q, int H_kv, int G, int r,
                               int ctx_cap, int ctx, int n_sel, int n_splits, float rope_base,
                               hipStream_t st, hipEvent_t t_start, hipEvent_t t_stop) {
   const dim3 grid(n_splits * (H_kv / kNH) * B);
@@ -289,9 +301,9 @@ hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, con
 #define SALS_SK(RR, QQ)                                                                              \
   if (t_start)                                                                                       \
     hipExtLaunchKernelGGL(shared_keys_kernel<RR, QQ>, grid, dim3(kNT), 0, st, t_start, t_stop, 0, qq, lk, \
-                          pk, sel, pbuf, pstat, H_q, H_kv, G, ctx_cap, ctx, n_sel, n_splits, rope_base);  \
+                          pk, sel, cnt, pbuf, pstat, H_q, H_kv, G, ctx_cap, ctx, n_sel, n_splits, rope_base);  \
   else                                                                                               \
-    shared_keys_kernel<RR, QQ><<<grid, kNT, 0, st>>>(qq, lk, pk, sel, pbuf, pstat, H_q, H_kv, G,       \
+    shared_keys_kernel<RR, QQ><<<grid, kNT, 0, st>>>(qq, lk, pk, sel, cnt, pbuf, pstat, H_q, H_kv, G,       \
                                                      ctx_cap, ctx, n_sel, n_splits, rope_base)
 #define SALS_SK_R(RR) \
   if (nqh <= 1) {     \

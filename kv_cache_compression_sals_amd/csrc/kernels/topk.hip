@@ -18,6 +18,8 @@
 // the remaining digits and the ordered compaction run over the whole row instead (slower).
 // Every pass is branch-free over the keys and ranks come from ballots, so per-key work is a few
 // VALU operations: with one row per CU the passes are bound by issue rate, not memory.
+#include <string.h>
+
 #include <type_traits>
 
 #include "../common.h"
@@ -91,11 +93,17 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remainin
 // okeys[0 .. kp)), followed by the window out[kp + j] = wstart + j, j < wcount. Keys are
 // float_key(src[i]) with map(i) = obase + i, or (GATHER) the given keys ckeys[i] with
 // map(i) = cand[i]. GATHER requires IN_LDS.
+// Threshold mode (thr): only keys >= tkey may be selected, so kp becomes min(kp, #keys >= tkey)
+// (counted over the raw keys before anything else); out[kp + wcount .. pad_to) is filled with -1
+// and *cnt_out receives kp + wcount. For GATHER the count runs over the candidates: a row with
+// fewer than kp passing keys has all of them among the candidates, otherwise at least kp pass
+// there too, so min(kp, count) is the row's.
 template <bool IN_LDS, bool GATHER>
 __device__ __forceinline__ void topk_body(const float* __restrict__ src, const int32_t* __restrict__ cand,
                                           const uint32_t* __restrict__ ckeys, int n, int kp,
                                           int32_t* __restrict__ out, uint32_t* __restrict__ okeys,
-                                          int obase, int wcount, int wstart, bool vec) {
+                                          int obase, int wcount, int wstart, bool vec, bool thr,
+                                          uint32_t tkey, int32_t* __restrict__ cnt_out, int pad_to) {
   static_assert(IN_LDS || !GATHER, "candidate keys are staged in LDS");
   constexpr int LIST = TopkLds<IN_LDS>::LIST;
   __shared__ __attribute__((aligned(16))) uint32_t keys[IN_LDS ? kLdsKeys : 1];
@@ -111,6 +119,27 @@ __device__ __forceinline__ void topk_body(const float* __restrict__ src, const i
     else return obase + i;
   };
 
+  if (thr) {
+    if (kp > 0) {
+      uint32_t mine = 0;
+      for (int i = tid; i < Tc; i += kThreads) {
+        uint32_t k;
+        if constexpr (GATHER) k = ckeys[i];
+        else k = float_key(src[i]);
+        mine += k >= tkey ? 1u : 0u;
+      }
+      const uint32_t wsum = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(mine, lane), 63);
+      if (lane == 0) scan[wave] = wsum;
+      __syncthreads();
+      uint32_t total = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) total += scan[w];
+      __syncthreads();  // scan is reused below
+      kp = (int)min((uint32_t)kp, total);
+    }
+    for (int j = kp + wcount + tid; j < pad_to; j += kThreads) out[j] = -1;
+    if (tid == 0 && cnt_out) *cnt_out = kp + wcount;
+  }
   for (int j = tid; j < wcount; j += kThreads) out[kp + j] = wstart + j;
   if (kp <= 0) return;
   if (kp >= Tc) {
@@ -423,10 +452,11 @@ template <bool IN_LDS>
 __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __restrict__ S,
                                                                int32_t* __restrict__ sel, int Tc,
                                                                int ldS, int kp, int ctx, int n_sel,
-                                                               bool vec) {
+                                                               bool vec, bool thr, uint32_t tkey,
+                                                               int32_t* __restrict__ cnt) {
   const int row = blockIdx.x;
   topk_body<IN_LDS, false>(S + (size_t)row * ldS, nullptr, nullptr, Tc, kp, sel + (size_t)row * n_sel,
-                           nullptr, 0, ctx - Tc, Tc, vec);
+                           nullptr, 0, ctx - Tc, Tc, vec, thr, tkey, cnt ? cnt + row : nullptr, n_sel);
 }
 
 // Rows longer than the LDS staging array: one workgroup per (row, slice of slen keys) keeps the
@@ -443,17 +473,18 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __res
   const int s0 = s * slen, n = min(slen, Tc - s0);
   const size_t o = ((size_t)row * ns + s) * kp;
   topk_body<true, false>(S + (size_t)row * ldS + s0, nullptr, nullptr, n, kp, cand + o, ckeys + o, s0, 0, 0,
-                         vec);
+                         vec, false, 0u, nullptr, 0);
 }
 
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const int32_t* __restrict__ cand,
                                                               const uint32_t* __restrict__ ckeys,
                                                               int32_t* __restrict__ sel, int Tc, int kp,
-                                                              int ns, int ctx, int n_sel) {
+                                                              int ns, int ctx, int n_sel, bool thr,
+                                                              uint32_t tkey, int32_t* __restrict__ cnt) {
   const int row = blockIdx.x;
   const size_t o = (size_t)row * ns * kp;
   topk_body<true, true>(nullptr, cand + o, ckeys + o, ns * kp, kp, sel + (size_t)row * n_sel, nullptr, 0,
-                        ctx - Tc, Tc, false);
+                        ctx - Tc, Tc, false, thr, tkey, cnt ? cnt + row : nullptr, n_sel);
 }
 
 }  // namespace
@@ -473,20 +504,28 @@ size_t topk_candidate_bytes(int rows, int Tc, int kp) {
   return ns ? (size_t)rows * ns * kp * 8 : 0;  // positions, then keys
 }
 
+uint32_t threshold_key(float tau) {
+  uint32_t u;
+  const float z = tau == 0.0f ? 0.0f : tau;  // -0.0 ranks as +0.0
+  memcpy(&u, &z, 4);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, int Tc, int kp,
-                              int ctx, int n_sel, int32_t* cand, hipStream_t st) {
+                              int ctx, int n_sel, int32_t* cand, hipStream_t st, bool thr, uint32_t tkey,
+                              int32_t* cnt) {
   if (rows <= 0) return hipSuccess;
   const bool vec = (ldS & 3) == 0 && ((uintptr_t)S & 15) == 0;
   int slen = 0;
   const int ns = cand ? topk_slices(Tc, kp, &slen) : 0;
   if (Tc <= kLdsKeys) {
-    topk_window_kernel<true><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec);
+    topk_window_kernel<true><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt);
   } else if (ns > 0) {
     uint32_t* ckeys = (uint32_t*)(cand + (size_t)rows * ns * kp);
     topk_slice_kernel<<<rows * ns, kThreads, 0, st>>>(S, cand, ckeys, Tc, ldS, kp, slen, ns, vec);
-    topk_merge_kernel<<<rows, kThreads, 0, st>>>(cand, ckeys, sel, Tc, kp, ns, ctx, n_sel);
+    topk_merge_kernel<<<rows, kThreads, 0, st>>>(cand, ckeys, sel, Tc, kp, ns, ctx, n_sel, thr, tkey, cnt);
   } else {
-    topk_window_kernel<false><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec);
+    topk_window_kernel<false><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt);
   }
   return hipGetLastError();
 }

@@ -51,8 +51,9 @@ struct VSLayout {
 template <class T, int CB>
 __global__ __launch_bounds__(kThreads) void value_sum_kernel(
     const float* __restrict__ pbuf, const float* __restrict__ pstat, const int32_t* __restrict__ sel,
-    const typename T::elem* __restrict__ Lv, float* __restrict__ zpart, int B, int H_q, int G,
-    int r, int ctx_cap, int n_sel, int split_len, int n_splits, int nsub, int cl, int nch) {
+    const int32_t* __restrict__ cnt, const typename T::elem* __restrict__ Lv, float* __restrict__ zpart,
+    int B, int H_q, int G, int r, int ctx_cap, int n_sel, int split_len, int n_splits, int nsub, int cl,
+    int nch) {
   using elem = typename T::elem;
   using W = Win<T>;
   using LY = VSLayout<T>;
@@ -69,7 +70,8 @@ __global__ __launch_bounds__(kThreads) void value_sum_kernel(
   const int HS = H_q / G, hs16 = (HS + 15) / 16 * 16;
   const int sp = c / nsub, u = c % nsub;
   const int t0 = sp * split_len + u * cl;
-  const int t1 = min(sp * split_len + min((u + 1) * cl, split_len), n_sel);
+  // a ragged (thresholded) row ends at its own count: chunks past it sum nothing
+  const int t1 = min(sp * split_len + min((u + 1) * cl, split_len), cnt ? cnt[bs] : n_sel);
   const int nt = max(t1 - t0, 0);
   const int ntp = (nt + W::WLEN - 1) / W::WLEN * W::WLEN;  // whole MFMA windows
   const int ts = LY::ts(cl);
@@ -381,13 +383,13 @@ bool value_plan(int dtype, int B, int H_q, int H_kv, int G, int r, int n_sel, in
 }
 
 hipError_t launch_value_sum(int dtype, const ValuePlan& vp, const float* pbuf, const float* pstat,
-                            const int32_t* sel, const void* Lv, float* zpart, int B, int H_q, int G,
-                            int r, int ctx_cap, int n_sel, int split_len, int n_splits,
+                            const int32_t* sel, const int32_t* cnt, const void* Lv, float* zpart, int B,
+                            int H_q, int G, int r, int ctx_cap, int n_sel, int split_len, int n_splits,
                             hipStream_t st) {
   const dim3 grid((r / vp.cb) * vp.nch * B * G);
 #define SALS_VS(TT, CBV)                                                                      \
   value_sum_kernel<TT, CBV><<<grid, kThreads, vp.lds, st>>>(                                 \
-      pbuf, pstat, sel, (const TT::elem*)Lv, zpart, B, H_q, G, r, ctx_cap, n_sel,             \
+      pbuf, pstat, sel, cnt, (const TT::elem*)Lv, zpart, B, H_q, G, r, ctx_cap, n_sel,        \
       split_len, n_splits, vp.nsub, vp.cl, vp.nch)
   if (dtype == 0 && vp.cb == 64) SALS_VS(F32, 64);
   else if (dtype == 0) SALS_VS(F32, 32);

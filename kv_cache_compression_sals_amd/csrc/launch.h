@@ -32,20 +32,28 @@ hipError_t launch_latent_score(int dtype, const float* qpart, int npart, const v
 // candidates are split into topk_slices(...) slices whose candidates (positions, then their
 // keys: topk_candidate_bytes(...) bytes) go to `cand`; with cand null, or no valid split, one
 // workgroup per row reads the row from memory in every pass instead.
+// Threshold mode (thr): a row keeps only the candidates whose key is at least tkey
+// (float_key of the threshold), at most kp of them, so its top-k count is min(kp, #passing);
+// the window follows them, the rest of the row (up to n_sel) is filled with -1, and cnt[row]
+// receives the row's length (count + window).
 int topk_slices(int Tc, int kp, int* slen);
 size_t topk_candidate_bytes(int rows, int Tc, int kp);
 hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, int Tc, int kp,
-                              int ctx, int n_sel, int32_t* cand, hipStream_t st);
+                              int ctx, int n_sel, int32_t* cand, hipStream_t st, bool thr = false,
+                              uint32_t tkey = 0, int32_t* cnt = nullptr);
+uint32_t threshold_key(float tau);
 
 // Gather + rebuild + RoPE + attention over the selected rows, split along the selected set.
 // With n_splits == 1 the normalised result goes to out; otherwise (m, l, o) partials go to part.
+// cnt (null for a fixed n_sel) gives each selection row's own length for a ragged (thresholded)
+// selection padded to n_sel; the same holds for launch_shared_keys and launch_value_sum.
 // With pbuf non-null the kernel stops after the softmax and hands the probabilities to the
 // shared-selection value kernels below: pbuf[b][h][j] = exp(logit_j - m_split) (rows of
 // round_up(n_sel, 4) floats) and pstat[b][h][split] = (m, l).
 hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const void* Lv,
-                                const void* Pk, const void* Pv, const int32_t* sel, float* out,
-                                float* part, float* pbuf, float* pstat, int B, int H_q, int H_kv,
-                                int d, int r, int G, int ctx_cap, int ctx, int n_sel,
+                                const void* Pk, const void* Pv, const int32_t* sel, const int32_t* cnt,
+                                float* out, float* part, float* pbuf, float* pstat, int B, int H_q,
+                                int H_kv, int d, int r, int G, int ctx_cap, int ctx, int n_sel,
                                 int split_len, int n_splits, float rope_base, hipStream_t st,
                                 hipEvent_t t_start = nullptr, hipEvent_t t_stop = nullptr);
 
@@ -57,7 +65,7 @@ hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const 
 bool shared_keys_supported(int dtype, int H_q, int H_kv, int G, int d, int r);
 int shared_keys_split();
 hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, const int32_t* sel,
-                              float* pbuf, float* pstat, int B, int H_q, int H_kv, int G, int r,
+                              const int32_t* cnt, float* pbuf, float* pstat, int B, int H_q, int H_kv, int G, int r,
                               int ctx_cap, int ctx, int n_sel, int n_splits, float rope_base,
                               hipStream_t st, hipEvent_t t_start = nullptr, hipEvent_t t_stop = nullptr);
 
@@ -89,8 +97,8 @@ struct ValuePlan {
 bool value_plan(int dtype, int B, int H_q, int H_kv, int G, int r, int n_sel, int split_len,
                 int n_splits, ValuePlan* vp);
 hipError_t launch_value_sum(int dtype, const ValuePlan& vp, const float* pbuf, const float* pstat,
-                            const int32_t* sel, const void* Lv, float* zpart, int B, int H_q, int G,
-                            int r, int ctx_cap, int n_sel, int split_len, int n_splits,
+                            const int32_t* sel, const int32_t* cnt, const void* Lv, float* zpart, int B,
+                            int H_q, int G, int r, int ctx_cap, int n_sel, int split_len, int n_splits,
                             hipStream_t st);
 hipError_t launch_value_product(int dtype, const ValuePlan& vp, const float* zpart, const void* Pv,
                                 float* out, int B, int H_q, int H_kv, int d, int r, hipStream_t st);

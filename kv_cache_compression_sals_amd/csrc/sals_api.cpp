@@ -65,7 +65,7 @@ struct DecodePlan {
   bool shared;  // value side by the shared-selection kernels (one selection per >= 4 KV heads)
   bool skeys;   // key side of a shared selection by the two-head tile kernel
   sals::ValuePlan vp;
-  size_t off_qpart, off_cand, off_S, off_sel, off_part, off_p, off_pstat, off_zp, total;
+  size_t off_qpart, off_cand, off_S, off_sel, off_cnt, off_part, off_p, off_pstat, off_zp, total;
 };
 
 sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_t ctx,
@@ -105,6 +105,8 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   off += align_up((size_t)s->B * sel->G * p->ldS * 4);
   p->off_sel = off;
   off += align_up((size_t)s->B * sel->G * p->n_sel * 4);
+  p->off_cnt = off;  // per-row lengths of a thresholded selection
+  off += align_up((size_t)s->B * sel->G * 4);
   p->skeys = s->H_kv / sel->G >= 4 &&
              sals::shared_keys_supported(s->dtype, s->H_q, s->H_kv, sel->G, s->d, s->r);
   if (p->skeys) {  // splits of the tile kernel's token count
@@ -192,17 +194,22 @@ sals_status make_dense_plan(const kvc_shape* c, int32_t n, DensePlan* p) {
 
 namespace {
 
+// Threshold selection (thr): a row keeps its candidates scoring at least tau, at most k of them,
+// plus the window; its length goes to cnt_out (or to the workspace) and the rows of sel are
+// padded with -1 to the largest length.
 sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_base, const void* q,
                         const void* Lk, const void* Lv, const void* Pk, const void* Pv,
                         int32_t ctx_cap, int32_t ctx, float* out, int32_t* sel_out, void* ws,
-                        size_t ws_bytes, sals_stream_t stream, void* const* events) {
+                        size_t ws_bytes, sals_stream_t stream, void* const* events, bool thr = false,
+                        float tau = 0.f, int32_t* cnt_out = nullptr) {
   if (!s || !sel || !q || !Lk || !Lv || !Pk || !Pv || !out) return SALS_ERR_NULL;
   DecodePlan p;
   sals_status st = make_decode_plan(s, sel, ctx, &p);
   if (st != SALS_OK) return st;
   if (ctx > ctx_cap || !(rope_base > 1.0f) || !isfinite(rope_base)) return SALS_ERR_RANGE;
+  if (thr && (sel->w < 1 || !isfinite(tau))) return SALS_ERR_RANGE;
   if (misaligned(q) || misaligned(Lk) || misaligned(Lv) || misaligned(Pk) || misaligned(Pv) ||
-      misaligned(out) || misaligned(sel_out) || misaligned(ws))
+      misaligned(out) || misaligned(sel_out) || misaligned(ws) || misaligned(cnt_out))
     return SALS_ERR_ALIGN;
   if (!ws || ws_bytes < p.total) return SALS_ERR_WORKSPACE;
   if ((st = device_ready()) != SALS_OK) return st;
@@ -215,12 +222,14 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   float* pbuf = p.shared ? (float*)(w + p.off_p) : nullptr;
   float* pstat = p.shared ? (float*)(w + p.off_pstat) : nullptr;
   float* zpart = (float*)(w + p.off_zp);
+  int32_t* cnt = thr ? (cnt_out ? cnt_out : (int32_t*)(w + p.off_cnt)) : nullptr;
   const int G = sel->G;
   hipError_t e = hipSuccess;
   auto mark = [&](int i) {
     if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], hs);
   };
-  const bool score = p.kp > 0 && p.kp < p.Tc;
+  // scores are needed to rank a top-k, and for a threshold to test every candidate
+  const bool score = p.kp > 0 && (thr || p.kp < p.Tc);
   mark(0);
   if (score && e == hipSuccess)
     e = sals::launch_latent_query(s->dtype, q, Pk, qpart, s->B, s->H_q, s->H_kv, s->d, s->r, G,
@@ -232,20 +241,21 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   mark(2);
   if (e == hipSuccess)
     e = sals::launch_topk_window(S, p.ldS, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel,
-                                 (int32_t*)(w + p.off_cand), hs);
+                                 (int32_t*)(w + p.off_cand), hs, thr, thr ? sals::threshold_key(tau) : 0u,
+                                 cnt);
   // the attention kernel's own start and end (recorded by the runtime around the kernel) bound
   // its stage, so that the traced time of the dominant kernel excludes the launch gap
   hipEvent_t k0 = events ? (hipEvent_t)events[3] : nullptr, k1 = events ? (hipEvent_t)events[4] : nullptr;
   if (e == hipSuccess && p.skeys)
-    e = sals::launch_shared_keys(q, Lk, Pk, selb, pbuf, pstat, s->B, s->H_q, s->H_kv, G, s->r,
+    e = sals::launch_shared_keys(q, Lk, Pk, selb, cnt, pbuf, pstat, s->B, s->H_q, s->H_kv, G, s->r,
                                  ctx_cap, ctx, p.n_sel, p.n_splits, rope_base, hs, k0, k1);
   else if (e == hipSuccess)
-    e = sals::launch_select_attend(s->dtype, q, Lk, Lv, Pk, Pv, selb, out, part, pbuf, pstat,
+    e = sals::launch_select_attend(s->dtype, q, Lk, Lv, Pk, Pv, selb, cnt, out, part, pbuf, pstat,
                                    s->B, s->H_q, s->H_kv, s->d, s->r, G, ctx_cap, ctx, p.n_sel,
                                    p.split_len, p.n_splits, rope_base, hs, k0, k1);
   if (p.shared) {
     if (e == hipSuccess)
-      e = sals::launch_value_sum(s->dtype, p.vp, pbuf, pstat, selb, Lv, zpart, s->B, s->H_q, G,
+      e = sals::launch_value_sum(s->dtype, p.vp, pbuf, pstat, selb, cnt, Lv, zpart, s->B, s->H_q, G,
                                  s->r, ctx_cap, p.n_sel, p.split_len, p.n_splits, hs);
     if (e == hipSuccess)
       e = sals::launch_value_product(s->dtype, p.vp, zpart, Pv, out, s->B, s->H_q, s->H_kv, s->d,
@@ -376,6 +386,15 @@ sals_status sals_decode_step(const sals_shape* s, const sals_select* sel, float 
                              int32_t* sel_out, void* ws, size_t ws_bytes, sals_stream_t stream) {
   return decode_impl(s, sel, rope_base, q, Lk, Lv, Pk, Pv, ctx_cap, ctx, out, sel_out, ws,
                      ws_bytes, stream, nullptr);
+}
+
+sals_status sals_decode_step_threshold(const sals_shape* s, const sals_select* sel, float tau,
+                                       float rope_base, const void* q, const void* Lk, const void* Lv,
+                                       const void* Pk, const void* Pv, int32_t ctx_cap, int32_t ctx,
+                                       float* out, int32_t* sel_out, int32_t* n_sel_out, void* ws,
+                                       size_t ws_bytes, sals_stream_t stream) {
+  return decode_impl(s, sel, rope_base, q, Lk, Lv, Pk, Pv, ctx_cap, ctx, out, sel_out, ws, ws_bytes,
+                     stream, nullptr, true, tau, n_sel_out);
 }
 
 sals_status sals_decode_step_noalloc(const sals_shape* s, const sals_select* sel, float rope_base,
