@@ -35,6 +35,9 @@ from .sals import (  # noqa: F401
     stored_to_f64,
     topk_lowest_index,
 )
-from .compact import compact_from_importance, dense_decode, importance, kv_compact, layer_budgets, sparsity  # noqa: F401
+from .compact import (  # noqa: F401
+    compact_from_importance, dense_decode, energy_budgets, importance, importance_budget, kv_compact, layer_budgets,
+    mass_budget, sparsity,
+)
 from .outlier import dct_basis, deviation_energy, lowpass, outlier_compact, outlier_importance  # noqa: F401
 from .quant import dequantize_rows, mixed_decode, mixed_quantize, mixed_rows, quantize_group, quantize_rows  # noqa: F401

@@ -149,3 +149,43 @@ def dense_decode(q, K, V, *, n: int, H_kv: int, dtype: str = "bf16", pairs=None)
         Vf = stored_to_f64(V[b, g, :n], dtype)
         out[b, h] = _softmax(Kf @ qf[b, h] / np.sqrt(d)) @ Vf
     return out
+
+
+def mass_budget(imp_row, mass: float):
+    """(n, total) for one importance row (values >= 0): total = sum of the row, n = the smallest
+    count whose n largest values sum to at least mass * total (at least 1). The ZipVL abstract
+    sets the ratio of important tokens from the distribution of the attention scores rather than
+    a fixed hyper-parameter; reading: the share of tokens that carries a fixed fraction of the
+    normalized importance mass."""
+    v = np.sort(np.asarray(imp_row, dtype=np.float64))[::-1]
+    total = float(v.sum())
+    target = mass * total
+    run = 0.0
+    n = 0
+    while n < len(v) and run < target:
+        run += v[n]
+        n += 1
+    return max(n, 1), total
+
+
+def importance_budget(importance, *, ctx: int, mass: float):
+    """Per (sequence, KV head) row of importance [B, H_kv, >= ctx]: n_keep [B, H_kv] and total
+    [B, H_kv] (mass_budget), the layer's ratio = sum(n_keep) / (rows * ctx) (ZipVL: one dynamic
+    ratio per layer) and the layer's energy = sum(total) (the FlashCache budget input)."""
+    B, H = importance.shape[0], importance.shape[1]
+    n = np.zeros((B, H), dtype=np.int64)
+    tot = np.zeros((B, H))
+    for b in range(B):
+        for g in range(H):
+            n[b, g], tot[b, g] = mass_budget(importance[b, g, :ctx], mass)
+    return dict(n_keep=n, total=tot, layer_ratio=n.sum() / (B * H * ctx), layer_energy=tot.sum())
+
+
+def energy_budgets(energies, total: int, ctx: int) -> np.ndarray:
+    """Per-layer cache sizes from the layers' outlier energies (FlashCache page: a dynamic budget
+    allocation decides each layer's KV cache size so that more outlier KVs are kept). Reading: a
+    layer's share of the total budget is proportional to its outlier energy, i.e. layer_budgets
+    with the ratios E_l / max E (the max cancels in the normaliser)."""
+    e = np.asarray(energies, dtype=np.float64)
+    top = e.max()
+    return layer_budgets(e / top if top > 0 else np.zeros_like(e), total, ctx)

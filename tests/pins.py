@@ -659,6 +659,37 @@ def pin_decode_threshold():
     assert all(np.array_equal(low["sel"][0][s], top["sel"][0, s]) for s in range(G))
 
 
+def pin_mass_budget():
+    """Hand-worked: [4, 3, 2, 1] holds 10; 70% needs 4 + 3 (n = 2), 71% needs three values; ties
+    [2, 2, 2, 2] at 50% need two; a row of zeros keeps one; order does not matter; random rows
+    against a cumulative sum of the sorted values."""
+    assert OC.mass_budget([1.0, 4.0, 2.0, 3.0], 0.7) == (2, 10.0)
+    assert OC.mass_budget([4.0, 3.0, 2.0, 1.0], 0.71)[0] == 3
+    assert OC.mass_budget([2.0, 2.0, 2.0, 2.0], 0.5)[0] == 2
+    assert OC.mass_budget([0.0, 0.0, 0.0], 0.9) == (1, 0.0)
+    assert OC.mass_budget([5.0, 0.0, 0.0], 1.0)[0] == 1
+    assert OC.mass_budget([1.0, 1.0, 1.0], 1.0)[0] == 3
+    rs = np.random.default_rng(10)
+    for _ in range(50):
+        v = rs.exponential(size=int(rs.integers(1, 200)))
+        m = float(rs.uniform(0.05, 1.0))
+        c = np.cumsum(np.sort(v)[::-1])
+        assert OC.mass_budget(v, m)[0] == int(np.argmax(c >= m * v.sum() - 1e-12)) + 1
+    I = rs.exponential(size=(2, 3, 50))
+    r = OC.importance_budget(I, ctx=40, mass=0.5)
+    assert r["n_keep"][1, 2] == OC.mass_budget(I[1, 2, :40], 0.5)[0]
+    assert abs(r["layer_ratio"] - r["n_keep"].sum() / (6 * 40)) < 1e-15
+    assert abs(r["layer_energy"] - I[:, :, :40].sum()) < 1e-9
+
+
+def pin_energy_budgets():
+    """Budgets follow the energies: equal energies split evenly, 1:4 splits 1:4, a zero-energy
+    layer gets the minimum of one token, the clamp to ctx holds."""
+    assert list(OC.energy_budgets([2.0, 2.0], 100, 1000)) == [50, 50]
+    assert list(OC.energy_budgets([1.0, 4.0], 500, 1000)) == [100, 400]
+    assert list(OC.energy_budgets([0.0, 5.0], 100, 60)) == [1, 60]
+
+
 PINS = [
     pin_stored_decode,
     pin_rope_d2_closed_form,
@@ -687,4 +718,6 @@ PINS = [
     pin_mixed_decode,
     pin_select_threshold,
     pin_decode_threshold,
+    pin_mass_budget,
+    pin_energy_budgets,
 ]

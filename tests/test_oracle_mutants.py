@@ -20,6 +20,12 @@ ORACLE_DIR = os.path.dirname(OS.__file__)
 
 MUTANTS = [
     # (file, original snippet, mutated snippet, what the mistake is)
+    ("compact.py", "    while n < len(v) and run < target:", "    while n < len(v) and run <= target:",
+     "mass budget takes one token past the target"),
+    ("compact.py", "v = np.sort(np.asarray(imp_row, dtype=np.float64))[::-1]", "v = np.asarray(imp_row, dtype=np.float64)",
+     "mass budget in position order instead of by size"),
+    ("compact.py", "return layer_budgets(e / top if top > 0 else np.zeros_like(e), total, ctx)",
+     "return layer_budgets(1.0 - e / top if top > 0 else np.zeros_like(e), total, ctx)", "budget falls with energy"),
     ("sals.py", "c = int(np.count_nonzero(S >= tau))", "c = int(np.count_nonzero(S > tau))",
      "a score equal to the threshold fails it"),
     ("sals.py", "top = topk_lowest_index(S, min(k, c))", "top = topk_lowest_index(S, c)", "threshold set not capped at k"),
