@@ -277,6 +277,29 @@ sals_status kv_layer_budgets(const float* nonsparse, int32_t L, int64_t total, i
                              int32_t* budgets);
 
 /*
+ * kv_importance_budget - dynamic budgets from an importance distribution.
+ *   For every sequence b and KV head g (a row of importance[b, g, :ctx], values >= 0; negative
+ *   values count as 0):
+ *     total[b, g]  = sum of the row                                               (fp64 sum, fp32)
+ *     n_keep[b, g] = the smallest n >= 1 whose n largest values sum to at least mass * total
+ *   and for the layer (nullable single floats):
+ *     layer_ratio  = sum of n_keep / (B H_kv ctx)   (ZipVL abstract: the ratio of important tokens
+ *                    follows the layer's attention distribution instead of a fixed value; use
+ *                    ceil(layer_ratio * ctx) as the layer's k_keep or n_hi)
+ *     layer_energy = sum of total                  (FlashCache abstract: a dynamic budget decides
+ *                    each layer's cache size; with the outlier importance of
+ *                    kv_outlier_importance, kv_layer_budgets over E_l / max E gives budgets in
+ *                    proportion to the layers' outlier energies)
+ * Args: c (B, H_kv used); importance [B, H_kv, ctx] fp32; 0 < mass <= 1; n_keep [B, H_kv] int32
+ *   and total [B, H_kv] fp32 written; layer_ratio, layer_energy: NULL or one device float each.
+ * Sums are fp64 in a fixed order, so results are deterministic.
+ * Errors: NULL/ALIGN/SHAPE/RANGE as stated above, HIP on launch failure.
+ */
+sals_status kv_importance_budget(const kvc_shape* c, const float* importance, int32_t ctx, float mass,
+                                 int32_t* n_keep, float* total, float* layer_ratio, float* layer_energy,
+                                 sals_stream_t stream);
+
+/*
  * kv_compact_from_importance - the selection and gather of kv_compact from an importance the
  * caller supplies (PureKV abstract: attention measured on a lower layer estimates the importance
  * of the tokens of higher layers, so those layers need no attention scores of their own).

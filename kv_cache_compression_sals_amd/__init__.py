@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     SalsError,
     kv_compact,
     kv_compact_from_importance,
+    kv_importance_budget,
     kv_importance_sparsity,
     kv_importance_sparsity_workspace_bytes,
     kv_layer_budgets,

@@ -552,3 +552,28 @@ def sals_dense_decode_mixed(q: torch.Tensor, cache: dict, *, out: Optional[torch
         p("params_lo", n_lo), n_lo, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return out
+
+
+# ---- dynamic budgets from an importance distribution --------------------------------------------
+
+def kv_importance_budget(importance: torch.Tensor, *, mass: float, ctx: Optional[int] = None, stream=None):
+    """Per (sequence, KV head) row of importance [B, H_kv, ctx] (fp32, >= 0): the smallest number of
+    tokens holding `mass` of the row's importance, and the row total; plus the layer's ratio
+    (mean count / ctx) and energy (summed importance), computed on the device.
+    Returns (n_keep [B, H_kv] int32, total [B, H_kv] fp32, layer_ratio [1] fp32, layer_energy [1] fp32)."""
+    if importance.dim() != 3 or importance.dtype != torch.float32:
+        raise ValueError("importance must be a float32 [B, H_kv, ctx] tensor")
+    B, H_kv, n = importance.shape
+    ctx = n if ctx is None else ctx
+    if ctx != n:
+        importance = importance[:, :, :ctx].contiguous()
+    dev = importance.device
+    n_keep = torch.empty((B, H_kv), dtype=torch.int32, device=dev)
+    total = torch.empty((B, H_kv), dtype=torch.float32, device=dev)
+    ratio = torch.empty((4,), dtype=torch.float32, device=dev)
+    energy = torch.empty((4,), dtype=torch.float32, device=dev)
+    c = KvcShape(B, H_kv, H_kv, 128, 1)
+    _check("kv_importance_budget", lib().kv_importance_budget(
+        ctypes.byref(c), _ptr(importance), ctx, ctypes.c_float(mass), _ptr(n_keep), _ptr(total), _ptr(ratio),
+        _ptr(energy), _stream(stream)))
+    return n_keep, total, ratio[:1], energy[:1]

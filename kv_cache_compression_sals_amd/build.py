@@ -39,6 +39,7 @@ SOURCES = [
     "kernels/compact.hip",
     "kernels/outlier.hip",
     "kernels/quant.hip",
+    "kernels/budget.hip",
 ]
 
 

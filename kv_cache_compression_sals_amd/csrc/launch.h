@@ -151,6 +151,12 @@ hipError_t launch_mixed_decode(const void* q, const uint8_t* codes_hi, const flo
                                const float* params_lo, float* out, float* part, int B, int H_q, int H_kv, int d,
                                int n_hi, int n_lo, int split_len, int n_splits, hipStream_t st);
 
+// Importance-mass budgets per row of a non-negative importance [rows, ctx]: n_keep = the smallest
+// count of the largest values holding `mass` of the row total, total = the row total; ratio and
+// energy (nullable) = sum(n_keep) / (rows * ctx) and sum(total).
+hipError_t launch_mass_budget(const float* imp, int rows, int ctx, float mass, int32_t* n_keep, float* total,
+                              float* ratio, float* energy, hipStream_t st);
+
 // Flash-decode over a contiguous cache: partials per split, or out directly (n_splits == 1).
 // Query heads of one KV head that a dense-decode workgroup serves together: 4, 2 or 1.
 __host__ __device__ inline int dense_heads_per_group(int nqh) { return nqh % 4 == 0 ? 4 : nqh % 2 == 0 ? 2 : 1; }

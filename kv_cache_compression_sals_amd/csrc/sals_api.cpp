@@ -509,6 +509,20 @@ sals_status kv_importance_sparsity(const kvc_shape* c, const void* K, const void
   return e == hipSuccess ? SALS_OK : hip_fail(e);
 }
 
+sals_status kv_importance_budget(const kvc_shape* c, const float* importance, int32_t ctx, float mass,
+                                 int32_t* n_keep, float* total, float* layer_ratio, float* layer_energy,
+                                 sals_stream_t stream) {
+  if (!c || !importance || !n_keep || !total) return SALS_ERR_NULL;
+  sals_status st = check_kvc_shape(c);
+  if (st != SALS_OK) return st;
+  if (ctx < 1 || ctx > (1 << 26) || !(mass > 0.f && mass <= 1.f)) return SALS_ERR_RANGE;
+  if (misaligned(importance) || misaligned(n_keep) || misaligned(total)) return SALS_ERR_ALIGN;
+  if ((st = device_ready()) != SALS_OK) return st;
+  hipError_t e = sals::launch_mass_budget(importance, c->B * c->H_kv, ctx, mass, n_keep, total, layer_ratio,
+                                          layer_energy, (hipStream_t)stream);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
 sals_status kv_layer_budgets(const float* nonsparse, int32_t L, int64_t total, int32_t ctx,
                              int32_t* budgets) {
   if (!nonsparse || !budgets) return SALS_ERR_NULL;
