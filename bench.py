@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of one SALS decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only c2,c3]
-                    [--calib-copy-mib M]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--replays R] [--no-cpu-baseline]
+                    [--no-hbm-probe] [--only c1,c2,c3,c4,c5] [--calib-copy-mib M]
 
 A step is one call of the decode path on one attention layer: latent query, latent scoring of
 every cached token, top-k + window selection, gather + rebuild + RoPE + attention over the
@@ -28,11 +28,19 @@ goes to stderr.
 --calib-copy-mib M first copies an M MiB buffer with torch (a plain copy kernel of known size),
 so that a counter run can scale FETCH_SIZE / WRITE_SIZE to bytes.
 
---only may also name c4 (post-prefill compaction of the 16K-context VLM-shaped cache, then the
-dense decode over the compact cache) and c5 (one decode step through 32 independent layers of
-the 128K-context GQA workload, all resident). They are reported as extra objects of the JSON
-line (timed as K back-to-back calls between HIP events, resp. one replay of K captured 32-layer
-steps); the default run leaves them out because their inputs take a minute to generate.
+The default run also measures, as extra objects of the same JSON line (--only picks a subset):
+  c1  the tiny fp32 layer (ctx 512): latency only;
+  c4  post-prefill compaction of the 16K-context VLM-shaped cache (kv_compact and its stages, the
+      dense decode over the compact cache, reuse of the importance, sparsity, the frequency-domain
+      outlier importance, the mixed-precision cache and its decode, the importance budgets), each
+      timed as K back-to-back calls between HIP events (K at most 10);
+  c5  one decode step through 32 independent resident layers of the 128K-context GQA workload
+      (one replay of K captured 32-layer steps), with per-stage times from a traced pass.
+Before the workloads, an in-tree streaming read (sals_hbm_read) measures the HBM read bandwidth
+that hbm_frac_measured is stated against. Each decode workload also reports the median, p10 and
+p90 of the per-step time over --replays further replays, a warm variant (every step on the same
+input copy), the scoring + attention HBM fraction, and threshold selection on the same layer.
+The cpu_baseline object adds the CPU model and one-thread oracle times.
 """
 
 from __future__ import annotations
@@ -149,7 +157,7 @@ def algorithmic(cfg, ctx):
     )
 
 
-def run_workload(cfg, steps, warmup, label):
+def run_workload(cfg, steps, warmup, label, replays=10, comparators=True):
     import numpy as np
     import torch
 
@@ -200,6 +208,17 @@ def run_workload(cfg, steps, warmup, label):
     graph.replay()
     torch.cuda.synchronize()
     us_step = (time.perf_counter() - t_start) / steps * 1e6
+    # spread: further timed replays of the same graph (cold: rotated inputs), and a warm graph
+    # whose steps all reuse one input copy (resident in the Infinity Cache when it fits)
+    rep = replay_stats(graph, steps, replays)
+    warm_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(warm_graph):
+        for _ in range(steps):
+            step(0)
+    warm_graph.replay()
+    torch.cuda.synchronize()
+    warm = replay_stats(warm_graph, steps, replays)
+    del warm_graph
 
     # ---- per-kernel durations: the same K steps, eagerly, with HIP events on the launch stream ----
     # The C entry point is called with argument lists marshalled beforehand, so the host issues
@@ -227,9 +246,72 @@ def run_workload(cfg, steps, warmup, label):
     event_step_us = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(steps)) / steps * 1e3
     del graph, copies
     torch.cuda.empty_cache()
-    comp = run_comparators(cfg, base, ctx, steps, warmup) if cfg.dtype == "bf16" else None
+    comp = run_comparators(cfg, base, ctx, steps, warmup) if cfg.dtype == "bf16" and comparators else None
+    thr = run_threshold(cfg, base, ctx, steps, warmup) if cfg.dtype == "bf16" and comparators else None
     return dict(case=case, us=us_step, stage_us=stage_us, event_step_us=event_step_us, eager_us=eager_us,
-                comparators=comp)
+                comparators=comp, replays=rep, warm=warm, threshold=thr)
+
+
+def replay_stats(graph, steps, replays):
+    """Median, p10 and p90 of the per-step time over `replays` timed replays of a captured graph
+    of `steps` steps (each replay between two device synchronisations)."""
+    import numpy as np
+    import torch
+
+    per = []
+    for _ in range(replays):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        per.append((time.perf_counter() - t0) / steps * 1e6)
+    return dict(median=round(float(np.median(per)), 2), p10=round(float(np.percentile(per, 10)), 2),
+                p90=round(float(np.percentile(per, 90)), 2), replays=replays)
+
+
+def run_threshold(cfg, base, ctx, steps, warmup):
+    """sals_decode_step_threshold on the same layer, with tau set (by bisection on the kernels' own
+    per-row counts) so that the rows keep about half of the top-k capacity on average; timed as
+    `steps` back-to-back calls between two HIP events."""
+    import torch
+
+    import kv_cache_compression_sals_amd as sals
+
+    q, Lk, Lv, Pk, Pv = (base[n] for n in ("q", "Lk", "Lv", "Pk", "Pv"))
+    kw = dict(ctx=ctx, k=cfg.k, w=cfg.w, G=cfg.G, rope_base=cfg.base)
+    wc = min(cfg.w, ctx)
+    out = torch.empty((cfg.B, cfg.H_q, cfg.d), dtype=torch.float32, device="cuda")
+    cnt = torch.empty((cfg.B, cfg.G), dtype=torch.int32, device="cuda")
+    ws = torch.empty(sals.sals_decode_workspace_bytes(q, Pk, ctx=ctx, k=cfg.k, w=cfg.w, G=cfg.G), dtype=torch.uint8,
+                     device="cuda")
+
+    def mean_kept(tau):
+        sals.sals_decode_step_threshold(q, Lk, Lv, Pk, Pv, tau=tau, out=out, n_sel_out=cnt, workspace=ws, **kw)
+        return float((cnt.float() - wc).mean().item())
+
+    lo, hi = -1e4, 1e4
+    for _ in range(40):
+        mid = (lo + hi) / 2
+        if mean_kept(mid) > cfg.k / 2:
+            lo = mid
+        else:
+            hi = mid
+    tau = (lo + hi) / 2
+    kept = mean_kept(tau)
+    call = lambda: sals.sals_decode_step_threshold(q, Lk, Lv, Pk, Pv, tau=tau, out=out, n_sel_out=cnt,  # noqa: E731
+                                                   workspace=ws, **kw)
+    for _ in range(warmup):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return dict(us_per_step=round(e0.elapsed_time(e1) / steps * 1e3, 2), tau=round(tau, 4),
+                mean_kept_candidates=round(kept, 1), capacity=cfg.k,
+                note="threshold selection, eager calls between HIP events (not a captured graph)")
 
 
 def run_comparators(cfg, base, ctx, steps, warmup):
@@ -281,40 +363,57 @@ def run_comparators(cfg, base, ctx, steps, warmup):
 
 
 def run_compact_workload(cfg, steps, warmup, label):
-    """kv_compact on the full compaction workload, then sals_dense_decode over the compact cache,
-    and kv_compact_from_importance (selection and gather from a given importance, as a higher
-    layer reusing this layer's); each timed as `steps` back-to-back calls between two HIP events."""
+    """The post-prefill compaction workload (B=16, 32 heads, ctx 16384, w=64, 10% kept), each call
+    timed as `steps` back-to-back calls between two HIP events:
+      kv_compact (and its stages, through kv_compact_traced), the dense decode over the compact
+      cache, kv_compact_from_importance (a higher layer reusing this layer's importance),
+      kv_importance_sparsity, kv_outlier_importance (frequency-domain importance, 32 frequencies)
+      and the compaction it drives, kv_quantize_mixed + sals_dense_decode_mixed (10% of the tokens
+      at 8 bits, the rest at 4), kv_importance_budget, and the dense decode over the full cache."""
+    import ctypes
+
     import numpy as np
     import torch
 
     import kv_cache_compression_sals_amd as sals
+    from kv_cache_compression_sals_amd._lib import KvcShape, lib
     from workloads import compact_case
 
     t0 = time.time()
     case = compact_case(cfg, threads=16)
     log(f"[{label}] generated inputs in {time.time() - t0:.1f}s")
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
     K, V, Qobs, q = (dev(case[n]) for n in ("K", "V", "Qobs", "q"))
     del case
     B, H_kv, ctx_cap, d = K.shape
+    H_q, w = Qobs.shape[1], Qobs.shape[2]
     ctx, kk = cfg.ctx, cfg.k_keep
     Kc = torch.empty((B, H_kv, kk, d), dtype=K.dtype, device="cuda")
     Vc, kept = torch.empty_like(Kc), torch.empty((B, H_kv, kk), dtype=torch.int32, device="cuda")
-    out = torch.empty((B, Qobs.shape[1], d), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, H_q, d), dtype=torch.float32, device="cuda")
     ws_c = torch.empty(sals.kv_compact_workspace_bytes(K, Qobs, ctx=ctx, k_keep=kk), dtype=torch.uint8, device="cuda")
     ws_d = torch.empty(sals.sals_dense_decode_workspace_bytes(q, Kc, n=kk), dtype=torch.uint8, device="cuda")
+    ws_f = torch.empty(sals.sals_dense_decode_workspace_bytes(q, K, n=ctx), dtype=torch.uint8, device="cuda")
     imp = torch.empty((B, H_kv, ctx), dtype=torch.float32, device="cuda")
-    compact = lambda: sals.kv_compact(K, V, Qobs, ctx=ctx, k_keep=kk, Kc=Kc, Vc=Vc, kept=kept, importance=imp,
+    compact = lambda: sals.kv_compact(K, V, Qobs, ctx=ctx, k_keep=kk, Kc=Kc, Vc=Vc, kept=kept, importance=imp,  # noqa: E731
                                       workspace=ws_c)
-    decode = lambda: sals.sals_dense_decode(q, Kc, Vc, n=kk, out=out, workspace=ws_d)
-    # a higher layer compacted by this layer's importance (the same cache stands in for it)
-    reuse = lambda: sals.kv_compact_from_importance(K, V, imp, k_keep=kk, Kc=Kc, Vc=Vc, kept=kept)
-    # importance plus the post-vision sparsity per head at p = 1e-3 (the input of layer budgets)
-    spars = torch.empty((B, Qobs.shape[1]), dtype=torch.float32, device="cuda")
+    decode = lambda: sals.sals_dense_decode(q, Kc, Vc, n=kk, out=out, workspace=ws_d)  # noqa: E731
+    full = lambda: sals.sals_dense_decode(q, K, V, n=ctx, out=out, workspace=ws_f)  # noqa: E731
+    reuse = lambda: sals.kv_compact_from_importance(K, V, imp, k_keep=kk, Kc=Kc, Vc=Vc, kept=kept)  # noqa: E731
+    spars = torch.empty((B, H_q), dtype=torch.float32, device="cuda")
     ws_s = torch.empty(sals.kv_importance_sparsity_workspace_bytes(K, Qobs, ctx=ctx), dtype=torch.uint8,
                        device="cuda")
-    sparse = lambda: sals.kv_importance_sparsity(K, Qobs, ctx=ctx, p=1e-3, importance=imp, sparsity=spars,
+    sparse = lambda: sals.kv_importance_sparsity(K, Qobs, ctx=ctx, p=1e-3, importance=imp, sparsity=spars,  # noqa: E731
                                                  workspace=ws_s)
+    n_freq = 32
+    oimp = torch.empty_like(imp)
+    ws_o = torch.empty(sals.kv_outlier_importance_workspace_bytes(K, ctx=ctx, n_freq=n_freq), dtype=torch.uint8,
+                       device="cuda")
+    outlier = lambda: sals.kv_outlier_importance(K, V, ctx=ctx, n_freq=n_freq, importance=oimp, workspace=ws_o)  # noqa: E731
+    outlier_keep = lambda: sals.kv_compact_from_importance(K, V, oimp, k_keep=kk, Kc=Kc, Vc=Vc, kept=kept)  # noqa: E731
+    mixed = {}
+    quantize = lambda: sals.kv_quantize_mixed(K, V, imp, n_hi=kk, out=mixed)  # noqa: E731
+    budget = lambda: sals.kv_importance_budget(imp, mass=0.9)  # noqa: E731
 
     def timed(fn):
         for _ in range(warmup):
@@ -328,22 +427,70 @@ def run_compact_workload(cfg, steps, warmup, label):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps * 1e3
 
-    c_us, d_us, r_us, s_us = timed(compact), timed(decode), timed(reuse), timed(sparse)
+    c_us, d_us, r_us, s_us, f_us = timed(compact), timed(decode), timed(reuse), timed(sparse), timed(full)
+    o_us, ok_us = timed(outlier), timed(outlier_keep)
+    q_us = timed(quantize)
+    ws_m = torch.empty(sals.sals_dense_decode_mixed_workspace_bytes(q, H_kv, n_hi=kk, n_lo=ctx - kk), dtype=torch.uint8,
+                       device="cuda")
+    md_us = timed(lambda: sals.sals_dense_decode_mixed(q, mixed, out=out, workspace=ws_m))
+    b_us = timed(budget)
+
+    # the stages of kv_compact, from HIP events on its stream
+    c = KvcShape(B, H_q, H_kv, d, 1)
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        handles = (ctypes.c_void_p * 5)(*[e.cuda_event for e in evs[i]])
+        st = lib().kv_compact_traced(ctypes.byref(c), K.data_ptr(), V.data_ptr(), Qobs.data_ptr(), w, ctx_cap, ctx,
+                                     kk, Kc.data_ptr(), Vc.data_ptr(), kept.data_ptr(), imp.data_ptr(), ws_c.data_ptr(),
+                                     ws_c.numel(), stream, handles, 5)
+        if st:
+            raise RuntimeError(f"kv_compact_traced returned {st}")
+    torch.cuda.synchronize()
+    names = ["importance_stats", "importance_accum", "topk", "gather"]
+    stage_us = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps * 1e3
+                for j, n in enumerate(names)}
     s = 2
+    k_bytes = B * H_kv * ctx * d * s
+    q_bytes = Qobs.numel() * s
+    stage_bytes = {"importance_stats": k_bytes + q_bytes, "importance_accum": k_bytes + q_bytes + B * H_kv * ctx * 4,
+                   "topk": B * H_kv * ctx * 4 + B * H_kv * kk * 4, "gather": 4 * B * H_kv * kk * d * s}
+    dom = max(stage_us, key=stage_us.get)
+    achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
+    roofline = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None, algorithmic_per_launch=stage_bytes[dom],
+                    avg_launch_us=round(stage_us[dom], 2),
+                    flops_per_launch=2 * B * H_q * w * ctx * d)
     # compaction: K once for the importance (its second pass is recomputation), the kept K and V
     # rows read and written once, the observation queries; decode: the compact cache once
-    c_bytes = B * H_kv * ctx * d * s + 4 * B * H_kv * kk * d * s + Qobs.numel() * s
+    c_bytes = k_bytes + 4 * B * H_kv * kk * d * s + q_bytes
     d_bytes = 2 * B * H_kv * kk * d * s
+    f_bytes = 2 * k_bytes
     r_bytes = B * H_kv * ctx * 4 + 4 * B * H_kv * kk * d * s
-    H_q = Qobs.shape[1]
-    del K, V, Qobs, Kc, Vc, ws_c, ws_d, imp, ws_s
+    o_bytes = 2 * k_bytes + B * H_kv * ctx * 4  # K and V once, the importance out
+    n_lo = ctx - kk
+    m_bytes = 2 * B * H_kv * (kk * (d + d // 32 * 8) + n_lo * (d // 2 + d // 32 * 8))  # both sets, codes + params
+    qz_bytes = 2 * k_bytes + B * H_kv * ctx * 4 + m_bytes
+    gbps = lambda nbytes, us: round(nbytes / (us * 1e-6) / 1e9, 1)  # noqa: E731
+    del K, V, Qobs, Kc, Vc, ws_c, ws_d, ws_f, imp, ws_s, oimp, ws_o, mixed, ws_m
     torch.cuda.empty_cache()
-    return dict(workload=f"{label}: B={B} H_q={H_q} H_kv={H_kv} d={d} ctx={ctx} w={cfg.w} "
-                         f"k_keep={kk}, bf16",
-                compact_us=round(c_us, 1), compact_gbps=round(c_bytes / (c_us * 1e-6) / 1e9, 1),
-                decode_us=round(d_us, 2), decode_gbps=round(d_bytes / (d_us * 1e-6) / 1e9, 1),
-                from_importance_us=round(r_us, 2), from_importance_gbps=round(r_bytes / (r_us * 1e-6) / 1e9, 1),
+    return dict(workload=f"{label}: B={B} H_q={H_q} H_kv={H_kv} d={d} ctx={ctx} w={w} k_keep={kk}, bf16",
+                compact_us=round(c_us, 1), compact_gbps=gbps(c_bytes, c_us),
+                stage_us={k: round(v, 2) for k, v in stage_us.items()}, roofline=roofline,
+                decode_us=round(d_us, 2), decode_gbps=gbps(d_bytes, d_us),
+                full_cache_decode_us=round(f_us, 2), full_cache_decode_gbps=gbps(f_bytes, f_us),
+                from_importance_us=round(r_us, 2), from_importance_gbps=gbps(r_bytes, r_us),
                 importance_sparsity_us=round(s_us, 1),
+                outlier_importance_us=round(o_us, 1), outlier_importance_gbps=gbps(o_bytes, o_us),
+                outlier_compact_us=round(o_us + ok_us, 1), n_freq=n_freq,
+                quantize_mixed_us=round(q_us, 1), quantize_mixed_gbps=gbps(qz_bytes, q_us),
+                mixed_decode_us=round(md_us, 2), mixed_decode_gbps=gbps(m_bytes, md_us),
+                mixed_cache_bytes=m_bytes, bf16_cache_bytes=f_bytes,
+                importance_budget_us=round(b_us, 2),
                 compact_bytes=c_bytes, decode_bytes=d_bytes, from_importance_bytes=r_bytes)
 
 
@@ -401,14 +548,59 @@ def run_layers_workload(cfg, steps, warmup, label, n_layers=32):
     graph.replay()
     torch.cuda.synchronize()
     us = (time.perf_counter() - t_start) / steps * 1e6
+    rep = replay_stats(graph, steps, 3)
     alg = algorithmic(cfg, ctx)
-    del graph, layers, ws
+    del graph
+    # per-stage durations: one eager pass through the layers with HIP events at the stage boundaries
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_layers)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for l, t in enumerate(layers):
+        sals.sals_decode_step_traced(t["q"], t["Lk"], t["Lv"], t["Pk"], t["Pv"], evs[l], out=outs[l], workspace=ws,
+                                     **kw)
+    torch.cuda.synchronize()
+    stage_us = {name: sum(evs[l][j].elapsed_time(evs[l][j + 1]) for l in range(n_layers)) / n_layers * 1e3
+                for j, name in enumerate(stages_of(cfg))}
+    rl, _ = roofline_for(cfg, ctx, stage_us, label)
+    del layers, ws
     torch.cuda.empty_cache()
     return dict(workload=f"{label}: {n_layers} layers, B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} d={cfg.d} "
                          f"ctx={ctx} r={cfg.r} k={cfg.k} w={cfg.w} G={cfg.G}",
-                us_per_step=round(us, 1), us_per_layer=round(us / n_layers, 2),
+                us_per_step=round(us, 1), us_per_layer=round(us / n_layers, 2), us_per_step_stats=rep,
                 kv_gbps=round(n_layers * alg["compulsory"] / (us * 1e-6) / 1e9, 1),
-                compulsory_bytes_per_step=n_layers * alg["compulsory"])
+                hbm_frac=round(n_layers * alg["compulsory"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                compulsory_bytes_per_step=n_layers * alg["compulsory"],
+                stage_us_per_layer={k: round(v, 2) for k, v in stage_us.items()}, roofline=rl)
+
+
+def measure_hbm(gib=2):
+    """HBM read bandwidth of the in-tree streaming kernel (sals_hbm_read) over a buffer of `gib`
+    GiB, for 2048, 4096 and 8192 workgroups: the best of five timed reads each."""
+    import torch
+
+    from kv_cache_compression_sals_amd._lib import lib
+
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(7)
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    best = 0.0
+    for blocks in (2048, 4096, 8192):
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            st = lib().sals_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if st:
+                raise RuntimeError(f"sals_hbm_read returned {st}")
+            best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return round(best, 1)
 
 
 def roofline_for(cfg, ctx, stage_us, label):
@@ -434,43 +626,89 @@ def roofline_for(cfg, ctx, stage_us, label):
     return rl, alg
 
 
-def cpu_baseline(case, budget_s=10.0):
-    """The oracle (fp64 NumPy, as it stands) on the same stored inputs: whole decode steps of the
-    workload (all sequences, all heads), repeated until about budget_s of CPU time has passed;
-    the mean step time is reported."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_step(case):
     import oracle
 
+    oracle.decode_step(case["q"], case["Lk"], case["Lv"], case["Pk"], case["Pv"], ctx=case["ctx"], k=case["k"],
+                       w=case["w"], G=case["G"], H_kv=case["H_kv"], base=case["base"], dtype=case["dtype"])
+
+
+def cpu_baseline(case, budget_s=10.0, tiny=None):
+    """The oracle (fp64 NumPy, as it stands) on the same stored inputs: whole decode steps of the
+    workload (all sequences, all heads), repeated until about budget_s of CPU time has passed;
+    the mean step time is reported, with every BLAS thread of the process. Beside it: one step
+    with a single thread, and the tiny fp32 workload's step (median of 5) with all threads and
+    with one."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     try:
-        from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
         cores = 1
     n, t0 = 0, time.perf_counter()
     while n == 0 or time.perf_counter() - t0 < budget_s:
-        oracle.decode_step(case["q"], case["Lk"], case["Lv"], case["Pk"], case["Pv"], ctx=case["ctx"],
-                           k=case["k"], w=case["w"], G=case["G"], H_kv=case["H_kv"], base=case["base"],
-                           dtype=case["dtype"])
+        _oracle_step(case)
         n += 1
     per_step = (time.perf_counter() - t0) / n
-    return dict(value=round(per_step * 1e6, 1), unit="us/decode_step", cores=cores, kind="oracle",
-                sample=f"{n} whole oracle decode steps of the same workload (all {case['B']} sequences, "
-                       f"all heads), mean, {n * per_step:.1f} s in total")
+    one = {}
+    with threadpool_limits(1):
+        t1 = time.perf_counter()
+        _oracle_step(case)
+        one["headline_us"] = round((time.perf_counter() - t1) * 1e6, 1)
+    if tiny is not None:
+        def med5():
+            ts = []
+            for _ in range(5):
+                t1 = time.perf_counter()
+                _oracle_step(tiny)
+                ts.append(time.perf_counter() - t1)
+            return round(sorted(ts)[2] * 1e6, 1)
+        tiny_all = med5()
+        with threadpool_limits(1):
+            one["tiny_us"] = med5()
+    out = dict(value=round(per_step * 1e6, 1), unit="us/decode_step", cores=cores, kind="oracle",
+               sample=f"{n} whole oracle decode steps of the same workload (all {case['B']} sequences, "
+                      f"all heads), mean, {n * per_step:.1f} s in total", cpu_model=cpu_model(),
+               one_thread=one)
+    if tiny is not None:
+        out["tiny_us"] = tiny_all
+    return out
 
 
-def summary(cfg, r, label):
+def summary(cfg, r, label, hbm_measured=None):
     rl, alg = roofline_for(cfg, r["case"]["ctx"], r["stage_us"], label)
     gbps = alg["compulsory"] / (r["us"] * 1e-6) / 1e9
+    # scoring + attention: the latent scan and the rebuild/attention stage over their summed time
+    sa = ("latent_score", "select_attend") + (("value",) if "value" in r["stage_us"] else ())
+    sa_bytes = sum(alg["stage_bytes"][k] for k in sa)
+    sa_us = sum(r["stage_us"][k] for k in sa)
     return dict(
         us_per_step=round(r["us"], 2),
+        us_per_step_stats=r["replays"],
+        warm_us_per_step=r["warm"]["median"],
         kv_gbps=round(gbps, 1),
         hbm_frac=round(gbps / HBM_PEAK_GBPS, 4),
+        hbm_frac_measured=round(gbps / hbm_measured, 4) if hbm_measured else None,
+        scoring_attention_gbps=round(sa_bytes / (sa_us * 1e-6) / 1e9, 1),
+        scoring_attention_hbm_frac=round(sa_bytes / (sa_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         eager_us_per_step=round(r["eager_us"], 2),
         event_us_per_step=round(r["event_step_us"], 2),
         stage_us={k: round(v, 2) for k, v in r["stage_us"].items()},
         k_rebuild_tflops=round(alg["k_rebuild_flops"] / (r["stage_us"]["select_attend"] * 1e-6) / 1e12, 1),
         compulsory_bytes=alg["compulsory"],
         roofline=rl,
-    ) | ({} if not r.get("comparators") else dict(comparators=dict(
+    ) | ({} if not r.get("threshold") else dict(threshold=r["threshold"])) | (
+        {} if not r.get("comparators") else dict(comparators=dict(
         r["comparators"],
         speedup_vs_dense_full_kv=round(r["comparators"]["dense_full_kv_us"] / r["us"], 2),
         speedup_vs_full_rebuild=round(r["comparators"]["full_rebuild_then_dense_us"] / r["us"], 2))))
@@ -481,8 +719,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replays", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="c2,c3")
+    ap.add_argument("--no-hbm-probe", action="store_true")
+    ap.add_argument("--only", default="c1,c2,c3,c4,c5")
     ap.add_argument("--calib-copy-mib", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -505,23 +745,39 @@ def main():
         torch.cuda.synchronize()
         log(f"[calib] copied {args.calib_copy_mib} MiB")
         del a, b
+    hbm = None
+    if not args.no_hbm_probe:
+        hbm = measure_hbm()
+        log(f"[hbm] streaming read {hbm:.0f} GB/s")
 
-    labels = {"c2": "ctx4k", "c3": "ctx32k", "c4": "compact_ctx16k", "c5": "ctx128k_32layers"}
+    labels = {"c1": "ctx512_tiny", "c2": "ctx4k", "c3": "ctx32k", "c4": "compact_ctx16k", "c5": "ctx128k_32layers"}
     keys = [k for k in args.only.split(",") if k]
     extra = {}
     for key in [k for k in keys if k in ("c4", "c5")]:
         fn = run_compact_workload if key == "c4" else run_layers_workload
         extra[labels[key]] = fn(CONFIGS[key], min(args.steps, 10), min(args.warmup, 2), labels[key])
         log(f"[{labels[key]}] {extra[labels[key]]}")
-    keys = [k for k in keys if k not in ("c4", "c5")]
+    tiny = None
+    if "c1" in keys:
+        cfg = CONFIGS["c1"]
+        r = run_workload(cfg, args.steps, args.warmup, labels["c1"], args.replays, comparators=False)
+        sm = summary(cfg, r, labels["c1"], hbm)
+        extra[labels["c1"]] = dict(workload=f"{labels['c1']} decode, one layer: B={cfg.B} H_q={cfg.H_q} "
+                                            f"H_kv={cfg.H_kv} d={cfg.d} ctx={cfg.ctx} r={cfg.r} k={cfg.k} w={cfg.w} "
+                                            f"G={cfg.G}, fp32 (latency-bound)",
+                                   us_per_step=sm["us_per_step"], us_per_step_stats=sm["us_per_step_stats"],
+                                   warm_us_per_step=sm["warm_us_per_step"], stage_us=sm["stage_us"])
+        tiny = r["case"]
+        log(f"[{labels['c1']}] {sm['us_per_step']:.1f} us/step")
+    keys = [k for k in keys if k in ("c2", "c3")]
     if not keys:
         print("--only must name c2 or c3 (the step the JSON line's value reports)", file=sys.stderr)
         sys.exit(2)
     res = {}
     for key in keys:
         cfg = CONFIGS[key]
-        r = run_workload(cfg, args.steps, args.warmup, labels[key])
-        res[key] = (cfg, r, summary(cfg, r, labels[key]))
+        r = run_workload(cfg, args.steps, args.warmup, labels[key], args.replays)
+        res[key] = (cfg, r, summary(cfg, r, labels[key], hbm))
         sm = res[key][2]
         log(f"[{labels[key]}] {sm['us_per_step']:.1f} us/step (eager traced {sm['eager_us_per_step']:.1f}), "
             f"{sm['kv_gbps']:.0f} GB/s effective, stages "
@@ -546,6 +802,7 @@ def main():
             "workload": f"{labels[head]} decode, one layer: B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} d={cfg.d} "
                         f"ctx={cfg.ctx} r={cfg.r} k={cfg.k} w={cfg.w} G={cfg.G}",
         },
+        "hbm_measured_gbps": hbm,
     }
     line.update({k: v for k, v in sm.items() if k != "us_per_step"})
     for key in keys[1:]:
@@ -556,7 +813,7 @@ def main():
     line.update(extra)
     if not args.no_cpu_baseline:
         log(f"[cpu] timing the oracle on a bounded sample of the {labels[head]} workload")
-        line["cpu_baseline"] = cpu_baseline(r["case"])
+        line["cpu_baseline"] = cpu_baseline(r["case"], tiny=tiny)
     print(json.dumps(line), flush=True)
 
 

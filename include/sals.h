@@ -239,6 +239,27 @@ sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const v
                        sals_stream_t stream);
 
 /*
+ * kv_compact_traced - kv_compact that also records caller-created HIP events on `stream` at its
+ * stage boundaries, for per-stage timing without a profiler (results identical to kv_compact):
+ * events[0] before the importance statistics pass, events[1] before the accumulation pass,
+ * events[2] before the top-k, events[3] before the gather, events[4] after it.
+ * events: at least 5 hipEvent_t handles (owned by the caller); SALS_ERR_NULL if events is NULL,
+ * SALS_ERR_RANGE if n_events < 5.
+ */
+sals_status kv_compact_traced(const kvc_shape* c, const void* K, const void* V, const void* Qobs,
+                              int32_t w, int32_t ctx_cap, int32_t ctx, int32_t k_keep, void* Kc, void* Vc,
+                              int32_t* kept, float* importance, void* ws, size_t ws_bytes,
+                              sals_stream_t stream, void* const* events, int32_t n_events);
+
+/*
+ * sals_hbm_read - a plain streaming read of `bytes` (a multiple of 16) at `src`, by `blocks`
+ * workgroups of 256 threads, each writing one word to sink[block]: the measured HBM read bandwidth
+ * that the kernels' fractions are also stated against (next to the 8 TB/s specification).
+ * Errors: NULL, RANGE (bytes 0 or not a multiple of 16, blocks outside [1, 2^20]), ALIGN, HIP.
+ */
+sals_status sals_hbm_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, sals_stream_t stream);
+
+/*
  * kv_importance_sparsity_workspace_bytes - workspace size of kv_importance_sparsity.
  */
 sals_status kv_importance_sparsity_workspace_bytes(const kvc_shape* c, int32_t ctx, int32_t w,

@@ -40,6 +40,7 @@ SOURCES = [
     "kernels/outlier.hip",
     "kernels/quant.hip",
     "kernels/budget.hip",
+    "kernels/probe.hip",
 ]
 
 

@@ -157,6 +157,10 @@ hipError_t launch_mixed_decode(const void* q, const uint8_t* codes_hi, const flo
 hipError_t launch_mass_budget(const float* imp, int rows, int ctx, float mass, int32_t* n_keep, float* total,
                               float* ratio, float* energy, hipStream_t st);
 
+// Streaming read of bytes (a multiple of 16) with `blocks` workgroups of 256 threads; sink gets
+// one word per workgroup.
+hipError_t launch_hbm_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t st);
+
 // Flash-decode over a contiguous cache: partials per split, or out directly (n_splits == 1).
 // Query heads of one KV head that a dense-decode workgroup serves together: 4, 2 or 1.
 __host__ __device__ inline int dense_heads_per_group(int nqh) { return nqh % 4 == 0 ? 4 : nqh % 2 == 0 ? 2 : 1; }

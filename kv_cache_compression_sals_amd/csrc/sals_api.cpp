@@ -443,10 +443,12 @@ sals_status kv_compact_workspace_bytes(const kvc_shape* c, int32_t ctx, int32_t 
   return SALS_OK;
 }
 
-sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const void* Qobs,
-                       int32_t w, int32_t ctx_cap, int32_t ctx, int32_t k_keep, void* Kc, void* Vc,
-                       int32_t* kept, float* importance, void* ws, size_t ws_bytes,
-                       sals_stream_t stream) {
+namespace {
+
+sals_status compact_impl(const kvc_shape* c, const void* K, const void* V, const void* Qobs, int32_t w,
+                         int32_t ctx_cap, int32_t ctx, int32_t k_keep, void* Kc, void* Vc, int32_t* kept,
+                         float* importance, void* ws, size_t ws_bytes, sals_stream_t stream,
+                         void* const* events) {
   if (!c || !K || !V || !Qobs || !Kc || !Vc || !kept) return SALS_ERR_NULL;
   CompactPlan p;
   sals_status st = make_compact_plan(c, ctx, w, k_keep, &p);
@@ -460,16 +462,57 @@ sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const v
   hipStream_t hs = (hipStream_t)stream;
   float* stats = (float*)((char*)ws + p.off_stats);
   float* I = importance ? importance : (float*)((char*)ws + p.off_I);
-  hipError_t e = sals::launch_importance_stats(c->dtype, K, Qobs, stats, c->B, c->H_q, c->H_kv,
-                                               c->d, w, ctx_cap, ctx, hs);
+  hipError_t e = hipSuccess;
+  auto mark = [&](int i) {
+    if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], hs);
+  };
+  mark(0);
+  if (e == hipSuccess)
+    e = sals::launch_importance_stats(c->dtype, K, Qobs, stats, c->B, c->H_q, c->H_kv, c->d, w, ctx_cap, ctx, hs);
+  mark(1);
   if (e == hipSuccess)
     e = sals::launch_importance_accum(c->dtype, K, Qobs, stats, I, c->B, c->H_q, c->H_kv, c->d, w,
                                       ctx_cap, ctx, hs);
+  mark(2);
   if (e == hipSuccess)
     e = sals::launch_topk_window(I, ctx, kept, c->B * c->H_kv, ctx, k_keep, ctx, k_keep, nullptr, hs);
+  mark(3);
   if (e == hipSuccess)
     e = sals::launch_gather_rows(c->dtype, K, V, kept, Kc, Vc, c->B * c->H_kv, c->d, ctx_cap,
                                  k_keep, hs);
+  mark(4);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
+}  // namespace
+
+sals_status kv_compact(const kvc_shape* c, const void* K, const void* V, const void* Qobs,
+                       int32_t w, int32_t ctx_cap, int32_t ctx, int32_t k_keep, void* Kc, void* Vc,
+                       int32_t* kept, float* importance, void* ws, size_t ws_bytes,
+                       sals_stream_t stream) {
+  return compact_impl(c, K, V, Qobs, w, ctx_cap, ctx, k_keep, Kc, Vc, kept, importance, ws, ws_bytes, stream,
+                      nullptr);
+}
+
+sals_status kv_compact_traced(const kvc_shape* c, const void* K, const void* V, const void* Qobs,
+                              int32_t w, int32_t ctx_cap, int32_t ctx, int32_t k_keep, void* Kc, void* Vc,
+                              int32_t* kept, float* importance, void* ws, size_t ws_bytes,
+                              sals_stream_t stream, void* const* events, int32_t n_events) {
+  if (!events) return SALS_ERR_NULL;
+  if (n_events < 5) return SALS_ERR_RANGE;
+  for (int i = 0; i < 5; ++i)
+    if (!events[i]) return SALS_ERR_NULL;
+  return compact_impl(c, K, V, Qobs, w, ctx_cap, ctx, k_keep, Kc, Vc, kept, importance, ws, ws_bytes, stream,
+                      events);
+}
+
+sals_status sals_hbm_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, sals_stream_t stream) {
+  if (!src || !sink) return SALS_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0 || blocks < 1 || blocks > (1 << 20)) return SALS_ERR_RANGE;
+  if (misaligned(src) || misaligned(sink)) return SALS_ERR_ALIGN;
+  sals_status st = device_ready();
+  if (st != SALS_OK) return st;
+  hipError_t e = sals::launch_hbm_read(src, bytes, sink, blocks, (hipStream_t)stream);
   return e == hipSuccess ? SALS_OK : hip_fail(e);
 }
 
