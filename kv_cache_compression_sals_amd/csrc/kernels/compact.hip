@@ -20,7 +20,7 @@ namespace sals {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 1024;  // tokens per workgroup
+constexpr int kChunk = SALS_IMP_CHUNK;  // tokens per workgroup
 constexpr int kQG = 64;       // observation queries per workgroup (4 MFMA column blocks)
 constexpr float kLog2e = 1.4426950408889634f;
 

@@ -9,8 +9,8 @@
 //   I[t] = ||K[t] - (C coef_K)[t]||^2 + ||V[t] - (C coef_V)[t]||^2   pass 2, per token
 // Both contractions run on bf16 MFMAs. The cache is exact in bf16; the basis values (fp32) and
 // the coefficients (fp32) enter as high + low bf16 parts, so every product carries about 2^-16
-// relative error and every sum is fp32. A basis value takes its angle from an exact integer
-// reduction, m = (2t + 1) f mod 4 ctx, and the hardware cosine of m / (4 ctx) revolutions.
+// relative error and every sum is fp32. A basis value takes its angle in revolutions,
+// (2t + 1) f / (4 ctx) reduced to [-1/2, 1/2) in fp64, and the hardware cosine of it.
 //
 // Pass 1: one workgroup per (b, g, K or V, chunk of 4096 tokens), in sub-tiles of 128 tokens.
 // The MFMA contracts over tokens, which is the slow axis of the cache, so each sub-tile is
@@ -37,12 +37,13 @@ constexpr int kSub = 128;    // tokens per pass-1 sub-tile
 constexpr int kRW = kSub / 2 + 4;  // LDS words per channel row of a transposed sub-tile (padded)
 constexpr int kTch2 = 2048;  // tokens per pass-2 workgroup
 
-// a_f cos(pi (2t + 1) f / (2 T)) in fp32, zero past the kept frequencies.
-__device__ __forceinline__ float dct_value(int t, int f, int T, int n_freq, float a0, float a1) {
+// a_f cos(pi (2t + 1) f / (2 T)) in fp32, zero past the kept frequencies. The angle in revolutions
+// is (2t + 1) f / (4 T): the product is an exact fp64 integer (below 2^34), times an fp64 1 / (4 T),
+// minus its floor, so the fraction carries ~1e-14 absolute error before the rounding to fp32.
+__device__ __forceinline__ float dct_value(int t, int f, double inv4T, int n_freq, float a0, float a1) {
   if (f >= n_freq) return 0.f;
-  const unsigned long long period = 4ull * (unsigned long long)T;
-  const unsigned long long m = ((2ull * (unsigned long long)t + 1ull) % period) * (unsigned long long)f % period;
-  float rev = (float)m / (float)period;  // [0, 1) revolutions
+  const double x = (2.0 * (double)t + 1.0) * (double)f * inv4T;
+  float rev = (float)(x - floor(x));  // [0, 1) revolutions
   rev = rev >= 0.5f ? rev - 1.0f : rev;
   return (f == 0 ? a0 : a1) * __builtin_amdgcn_cosf(rev);
 }
@@ -85,6 +86,7 @@ __global__ __launch_bounds__(256) void outlier_coef_kernel(const uint16_t* __res
   const uint16_t* X = (x ? V : K) + (size_t)pair * ctx_cap * D;
   const int t_begin = ch * kTch1, t_end = min(ctx, t_begin + kTch1);
   const float a0 = sqrtf(1.0f / (float)ctx), a1 = sqrtf(2.0f / (float)ctx);
+  const double inv4T = 1.0 / (4.0 * (double)ctx);
 
   // this thread's rows of a sub-tile: tokens 2p, 2p + 1; channels cq * CPT .. + CPT
   const int p = tid & 63, cq = tid >> 6;
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(256) void outlier_coef_kernel(const uint16_t* __res
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int t = s0 + 32 * ks + 8 * (l >> 4) + i;
-        v[i] = t < t_end ? dct_value(t, 16 * ft + (l & 15), ctx, n_freq, a0, a1) : 0.f;
+        v[i] = t < t_end ? dct_value(t, 16 * ft + (l & 15), inv4T, n_freq, a0, a1) : 0.f;
       }
       split8(v, bas[0][e], bas[1][e]);
     }
@@ -208,6 +210,7 @@ __global__ __launch_bounds__(256) void outlier_dev_kernel(const uint16_t* __rest
   const int wg = blockIdx.x;
   const int c2 = wg % nch2, pair = wg / nch2;
   const float a0 = sqrtf(1.0f / (float)ctx), a1 = sqrtf(2.0f / (float)ctx);
+  const double inv4T = 1.0 / (4.0 * (double)ctx);
   batched_copy<8>(2 * NA, tid, 256, [&](int i) { return afrag[(size_t)pair * 2 * NA + i]; },
                   [&](int i, const u32x4& v) { afr[i] = v; });
   __syncthreads();
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(256) void outlier_dev_kernel(const uint16_t* __rest
     for (int kf = 0; kf < KF; ++kf) {
       float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = ok ? dct_value(t, 32 * kf + 8 * q4 + i, ctx, n_freq, a0, a1) : 0.f;
+      for (int i = 0; i < 8; ++i) v[i] = ok ? dct_value(t, 32 * kf + 8 * q4 + i, inv4T, n_freq, a0, a1) : 0.f;
       split8(v, bh[kf], bl[kf]);
     }
     float dev = 0.f;

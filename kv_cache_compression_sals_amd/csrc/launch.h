@@ -117,6 +117,15 @@ hipError_t launch_project(int dtype, const void* X, const void* P, void* L, int 
 
 // ---- compaction and dense decode ---------------------------------------------------------
 
+// Tokens per workgroup of the two importance passes, and the size (MiB) of K the two passes
+// share per batch of sequences (0: one batch of every sequence).
+#ifndef SALS_IMP_CHUNK
+#define SALS_IMP_CHUNK 1024
+#endif
+#ifndef SALS_COMPACT_BATCH_MB
+#define SALS_COMPACT_BATCH_MB 0
+#endif
+
 // Per (b, g, observation query i): row max m and softmax denominator l of the causal logits.
 hipError_t launch_importance_stats(int dtype, const void* K, const void* Qobs, float* stats,
                                    int B, int H_q, int H_kv, int d, int w, int ctx_cap, int ctx,

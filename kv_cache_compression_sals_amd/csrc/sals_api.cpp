@@ -141,7 +141,7 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
 
 // ---- compaction plan -----------------------------------------------------------------------
 
-constexpr int kImpChunk = 1024;
+constexpr int kImpChunk = SALS_IMP_CHUNK;
 
 struct CompactPlan {
   size_t off_stats, off_I, total;
@@ -445,6 +445,42 @@ sals_status kv_compact_workspace_bytes(const kvc_shape* c, int32_t ctx, int32_t 
 
 namespace {
 
+// Sequences per importance batch (SALS_COMPACT_BATCH_MB MiB of K per batch; 0: all sequences in
+// one batch). The two importance passes read the same K, so batches small enough for the 256 MB
+// Infinity Cache let the second pass find it there; measured at the compaction workload (one
+// 134 MB sequence per batch), the smaller launches (512 workgroups) leave the chip underfilled
+// and cost more than the cache saves (1428 vs 1292 us), so the default is one batch.
+int compact_batch(const kvc_shape* c, int32_t ctx_cap) {
+  if (SALS_COMPACT_BATCH_MB <= 0) return c->B;
+  const double per_seq = (double)c->H_kv * ctx_cap * c->d * elem_size(c->dtype);
+  const int nb = (int)((SALS_COMPACT_BATCH_MB * (double)(1 << 20)) / per_seq);
+  return nb < 1 ? 1 : nb;
+}
+
+// The statistics pass (which & 1) and/or the accumulation pass (which & 2) of sequences
+// [b0, b0 + nb) (clamped to B), each batch with its own region of the statistics workspace
+// (merged stats, then chunk partials), so batches never overlap. With cnt / sparsity (the
+// post-vision sparsity), their rows of the batch are written too.
+hipError_t importance_batch(const kvc_shape* c, const void* K, const void* Qobs, int32_t w, int32_t ctx_cap,
+                            int32_t ctx, int b0, int nb, float* stats, float* I, float* cnt, float* sparsity,
+                            float p_thresh, hipStream_t hs, int which) {
+  if (b0 + nb > c->B) nb = c->B - b0;
+  const size_t es = elem_size(c->dtype);
+  const size_t n_chunks = (ctx + kImpChunk - 1) / kImpChunk;
+  const size_t per_seq_stats = (size_t)c->H_q * w * 2 + (size_t)c->H_q * w * n_chunks * 2;
+  const char* Kb = (const char*)K + (size_t)b0 * c->H_kv * ctx_cap * c->d * es;
+  const char* Qb = (const char*)Qobs + (size_t)b0 * c->H_q * w * c->d * es;
+  float* st = stats + (size_t)b0 * per_seq_stats;
+  float* Ib = I + (size_t)b0 * c->H_kv * ctx;
+  hipError_t e = hipSuccess;
+  if (which & 1) e = sals::launch_importance_stats(c->dtype, Kb, Qb, st, nb, c->H_q, c->H_kv, c->d, w, ctx_cap, ctx, hs);
+  if (e == hipSuccess && (which & 2))
+    e = sals::launch_importance_accum(c->dtype, Kb, Qb, st, Ib, nb, c->H_q, c->H_kv, c->d, w, ctx_cap, ctx, hs,
+                                      p_thresh, cnt ? cnt + (size_t)b0 * c->H_q * n_chunks : nullptr,
+                                      sparsity ? sparsity + (size_t)b0 * c->H_q : nullptr);
+  return e;
+}
+
 sals_status compact_impl(const kvc_shape* c, const void* K, const void* V, const void* Qobs, int32_t w,
                          int32_t ctx_cap, int32_t ctx, int32_t k_keep, void* Kc, void* Vc, int32_t* kept,
                          float* importance, void* ws, size_t ws_bytes, sals_stream_t stream,
@@ -467,12 +503,18 @@ sals_status compact_impl(const kvc_shape* c, const void* K, const void* V, const
     if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], hs);
   };
   mark(0);
-  if (e == hipSuccess)
-    e = sals::launch_importance_stats(c->dtype, K, Qobs, stats, c->B, c->H_q, c->H_kv, c->d, w, ctx_cap, ctx, hs);
-  mark(1);
-  if (e == hipSuccess)
-    e = sals::launch_importance_accum(c->dtype, K, Qobs, stats, I, c->B, c->H_q, c->H_kv, c->d, w,
-                                      ctx_cap, ctx, hs);
+  if (events) {  // traced: the two passes over all sequences, so that each has its own events
+    if (e == hipSuccess) e = importance_batch(c, K, Qobs, w, ctx_cap, ctx, 0, c->B, stats, I, nullptr, nullptr, 0.f,
+                                              hs, 1);
+    mark(1);
+    if (e == hipSuccess) e = importance_batch(c, K, Qobs, w, ctx_cap, ctx, 0, c->B, stats, I, nullptr, nullptr, 0.f,
+                                              hs, 2);
+  } else {
+    for (int b0 = 0; b0 < c->B && e == hipSuccess; b0 += compact_batch(c, ctx_cap))
+      e = importance_batch(c, K, Qobs, w, ctx_cap, ctx, b0, compact_batch(c, ctx_cap), stats, I, nullptr, nullptr,
+                           0.f, hs, 3);
+    mark(1);
+  }
   mark(2);
   if (e == hipSuccess)
     e = sals::launch_topk_window(I, ctx, kept, c->B * c->H_kv, ctx, k_keep, ctx, k_keep, nullptr, hs);
@@ -544,11 +586,10 @@ sals_status kv_importance_sparsity(const kvc_shape* c, const void* K, const void
   hipStream_t hs = (hipStream_t)stream;
   float* stats = (float*)((char*)ws + p.off_stats);
   float* cnt = (float*)((char*)ws + p.off_I);
-  hipError_t e = sals::launch_importance_stats(c->dtype, K, Qobs, stats, c->B, c->H_q, c->H_kv,
-                                               c->d, w, ctx_cap, ctx, hs);
-  if (e == hipSuccess)
-    e = sals::launch_importance_accum(c->dtype, K, Qobs, stats, importance, c->B, c->H_q, c->H_kv,
-                                      c->d, w, ctx_cap, ctx, hs, p_thresh, cnt, sparsity);
+  hipError_t e = hipSuccess;
+  for (int b0 = 0; b0 < c->B && e == hipSuccess; b0 += compact_batch(c, ctx_cap))
+    e = importance_batch(c, K, Qobs, w, ctx_cap, ctx, b0, compact_batch(c, ctx_cap), stats, importance, cnt,
+                         sparsity, p_thresh, hs, 3);
   return e == hipSuccess ? SALS_OK : hip_fail(e);
 }
 
