@@ -1,5 +1,5 @@
-// Dispatch of the gather + rebuild + RoPE + attention kernel over the instantiated shapes, and
-// the LSE merge of split partials.
+// Dispatch of the gather + rebuild + RoPE + attention kernel over the instantiated shapes, the
+// LSE merge of split partials, and the merge + value product of its latent partials.
 #include "../common.h"
 #include "../launch.h"
 #include "select_attend.inc"
@@ -87,6 +87,121 @@ hipError_t launch_combine(const float* part, float* out, int BH, int d, int n_sp
                           hipStream_t st) {
   if (BH <= 0) return hipSuccess;
   combine_kernel<<<BH, 128, 0, st>>>(part, out, d, n_splits);
+  return hipGetLastError();
+}
+
+// Split merge of the gather + attention kernel's latent partials, then the value product:
+//   M = max_s m_s,  w_s = e^{m_s - M},  L = sum_s w_s l_s,  z = sum_s w_s z_s   (z in latent space)
+//   out[b][h][c] = sum_k P_v[g*d + c][k] z[k] / L
+// z is linear in the probabilities, so merging before the product gives the result of the
+// per-split products at one product per head. Workgroup (b*H_q + h, row block): every workgroup
+// merges all r columns (thread j owns columns j, j + 256, ..., splits in chunks of kSch with an
+// online rescale) while its P_v rows, requested first, are in flight; NPH consecutive lanes share
+// one row, each holding LPT 16-byte chunks of it, so that one load instruction covers whole
+// 128-byte lines. The product runs in fp32.
+constexpr int kSch = 16;
+template <class T, int R>
+__global__ __launch_bounds__(256) void latent_combine_kernel(const float* __restrict__ part,
+                                                             const typename T::elem* __restrict__ Pv,
+                                                             float* __restrict__ out, int H_q, int H_kv,
+                                                             int d, int n_splits) {
+  using E = typename T::elem;
+  constexpr int EPL = 16 / (int)sizeof(E);
+  constexpr int CPR = R / EPL;               // 16-byte chunks per P_v row
+  constexpr int NPH = CPR < 8 ? CPR : 8;     // lanes per row
+  constexpr int LPT = CPR / NPH;             // chunks per lane
+  constexpr int RW = 256 / NPH;              // rows per workgroup
+  constexpr int ZC = (R + 255) / 256;        // merged columns per thread
+  static_assert(CPR % NPH == 0 && LPT <= 16, "row split");
+  __shared__ float zs[R];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int h = bh % H_q, g = h / (H_q / H_kv);
+  const int row = tid / NPH, ph = tid % NPH;
+  const int c = blockIdx.y * RW + row;
+  const E* prow = Pv + ((size_t)g * d + min(c, d - 1)) * R;
+  u32x4 pa[LPT];
+#pragma unroll
+  for (int t = 0; t < LPT; ++t) pa[t] = *(const u32x4*)(prow + (ph + NPH * t) * EPL);
+
+  const float* pp = part + (size_t)bh * n_splits * (R + 2);
+  float M = -INFINITY, L = 0.f, z[ZC];
+#pragma unroll
+  for (int u = 0; u < ZC; ++u) z[u] = 0.f;
+  for (int s0 = 0; s0 < n_splits; s0 += kSch) {
+    const int ns = min(kSch, n_splits - s0);
+    float mv[kSch], lv[kSch], zv[kSch][ZC];
+#pragma unroll
+    for (int s = 0; s < kSch; ++s) {
+      const float* ps = pp + (size_t)(s0 + min(s, ns - 1)) * (R + 2);
+      mv[s] = ps[0];
+      lv[s] = ps[1];
+#pragma unroll
+      for (int u = 0; u < ZC; ++u) zv[s][u] = ps[2 + min(tid + 256 * u, R - 1)];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int s = 0; s < kSch; ++s)
+      if (s < ns) Mc = fmaxf(Mc, mv[s]);
+    if (Mc == -INFINITY) continue;  // only empty splits so far
+    const float f = expf(M - Mc);    // 0 while M is still -inf
+    L *= f;
+#pragma unroll
+    for (int u = 0; u < ZC; ++u) z[u] *= f;
+#pragma unroll
+    for (int s = 0; s < kSch; ++s) {
+      const float w = s < ns ? expf(mv[s] - Mc) : 0.f;  // an empty split (m = -inf) weighs 0
+      L = fmaf(w, lv[s], L);
+#pragma unroll
+      for (int u = 0; u < ZC; ++u) z[u] = fmaf(w, zv[s][u], z[u]);
+    }
+    M = Mc;
+  }
+#pragma unroll
+  for (int u = 0; u < ZC; ++u)
+    if (tid + 256 * u < R) zs[tid + 256 * u] = z[u];
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int t = 0; t < LPT; ++t) {
+    const int k0 = (ph + NPH * t) * EPL;
+    float x[EPL];
+    sa::unpack_chunk<T>(pa[t], x);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc = fmaf(x[e], zs[k0 + e], acc);
+  }
+#pragma unroll
+  for (int o = 1; o < NPH; o <<= 1) acc += __shfl_xor(acc, o);
+  if (ph == 0 && c < d) out[(size_t)bh * d + c] = acc / L;
+}
+
+template <class T, int R>
+void launch_latent_combine_t(const float* part, const void* Pv, float* out, int BH, int H_q, int H_kv,
+                             int d, int n_splits, hipStream_t st) {
+  constexpr int EPL = 16 / (int)sizeof(typename T::elem);
+  constexpr int CPR = R / EPL;
+  constexpr int RW = 256 / (CPR < 8 ? CPR : 8);
+  const dim3 grid(BH, (d + RW - 1) / RW);
+  latent_combine_kernel<T, R><<<grid, 256, 0, st>>>(part, (const typename T::elem*)Pv, out, H_q, H_kv, d,
+                                                    n_splits);
+}
+
+hipError_t launch_latent_combine(int dtype, const float* part, const void* Pv, float* out, int B, int H_q,
+                                 int H_kv, int d, int r, int n_splits, hipStream_t st) {
+  const int BH = B * H_q;
+  if (BH <= 0) return hipSuccess;
+#define SALS_CASE(RR)                                                                    \
+  case RR:                                                                               \
+    if (dtype == 1)                                                                      \
+      launch_latent_combine_t<BF16, RR>(part, Pv, out, BH, H_q, H_kv, d, n_splits, st);  \
+    else                                                                                 \
+      launch_latent_combine_t<F32, RR>(part, Pv, out, BH, H_q, H_kv, d, n_splits, st);   \
+    break;
+  switch (r) {
+    SALS_CASE(32) SALS_CASE(64) SALS_CASE(128) SALS_CASE(256) SALS_CASE(384) SALS_CASE(512)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef SALS_CASE
   return hipGetLastError();
 }
 

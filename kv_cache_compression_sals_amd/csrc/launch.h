@@ -44,7 +44,9 @@ hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, i
 uint32_t threshold_key(float tau);
 
 // Gather + rebuild + RoPE + attention over the selected rows, split along the selected set.
-// With n_splits == 1 the normalised result goes to out; otherwise (m, l, o) partials go to part.
+// With n_splits == 1 the normalised result goes to out; otherwise latent partials
+// part[b][h][split] = (m, l, z[0 .. r)) with z = sum_j e^{logit_j - m} L_v[pos_j] go to part, for
+// launch_latent_combine.
 // cnt (null for a fixed n_sel) gives each selection row's own length for a ragged (thresholded)
 // selection padded to n_sel; the same holds for launch_shared_keys and launch_value_sum.
 // With pbuf non-null the kernel stops after the softmax and hands the probabilities to the
@@ -106,6 +108,11 @@ hipError_t launch_value_product(int dtype, const ValuePlan& vp, const float* zpa
 // LSE merge of split partials into out[b][h][:].
 hipError_t launch_combine(const float* part, float* out, int BH, int d, int n_splits,
                           hipStream_t st);
+
+// LSE merge of launch_select_attend's latent partials and the value product:
+// out[b][h][c] = sum_k P_v[g*d + c][k] z[k] / L, z and L merged over the splits.
+hipError_t launch_latent_combine(int dtype, const float* part, const void* Pv, float* out, int B, int H_q,
+                                 int H_kv, int d, int r, int n_splits, hipStream_t st);
 
 // Largest selected-set split that fits in on-chip memory for this shape (0 if unsupported).
 int select_attend_max_split(int dtype, int d, int r, int nqh);

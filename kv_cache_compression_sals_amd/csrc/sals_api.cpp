@@ -126,7 +126,7 @@ sals_status make_decode_plan(const sals_shape* s, const sals_select* sel, int32_
   if ((long)p->n_splits * s->H_kv * s->B > 0x7fffffffL) return SALS_ERR_RANGE;
   p->off_part = off;
   if (p->n_splits > 1 && !p->shared)
-    off += align_up((size_t)s->B * s->H_q * p->n_splits * (s->d + 2) * 4);
+    off += align_up((size_t)s->B * s->H_q * p->n_splits * (s->r + 2) * 4);
   p->off_p = p->off_pstat = p->off_zp = off;
   if (p->shared) {
     off += align_up((size_t)s->B * s->H_q * ((p->n_sel + 3) / 4 * 4) * 4);
@@ -261,7 +261,8 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
       e = sals::launch_value_product(s->dtype, p.vp, zpart, Pv, out, s->B, s->H_q, s->H_kv, s->d,
                                      s->r, hs);
   } else if (e == hipSuccess && p.n_splits > 1) {
-    e = sals::launch_combine(part, out, s->B * s->H_q, s->d, p.n_splits, hs);
+    e = sals::launch_latent_combine(s->dtype, part, Pv, out, s->B, s->H_q, s->H_kv, s->d, s->r,
+                                    p.n_splits, hs);
   }
   mark(5);
   return e == hipSuccess ? SALS_OK : hip_fail(e);
