@@ -2,22 +2,29 @@
 // index set S_{psi,k} of the VL-Cache responses, reviewer XVzL weakness 2).
 //
 // One workgroup of 1024 threads per row. Scores become order-preserving uint32 keys (signed
-// zeros equal). The k-th largest key tau is found by an MSB-first radix select, and the row is
-// read in full only twice:
-//   1. one pass stages the keys in LDS (rows up to 32768 candidates) and builds a 2048-bin
-//      histogram of the top 11 key bits (sign, exponent, 2 mantissa bits), from which the bin
-//      b1 holding the k-th largest follows;
-//   2. a second pass lists, in index order, every position whose key lies in b1 or above (the
-//      keys of the higher bins plus b1's keys: a short list). Each thread tests 16 consecutive
-//      keys into a 16-bit hit mask; its list position is a prefix sum of the mask counts. The
-//      next 11 key bits of tau come from a histogram over the listed keys of b1, the last 10
-//      from one more pass over the short list, and the selection is the list filtered by
-//      (key > tau, or key == tau for the first take_eq of them), which keeps the list's index
-//      order.
-// If the list would not fit (heavily tied or degenerate rows, or k close to the row length),
-// the remaining digits and the ordered compaction run over the whole row instead (slower).
-// Every pass is branch-free over the keys and ranks come from ballots, so per-key work is a few
-// VALU operations: with one row per CU the passes are bound by issue rate, not memory.
+// zeros equal); the k-th largest key tau is found, and the selection is every key > tau plus
+// the first take_eq keys == tau, in index order.
+//
+// Rows up to 32768 candidates (topk_rows) keep KPT = 4..32 keys per thread in registers, so that
+// every pass over the keys is VALU work on registers and each phase ends in one barrier:
+//   1. coalesced 16-byte loads (values kept in registers, keys staged in LDS in a padded layout)
+//      and the row's key range;
+//   2. a 2048-bin histogram of equal-width value bins over that range (a monotone map, so bins
+//      are ordered like the keys) gives the bin b1 holding the k-th largest. Scores fill a few
+//      float exponents, so bins of the key bits would crowd them into a handful of bins; value
+//      bins spread them;
+//   3. b1 usually holds a few keys: they are gathered and tau is the one whose counts of larger
+//      and equal keys in b1 bracket the rank left over. A crowded b1 (heavy ties, or a range
+//      stretched by outliers) falls back to three key-bit digits;
+//   4. ordered compaction: thread t owns the KPT consecutive keys from t * KPT (read back from
+//      LDS), its output slots follow from a block prefix sum of its counts, and the positions
+//      are scattered to LDS and written out with coalesced stores.
+// Longer rows are split into slices whose candidates are merged by the same routine
+// (topk_slices), or, when that does not fit, go through topk_global: key-bit digits with the row
+// read from global memory, listing every position in the threshold bin or above and filtering
+// that list.
+// With one row per CU a row is bound by that CU's load bandwidth, its VALU issue rate and barrier
+// latency, not by HBM.
 #include <string.h>
 
 #include <type_traits>
@@ -32,15 +39,9 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLdsKeys = 32768;
 constexpr int kBins = 2048;
-constexpr int kIPT = 16;  // keys per lane per chunk when a wave ranks a run (16 slices of 64)
-
-template <bool IN_LDS>
-struct TopkLds {
-  // short-list capacity (positions): rows staged in LDS have positions below 32768, so their
-  // list holds 16-bit entries
-  static constexpr int LIST = IN_LDS ? 10240 : 16384;
-  using entry = std::conditional_t<IN_LDS, uint16_t, int32_t>;
-};
+constexpr int kIPT = 16;     // keys per lane per chunk when a wave ranks a run (16 slices of 64)
+constexpr int kSmall = 512;  // the largest threshold bin resolved by counting
+constexpr int kList = 16384; // short-list capacity of topk_global (positions)
 
 // Finds, in hist[0 .. kBins), the bin b holding the `remaining`-th largest item (bins ordered by
 // value, highest bin = largest): bcast[0] = b, bcast[1] = items in bins above b, bcast[2] =
@@ -88,246 +89,430 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remainin
   __syncthreads();
 }
 
-// The selection of one workgroup: the kp largest of n keys, ties to the lowest position, written
-// to out[0 .. kp) in ascending position order as map(position) (and, with okeys, their keys to
-// okeys[0 .. kp)), followed by the window out[kp + j] = wstart + j, j < wcount. Keys are
-// float_key(src[i]) with map(i) = obase + i, or (GATHER) the given keys ckeys[i] with
-// map(i) = cand[i]. GATHER requires IN_LDS.
-// Threshold mode (thr): only keys >= tkey may be selected, so kp becomes min(kp, #keys >= tkey)
-// (counted over the raw keys before anything else); out[kp + wcount .. pad_to) is filled with -1
-// and *cnt_out receives kp + wcount. For GATHER the count runs over the candidates: a row with
-// fewer than kp passing keys has all of them among the candidates, otherwise at least kp pass
-// there too, so min(kp, count) is the row's.
-template <bool IN_LDS, bool GATHER>
-__device__ __forceinline__ void topk_body(const float* __restrict__ src, const int32_t* __restrict__ cand,
-                                          const uint32_t* __restrict__ ckeys, int n, int kp,
-                                          int32_t* __restrict__ out, uint32_t* __restrict__ okeys,
-                                          int obase, int wcount, int wstart, bool vec, bool thr,
-                                          uint32_t tkey, int32_t* __restrict__ cnt_out, int pad_to) {
-  static_assert(IN_LDS || !GATHER, "candidate keys are staged in LDS");
-  constexpr int LIST = TopkLds<IN_LDS>::LIST;
-  __shared__ __attribute__((aligned(16))) uint32_t keys[IN_LDS ? kLdsKeys : 1];
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
-  __shared__ typename TopkLds<IN_LDS>::entry list[LIST];
-  __shared__ __attribute__((aligned(16))) uint32_t scan[kWaves];
-  __shared__ uint32_t bcast[4];
-  __shared__ uint32_t mm[GATHER ? 2 * kWaves : 1];  // per-wave key minima and maxima
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int Tc = n;
-  auto map = [&](int i) -> int32_t {
-    if constexpr (GATHER) return cand[i];
-    else return obase + i;
-  };
+// The float value of an order-preserving key (inverse of float_key).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
 
+// Exclusive prefix of a per-wave count over the waves of the workgroup, and the block total.
+__device__ __forceinline__ void block_prefix(uint32_t mine, uint32_t* scan, uint32_t& before, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (lane == 0) scan[wave] = mine;
+  __syncthreads();
+  before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t v = scan[w];
+    before += (w < wave) ? v : 0u;
+    total += v;
+  }
+  __syncthreads();
+}
+
+// The part of a selection that needs no ranking: the window out[kp + j] = wstart + j (j < wcount)
+// and, in threshold mode (thr), the cap of kp by the number of keys >= tkey (counted over
+// key(i), i < Tc), the padding out[kp + wcount .. pad_to) = -1 and *cnt_out = kp + wcount.
+// Returns the number of keys left to select by rank, or 0 when the selection is complete
+// (kp <= 0, or every key selected: out[j] = map(j)). The same value in every thread.
+// For candidate keys the threshold count runs over the candidates: a row with fewer than kp
+// passing keys has all of them among the candidates, otherwise at least kp pass there too, so
+// min(kp, count) is the row's.
+template <class KeyF, class MapF>
+__device__ __forceinline__ int topk_prologue(KeyF key, MapF map, int Tc, int kp, int32_t* __restrict__ out,
+                                             int wcount, int wstart, bool thr, uint32_t tkey,
+                                             int32_t* __restrict__ cnt_out, int pad_to, uint32_t* scan) {
+  const int tid = threadIdx.x, lane = tid & 63;
   if (thr) {
     if (kp > 0) {
       uint32_t mine = 0;
-      for (int i = tid; i < Tc; i += kThreads) {
-        uint32_t k;
-        if constexpr (GATHER) k = ckeys[i];
-        else k = float_key(src[i]);
-        mine += k >= tkey ? 1u : 0u;
-      }
-      const uint32_t wsum = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(mine, lane), 63);
-      if (lane == 0) scan[wave] = wsum;
-      __syncthreads();
-      uint32_t total = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) total += scan[w];
-      __syncthreads();  // scan is reused below
+      for (int i = tid; i < Tc; i += kThreads) mine += key(i) >= tkey ? 1u : 0u;
+      uint32_t before, total;
+      block_prefix((uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(mine, lane), 63), scan, before, total);
       kp = (int)min((uint32_t)kp, total);
     }
     for (int j = kp + wcount + tid; j < pad_to; j += kThreads) out[j] = -1;
     if (tid == 0 && cnt_out) *cnt_out = kp + wcount;
   }
   for (int j = tid; j < wcount; j += kThreads) out[kp + j] = wstart + j;
-  if (kp <= 0) return;
+  if (kp <= 0) return 0;
   if (kp >= Tc) {
     for (int j = tid; j < Tc; j += kThreads) out[j] = map(j);
+    return 0;
+  }
+  return kp;
+}
+
+// LDS word of key i in the staging layout: 4 pad words after every 32 keys, so that a thread
+// reading its 32 consecutive keys as 16-byte pieces and a wave writing consecutive 16-byte pieces
+// both spread over the banks.
+__device__ __forceinline__ int padded(int i) { return i + ((i >> 5) << 2); }
+constexpr int kStageWords = kLdsKeys / 32 * 36;
+
+// The selection of one workgroup over at most kThreads * KPT keys (thread t owns the KPT
+// consecutive keys from t * KPT and holds them in registers): the kp largest of n keys, ties to
+// the lowest position, written to out[0 .. kp) in ascending position order as map(position)
+// (and, with okeys, their keys to okeys[0 .. kp)), followed by the window out[kp + j] =
+// wstart + j, j < wcount. Keys are float_key(src[i]) with map(i) = obase + i, or (GATHER) the
+// given keys ckeys[i] with map(i) = cand[i]. Threshold mode (thr): only keys >= tkey may be
+// selected, so kp becomes min(kp, #keys >= tkey); out[kp + wcount .. pad_to) is filled with -1
+// and *cnt_out receives kp + wcount. For GATHER the count runs over the candidates: a row with
+// fewer than kp passing keys has all of them among the candidates, otherwise at least kp pass
+// there too, so min(kp, count) is the row's.
+template <int KPT, bool GATHER>
+__device__ __forceinline__ void topk_rows(const float* __restrict__ src, const int32_t* __restrict__ cand,
+                                          const uint32_t* __restrict__ ckeys, int n, int kp,
+                                          int32_t* __restrict__ out, uint32_t* __restrict__ okeys,
+                                          int obase, int wcount, int wstart, bool vec, bool thr,
+                                          uint32_t tkey, int32_t* __restrict__ cnt_out, int pad_to) {
+  static_assert(KPT % 4 == 0 && KPT <= 32 && kThreads * KPT <= kLdsKeys, "keys per thread");
+  // staged keys (padded layout); after the ranking, the selection's positions in output order
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kStageWords];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins + 4];  // [kBins]: keys past the row
+  __shared__ __attribute__((aligned(16))) uint32_t scan[kWaves];
+  __shared__ uint32_t bcast[4];
+  __shared__ uint32_t mm[3 * kWaves];  // per-wave key minima, maxima and threshold counts
+  __shared__ uint32_t nsmall, tsel[2];  // small-bin gather count; (tau, take_eq)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Tc = n;
+  for (int i = tid; i < kBins + 4; i += kThreads) hist[i] = 0;
+  if (tid == 0) nsmall = 0;
+
+  // ---- 1. coalesced loads: this thread's 16-byte pieces u = tid + kThreads * q hold positions
+  //      4u .. 4u + 3. They are kept in registers (values for the histogram) and staged in LDS as
+  //      keys; the row's range (and, in threshold mode, the count of keys >= tkey) follows ----
+  using Reg = std::conditional_t<GATHER, uint32_t, float>;  // candidate keys, or scores
+  Reg pr[KPT];
+  uint32_t lmn = 0xffffffffu, lmx = 0u, npass = 0u;
+  // 16-byte loads stay inside the row rounded up to 4 elements (score rows are padded to 16
+  // bytes; candidate rows qualify only when their length is a multiple of 4); other rows load
+  // element by element at clamped positions. Every load is unconditional so that all are in
+  // flight together.
+  const bool v4 = GATHER ? (((uintptr_t)ckeys & 15) == 0 && (Tc & 3) == 0) : vec;
+  // (two separate loops: merged, the compiler would split the 16-byte loads into single words)
+  if (Tc > 0 && v4) {
+    const int last4 = ((Tc + 3) & ~3) - 4;
+    if constexpr (GATHER) {
+      uint4 w[KPT / 4];
+#pragma unroll
+      for (int q = 0; q < KPT / 4; ++q) w[q] = *(const uint4*)(ckeys + min(4 * (tid + kThreads * q), last4));
+#pragma unroll
+      for (int q = 0; q < KPT / 4; ++q) pr[4 * q] = w[q].x, pr[4 * q + 1] = w[q].y, pr[4 * q + 2] = w[q].z, pr[4 * q + 3] = w[q].w;
+    } else {
+      float4 w[KPT / 4];
+#pragma unroll
+      for (int q = 0; q < KPT / 4; ++q) w[q] = *(const float4*)(src + min(4 * (tid + kThreads * q), last4));
+#pragma unroll
+      for (int q = 0; q < KPT / 4; ++q) pr[4 * q] = w[q].x, pr[4 * q + 1] = w[q].y, pr[4 * q + 2] = w[q].z, pr[4 * q + 3] = w[q].w;
+    }
+  } else if (Tc > 0) {
+#pragma unroll
+    for (int q = 0; q < KPT / 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = min(4 * (tid + kThreads * q) + e, Tc - 1);
+        if constexpr (GATHER) pr[4 * q + e] = ckeys[i];
+        else pr[4 * q + e] = src[i];
+      }
+  }
+  auto key_of = [&](int e) -> uint32_t {
+    if constexpr (GATHER) return pr[e];
+    else return float_key(pr[e]);
+  };
+#pragma unroll
+  for (int q = 0; q < KPT / 4; ++q) {
+    const int i = 4 * (tid + kThreads * q);
+    uint32_t v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = key_of(4 * q + e);
+      const bool in = i + e < Tc;
+      lmn = min(lmn, in ? v[e] : 0xffffffffu);
+      lmx = max(lmx, in ? v[e] : 0u);
+      if (thr) npass += (in && v[e] >= tkey) ? 1u : 0u;
+    }
+    if (i < Tc) *(uint4*)&stage[padded(i)] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    lmn = min(lmn, (uint32_t)__shfl_xor((int)lmn, o));
+    lmx = max(lmx, (uint32_t)__shfl_xor((int)lmx, o));
+  }
+  if (thr) npass = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(npass, lane), 63);
+  if (lane == 0) {
+    mm[wave] = lmn;
+    mm[kWaves + wave] = lmx;
+    mm[2 * kWaves + wave] = npass;
+  }
+  __syncthreads();  // also orders the histogram zeroing before the atomics below
+  uint32_t total_pass = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    lmn = min(lmn, mm[w]);
+    lmx = max(lmx, mm[kWaves + w]);
+    total_pass += mm[2 * kWaves + w];
+  }
+
+  // ---- the parts that need no ranking ----
+  if (thr) {
+    if (kp > 0) kp = (int)min((uint32_t)kp, total_pass);
+    for (int j = kp + wcount + tid; j < pad_to; j += kThreads) out[j] = -1;
+    if (tid == 0 && cnt_out) *cnt_out = kp + wcount;
+  }
+  for (int j = tid; j < wcount; j += kThreads) out[kp + j] = wstart + j;
+  auto map = [&](int i) -> int32_t {
+    if constexpr (GATHER) return cand[i];
+    else return obase + i;
+  };
+  if (kp <= 0) return;
+  if (kp >= Tc) {
+    for (int j = tid; j < Tc; j += kThreads) {
+      out[j] = map(j);
+      if (okeys) okeys[j] = stage[padded(j)];
+    }
     return;
   }
-  auto key_at = [&](int i) -> uint32_t {
-    if constexpr (IN_LDS) return keys[i];
-    else return float_key(src[i]);
-  };
+
+  // ---- 2. histogram of equal-width value bins over the range ----
+  // bin(k) = clamp(floor(value(k) * s + o), 0, kBins - 1) with s = kBins / (max - min) and
+  // o = -min * s: one fused multiply-add is monotone in the value, so a larger key never lands
+  // in a lower bin, and equal keys share a bin. A range that is empty or not finite
+  // (infinities, NaN) puts every key in bin 0. Positions past the row count in hist[kBins].
+  const float vmin = key_value(lmn), vmax = key_value(lmx);
+  const float span = __fsub_rn(vmax, vmin);
+  float scale = __fdiv_rn((float)kBins, span);
+  if (!(span > 0.f) || !isfinite(span) || !isfinite(scale)) scale = 0.f;
+  const float off = scale == 0.f ? 0.f : -__fmul_rn(vmin, scale);
+  uint32_t kb[KPT];
+#pragma unroll
+  for (int q = 0; q < KPT / 4; ++q) {
+    const int i = 4 * (tid + kThreads * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x;
+      if constexpr (GATHER) x = key_value(pr[4 * q + e]);
+      else x = pr[4 * q + e];
+      const float t = fminf(fmaxf(__fmaf_rn(x, scale, off), 0.f), (float)(kBins - 1));
+      kb[4 * q + e] = i + e < Tc ? (uint32_t)t : (uint32_t)kBins;
+      atomicAdd(&hist[kb[4 * q + e]], 1u);
+    }
+  }
+  __syncthreads();
+  find_bin(hist, (uint32_t)kp, scan, bcast);
+  const uint32_t bin1 = bcast[0];
+  const uint32_t c1 = bcast[2];                  // keys in bin1
+  uint32_t remaining = (uint32_t)kp - bcast[1];  // rank of tau inside bin1, >= 1
+  // (bcast is next written inside a find_bin, after barriers every thread passes after these
+  // reads; hist is free once find_bin returns)
+
+  uint32_t tau, take_eq;
+  if (c1 <= (uint32_t)kSmall) {
+    // ---- 3. gather bin1's keys (in any order) into hist, one counter update per wave; tau is
+    //      the one whose counts of larger and equal keys in bin1 bracket the rank left over ----
+    uint32_t* small = hist;
+    uint32_t hm = 0;  // register slots of this thread's keys in bin1 (slot 4q + e: position 4u + e)
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) hm |= (kb[e] == bin1 ? 1u : 0u) << e;
+    const uint32_t cnt = (uint32_t)__popc(hm);
+    const uint32_t incl = wave_incl_scan(cnt, lane);
+    const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (wtot) {
+      uint32_t got = 0;
+      if (lane == 63) got = atomicAdd(&nsmall, wtot);
+      uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)got, 63) + incl - cnt;
+      while (hm) {  // the keys are read back from the staging array by position
+        const int e = __builtin_ctz(hm);
+        hm &= hm - 1u;
+        small[at++] = stage[padded(4 * (tid + kThreads * (e >> 2)) + (e & 3))];
+      }
+    }
+    __syncthreads();
+    if (tid < (int)c1) {
+      const uint32_t x = small[tid];
+      uint32_t gt = 0, ge = 0;
+      for (int j = 0; j < (int)c1; j += 16) {  // j + 15 < kSmall + 16 <= kBins
+        uint4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = *(const uint4*)&small[j + 4 * q];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t vv[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool in = j + 4 * q + e < (int)c1;
+            gt += (in && vv[e] > x) ? 1u : 0u;
+            ge += (in && vv[e] >= x) ? 1u : 0u;
+          }
+        }
+      }
+      if (gt < remaining && remaining <= ge) {  // every holder of tau writes the same values
+        tsel[0] = x;
+        tsel[1] = remaining - gt;
+      }
+    }
+    __syncthreads();
+    tau = tsel[0];
+    take_eq = tsel[1];
+  } else {
+    // ---- 3'. crowded bin (heavy ties, or a range stretched by outliers): three key-bit digits ----
+    uint32_t prefix = 0;
+    remaining = (uint32_t)kp;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+      const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
+      const uint32_t pmask = pass == 0 ? 0u : pass == 1 ? 0xffe00000u : 0xfffffc00u;
+      for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < KPT; ++e) {
+        const uint32_t x = key_of(e);
+        if (kb[e] < (uint32_t)kBins && (x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      find_bin(hist, remaining, scan, bcast);
+      prefix |= bcast[0] << shift;
+      remaining -= bcast[1];
+      __syncthreads();
+    }
+    tau = prefix;
+    take_eq = remaining;  // >= 1
+  }
+
+  // ---- 4. ordered compaction over this thread's KPT consecutive keys (from t * KPT): its output
+  //      slots start at the number of selected keys before its first key (a block prefix sum of
+  //      its counts); the positions go to LDS in output order (over the staged keys, read for the
+  //      last time before the barriers of that prefix sum) and are written out with coalesced
+  //      stores ----
+  const int b0 = tid * KPT;
+  const int nv = min(max(Tc - b0, 0), KPT);  // valid keys of this thread
+  const uint32_t vmask = nv >= 32 ? 0xffffffffu : ((1u << nv) - 1u);
+  uint32_t fgt = 0, feq = 0;
+#pragma unroll
+  for (int c = 0; c < KPT / 4; ++c) {
+    const uint4 w = *(const uint4*)&stage[padded(b0 + 4 * c)];  // stays inside the staging array
+    const uint32_t kc[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      fgt |= (kc[e] > tau ? 1u : 0u) << (4 * c + e);
+      feq |= (kc[e] == tau ? 1u : 0u) << (4 * c + e);
+    }
+  }
+  fgt &= vmask;
+  feq &= vmask;
+  const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);  // each <= 32768
+  const uint32_t incl = wave_incl_scan(packed, lane);
+  uint32_t before, total;
+  block_prefix((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), scan, before, total);
+  const uint32_t excl = before + incl - packed;
+  uint32_t ngt = excl & 0xffffu, neq = excl >> 16;
+  int32_t* obuf = (int32_t*)stage;
+  uint32_t m = fgt | feq;
+  while (m) {
+    const int e = __builtin_ctz(m);
+    m &= m - 1u;
+    if ((fgt >> e) & 1u) {
+      obuf[ngt + min(neq, take_eq)] = b0 + e;
+      ++ngt;
+    } else {
+      if (neq < take_eq) obuf[ngt + neq] = b0 + e;
+      ++neq;
+    }
+  }
+  __syncthreads();
+  batched_copy<4>(kp, tid, kThreads, [&](int j) { return obuf[j]; }, [&](int j, int32_t i) {
+    out[j] = map(i);
+    if (okeys) okeys[j] = GATHER ? ckeys[i] : float_key(src[i]);
+  });
+}
+
+// The selection of a row read from global memory (rows beyond the LDS staging array that are not
+// split into slices): keys float_key(src[i]), positions i, otherwise as topk_staged. Key bits
+// [31:21] give the threshold bin b1; every position in b1 or above is listed in index order
+// (ballot ranks), key bits [20:10] and [9:0] of tau come from histograms over the list, and the
+// list filtered is the selection. A list that would not fit resolves the digits over the row.
+__device__ __forceinline__ void topk_global(const float* __restrict__ src, int n, int kp, int32_t* __restrict__ out,
+                                            int wcount, int wstart, bool thr, uint32_t tkey,
+                                            int32_t* __restrict__ cnt_out, int pad_to) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  __shared__ int32_t list[kList];
+  __shared__ __attribute__((aligned(16))) uint32_t scan[kWaves];
+  __shared__ uint32_t bcast[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Tc = n;
+  auto key_at = [&](int i) -> uint32_t { return float_key(src[i]); };
+  kp = topk_prologue(key_at, [](int i) -> int32_t { return i; }, Tc, kp, out, wcount, wstart, thr, tkey, cnt_out,
+                     pad_to, scan);
+  if (kp == 0) return;
   // Keys of this wave for the chunk starting at `base`: wave w owns [base + w*1024, +1024), in
-  // 16 slices of 64 (lane l reads the l-th key of each slice, so LDS reads are conflict-free).
-  // Reads are unconditional (an LDS row never exceeds the staging array; global indices clamp)
-  // so that all 16 are in flight before the first use.
+  // 16 slices of 64 (lane l reads the l-th key of each slice). Reads are unconditional (indices
+  // clamp) so that all 16 are in flight before the first use.
   constexpr int kChunk = kThreads * kIPT;
   uint32_t kk[kIPT];
   auto load_keys = [&](int base) {
     const int w0 = base + wave * 64 * kIPT;
 #pragma unroll
-    for (int j = 0; j < kIPT; ++j) {
-      const int i = w0 + j * 64 + lane;
-      if constexpr (IN_LDS) kk[j] = keys[i];
-      else kk[j] = float_key(src[min(i, Tc - 1)]);
-    }
-  };
-  // Exclusive prefix of a per-wave count over the waves, and the block total.
-  auto wave_prefix = [&](uint32_t mine, uint32_t& before, uint32_t& total) {
-    if (lane == 0) scan[wave] = mine;
-    __syncthreads();
-    before = 0;
-    total = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t v = scan[w];
-      before += (w < wave) ? v : 0u;
-      total += v;
-    }
-    __syncthreads();
+    for (int j = 0; j < kIPT; ++j) kk[j] = key_at(min(w0 + j * 64 + lane, Tc - 1));
   };
   const unsigned long long lt_mask = (1ull << lane) - 1ull;
 
-  // ---- 1. keys to LDS and the digit-1 histogram (key bits [31:21]) in one pass ----
+  // ---- 1. the digit-1 histogram (key bits [31:21]) ----
   for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
   __syncthreads();
-  if constexpr (GATHER) {
-    // Candidate keys lie in a narrow range (each is among the largest of its slice), so their
-    // top 11 bits would fall in a few bins (long bin searches, contended histogram atomics).
-    // They are re-encoded as (key - min) << clz(max - min): strictly increasing on the range,
-    // so order and ties are unchanged, and the range fills the top key bits.
-    uint32_t kmn = 0xffffffffu, kmx = 0u;
-    batched_copy<kLdsKeys / kThreads>(Tc, tid, kThreads, [&](int i) { return ckeys[i]; },
-                                      [&](int i, uint32_t k) {
-                                        keys[i] = k;
-                                        kmn = min(kmn, k);
-                                        kmx = max(kmx, k);
-                                      });
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o));
-      kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o));
-    }
-    if (lane == 0) {
-      mm[wave] = kmn;
-      mm[kWaves + wave] = kmx;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      kmn = min(kmn, mm[w]);
-      kmx = max(kmx, mm[kWaves + w]);
-    }
-    const uint32_t range = kmx - kmn;
-    const int ls = range ? __clz(range) : 0;
-    for (int i = tid; i < Tc; i += kThreads) {
-      const uint32_t k = (keys[i] - kmn) << ls;
-      keys[i] = k;
-      atomicAdd(&hist[k >> 21], 1u);
-    }
-  } else if constexpr (IN_LDS) {
-    if (vec) {  // 16-byte loads (rows start on 16-byte boundaries); keys past Tc are never used
-      const float4* s4 = (const float4*)src;
-      batched_copy<kLdsKeys / 4 / kThreads>((Tc + 3) / 4, tid, kThreads, [&](int u) { return s4[u]; },
-                                            [&](int u, const float4& v) {
-                                              const uint32_t k0 = float_key(v.x), k1 = float_key(v.y),
-                                                             k2 = float_key(v.z), k3 = float_key(v.w);
-                                              *(uint4*)&keys[4 * u] = make_uint4(k0, k1, k2, k3);
-                                              atomicAdd(&hist[k0 >> 21], 1u);
-                                              if (4 * u + 1 < Tc) atomicAdd(&hist[k1 >> 21], 1u);
-                                              if (4 * u + 2 < Tc) atomicAdd(&hist[k2 >> 21], 1u);
-                                              if (4 * u + 3 < Tc) atomicAdd(&hist[k3 >> 21], 1u);
-                                            });
-    } else {
-      batched_copy<kLdsKeys / kThreads>(Tc, tid, kThreads, [&](int i) { return src[i]; },
-                                        [&](int i, float v) {
-                                          const uint32_t k = float_key(v);
-                                          keys[i] = k;
-                                          atomicAdd(&hist[k >> 21], 1u);
-                                        });
-    }
-  } else {
-    batched_copy<16>(Tc, tid, kThreads, [&](int i) { return src[i]; },
-                     [&](int, float v) { atomicAdd(&hist[float_key(v) >> 21], 1u); });
-  }
+  batched_copy<16>(Tc, tid, kThreads, [&](int i) { return src[i]; },
+                   [&](int, float v) { atomicAdd(&hist[float_key(v) >> 21], 1u); });
   __syncthreads();
   find_bin(hist, (uint32_t)kp, scan, bcast);
   const uint32_t bin1 = bcast[0];
   const uint32_t above = bcast[1];            // keys in bins above bin1
   const uint32_t nl = above + bcast[2];       // keys in bin1 or above
   uint32_t remaining = (uint32_t)kp - above;  // rank of tau inside bin1, >= 1
-  // (bcast is next written inside a find_bin, after barriers every thread passes after these
-  // reads; hist is free: the zeroing below is ordered before the next atomics by barriers)
 
-  if (nl <= (uint32_t)LIST) {
-    // ---- 2. list every position whose key is in bin1 or above, in index order; the same pass
-    //      builds the histogram of key bits [20:10] over bin1's keys ----
+  uint32_t tau, take_eq;
+  if (nl <= (uint32_t)kList) {
+    // ---- 2. list every position whose key is in bin1 or above, in index order ----
     for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
     const uint32_t lo = bin1 << 21;
     uint32_t run = 0;
-    if constexpr (IN_LDS) {
-      // each thread tests 16 consecutive keys (four 16-byte reads in a lane-dependent order, so
-      // that the 8 lanes sharing an LDS bank row hit 8 different 16-byte slots), keeps a 16-bit
-      // hit mask, and writes its hits in index order at its prefix-sum position
-      for (int base = 0; base < Tc; base += kChunk) {
-        const int b0 = base + tid * 16;
-        uint32_t hm = 0;
+    for (int base = 0; base < Tc; base += kChunk) {
+      load_keys(base);
+      const int w0 = base + wave * 64 * kIPT;
+      uint32_t cnt = 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int cc = ((lane >> 1) + c) & 3;
-          const uint4 k4 = *(const uint4*)&keys[b0 + cc * 4];
-          hm |= ((k4.x >= lo ? 1u : 0u) | (k4.y >= lo ? 2u : 0u) | (k4.z >= lo ? 4u : 0u) |
-                 (k4.w >= lo ? 8u : 0u)) << (cc * 4);
-        }
-        const int nv = min(max(Tc - b0, 0), 16);
-        hm &= nv >= 16 ? 0xffffu : ((1u << nv) - 1u);
-        const uint32_t cnt = (uint32_t)__popc(hm);
-        const uint32_t incl = wave_incl_scan(cnt, lane);
-        uint32_t before, total;
-        wave_prefix((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), before, total);
-        uint32_t at = run + before + incl - cnt;
-        while (hm) {
-          list[at++] = (uint16_t)(b0 + __builtin_ctz(hm));
-          hm &= hm - 1u;
-        }
-        run += total;
+      for (int j = 0; j < kIPT; ++j) cnt += (uint32_t)__popcll(__ballot(w0 + j * 64 + lane < Tc && kk[j] >= lo));
+      uint32_t before, total;
+      block_prefix(cnt, scan, before, total);
+      uint32_t at = run + before;
+      // the same tests as the count pass, recomputed: keeping its 16 ballots live across the
+      // barrier would spill scalar registers (the empty asm hides the equality from the
+      // compiler)
+      uint32_t lo_w = lo;
+      int tc_w = Tc;
+      asm volatile("" : "+v"(lo_w), "+v"(tc_w));
+#pragma unroll
+      for (int j = 0; j < kIPT; ++j) {
+        const int i = w0 + j * 64 + lane;
+        const bool hit = i < tc_w && kk[j] >= lo_w;
+        const unsigned long long m = __ballot(hit);
+        if (hit) list[at + (uint32_t)__popcll(m & lt_mask)] = i;
+        at += (uint32_t)__popcll(m);
       }
-    } else {
-      for (int base = 0; base < Tc; base += kChunk) {
-        load_keys(base);
-        const int w0 = base + wave * 64 * kIPT;
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int j = 0; j < kIPT; ++j)
-          cnt += (uint32_t)__popcll(__ballot(w0 + j * 64 + lane < Tc && kk[j] >= lo));
-        uint32_t before, total;
-        wave_prefix(cnt, before, total);
-        uint32_t at = run + before;
-        // the same tests as the count pass, recomputed: keeping its 16 ballots live across the
-        // barrier would spill scalar registers (the empty asm hides the equality from the
-        // compiler)
-        uint32_t lo_w = lo;
-        int tc_w = Tc;
-        asm volatile("" : "+v"(lo_w), "+v"(tc_w));
-#pragma unroll
-        for (int j = 0; j < kIPT; ++j) {
-          const int i = w0 + j * 64 + lane;
-          const bool hit = i < tc_w && kk[j] >= lo_w;
-          const unsigned long long m = __ballot(hit);
-          if (hit) list[at + (uint32_t)__popcll(m & lt_mask)] = i;
-          at += (uint32_t)__popcll(m);
-        }
-        run += total;
-      }
+      run += total;
     }
     __syncthreads();
-    // histogram of key bits [20:10] over the listed keys of bin1
+    // ---- key bits [20:10] over the listed keys of bin1, then [9:0] over those that match ----
     for (int u = tid; u < (int)nl; u += kThreads) {
       const uint32_t k = key_at(list[u]);
       if ((k >> 21) == bin1) atomicAdd(&hist[(k >> 10) & 0x7ffu], 1u);
     }
     __syncthreads();
-    // ---- key bits [20:10], then [9:0] over the list's keys that match so far ----
     find_bin(hist, remaining, scan, bcast);
     uint32_t prefix = lo | (bcast[0] << 10);
     remaining -= bcast[1];
     for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
     __syncthreads();
     {
-      constexpr int LU = (LIST + kThreads - 1) / kThreads;
+      constexpr int LU = kList / kThreads;
       int li[LU];
 #pragma unroll
       for (int u = 0; u < LU; ++u) li[u] = list[min(tid + u * kThreads, (int)nl - 1)];
@@ -340,25 +525,20 @@ __device__ __forceinline__ void topk_body(const float* __restrict__ src, const i
     }
     __syncthreads();
     find_bin(hist, remaining, scan, bcast);
-    const uint32_t tau = prefix | bcast[0], take_eq = remaining - bcast[1];
+    tau = prefix | bcast[0];
+    take_eq = remaining - bcast[1];
     // ---- 3. the selection is the list filtered, in list (index) order ----
-    constexpr int FPT = (LIST + kThreads - 1) / kThreads;  // list entries per thread: one pass
+    constexpr int FPT = kList / kThreads;  // list entries per thread: one pass
     uint32_t run_gt = 0, run_eq = 0;
     for (int base = 0; base < (int)nl; base += kThreads * FPT) {
       const int j0 = base + tid * FPT;
       uint32_t fgt = 0, feq = 0;
       int idx[FPT];
-      uint32_t kv[FPT];
 #pragma unroll
       for (int e = 0; e < FPT; ++e) idx[e] = list[min(j0 + e, (int)nl - 1)];
-      // output values requested before the block scan, so that their loads (candidate positions)
-      // are in flight while it runs
-      int32_t ov[FPT];
-#pragma unroll
-      for (int e = 0; e < FPT; ++e) ov[e] = map(idx[e]);
 #pragma unroll
       for (int e = 0; e < FPT; ++e) {
-        const uint32_t k = kv[e] = key_at(idx[e]);
+        const uint32_t k = key_at(idx[e]);
         const bool valid = j0 + e < (int)nl;
         fgt |= (uint32_t)(valid && k > tau) << e;
         feq |= (uint32_t)(valid && k == tau) << e;
@@ -366,20 +546,16 @@ __device__ __forceinline__ void topk_body(const float* __restrict__ src, const i
       const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);
       const uint32_t incl = wave_incl_scan(packed, lane);
       uint32_t before, total;
-      wave_prefix((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), before, total);  // wave total
+      block_prefix((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), scan, before, total);
       const uint32_t excl = before + incl - packed;
       uint32_t ngt = run_gt + (excl & 0xffffu), neq = run_eq + (excl >> 16);
 #pragma unroll
       for (int e = 0; e < FPT; ++e) {
         if ((fgt >> e) & 1u) {
-          out[ngt + min(neq, take_eq)] = ov[e];
-          if (okeys) okeys[ngt + min(neq, take_eq)] = kv[e];
+          out[ngt + min(neq, take_eq)] = idx[e];
           ++ngt;
         } else if ((feq >> e) & 1u) {
-          if (neq < take_eq) {
-            out[ngt + neq] = ov[e];
-            if (okeys) okeys[ngt + neq] = kv[e];
-          }
+          if (neq < take_eq) out[ngt + neq] = idx[e];
           ++neq;
         }
       }
@@ -407,8 +583,8 @@ __device__ __forceinline__ void topk_body(const float* __restrict__ src, const i
     remaining -= bcast[1];
     __syncthreads();
   }
-  const uint32_t tau = prefix;
-  const uint32_t take_eq = remaining;  // >= 1
+  tau = prefix;
+  take_eq = remaining;  // >= 1
   // ordered compaction over the whole row: ranks inside a wave's run from ballots, the runs'
   // packed (gt, eq) totals (each at most 16384, so 16 bits apiece) exchanged per chunk
   uint32_t run_gt = 0, run_eq = 0;
@@ -423,7 +599,7 @@ __device__ __forceinline__ void topk_body(const float* __restrict__ src, const i
       weq += (uint32_t)__popcll(__ballot(valid && kk[j] == tau));
     }
     uint32_t before, total;
-    wave_prefix(wgt | (weq << 16), before, total);
+    block_prefix(wgt | (weq << 16), scan, before, total);
     uint32_t ngt = run_gt + (before & 0xffffu), neq = run_eq + (before >> 16);
 #pragma unroll
     for (int j = 0; j < kIPT; ++j) {
@@ -433,13 +609,8 @@ __device__ __forceinline__ void topk_body(const float* __restrict__ src, const i
       const unsigned long long mg = __ballot(gt), me = __ballot(eq);
       const uint32_t bg = ngt + (uint32_t)__popcll(mg & lt_mask);  // gt keys before i
       const uint32_t be = neq + (uint32_t)__popcll(me & lt_mask);  // eq keys before i
-      if (gt) {
-        out[bg + min(be, take_eq)] = map(i);
-        if (okeys) okeys[bg + min(be, take_eq)] = kk[j];
-      } else if (eq && be < take_eq) {
-        out[bg + be] = map(i);
-        if (okeys) okeys[bg + be] = kk[j];
-      }
+      if (gt) out[bg + min(be, take_eq)] = i;
+      else if (eq && be < take_eq) out[bg + be] = i;
       ngt += (uint32_t)__popcll(mg);
       neq += (uint32_t)__popcll(me);
     }
@@ -448,22 +619,29 @@ __device__ __forceinline__ void topk_body(const float* __restrict__ src, const i
   }
 }
 
-template <bool IN_LDS>
+// One row per workgroup: rows of up to kThreads * KPT keys in registers (KPT > 0), longer rows
+// from global memory (KPT == 0).
+template <int KPT>
 __global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __restrict__ S,
                                                                int32_t* __restrict__ sel, int Tc,
                                                                int ldS, int kp, int ctx, int n_sel,
                                                                bool vec, bool thr, uint32_t tkey,
                                                                int32_t* __restrict__ cnt) {
   const int row = blockIdx.x;
-  topk_body<IN_LDS, false>(S + (size_t)row * ldS, nullptr, nullptr, Tc, kp, sel + (size_t)row * n_sel,
-                           nullptr, 0, ctx - Tc, Tc, vec, thr, tkey, cnt ? cnt + row : nullptr, n_sel);
+  if constexpr (KPT > 0)
+    topk_rows<KPT, false>(S + (size_t)row * ldS, nullptr, nullptr, Tc, kp, sel + (size_t)row * n_sel, nullptr, 0,
+                          ctx - Tc, Tc, vec, thr, tkey, cnt ? cnt + row : nullptr, n_sel);
+  else
+    topk_global(S + (size_t)row * ldS, Tc, kp, sel + (size_t)row * n_sel, ctx - Tc, Tc, thr, tkey,
+                cnt ? cnt + row : nullptr, n_sel);
 }
 
-// Rows longer than the LDS staging array: one workgroup per (row, slice of slen keys) keeps the
-// kp largest of its slice (ties to the lowest position) as candidates, in ascending position
+// Rows longer than the register-resident limit: one workgroup per (row, slice of slen keys) keeps
+// the kp largest of its slice (ties to the lowest position) as candidates, in ascending position
 // order, with their keys. Every element of the row's top kp is among its slice's top kp, with the
 // lowest-index ties of the row's threshold key included, so the row's selection over the
 // candidates (which are in ascending position order across slices) is exact.
+template <int KPT>
 __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __restrict__ S,
                                                               int32_t* __restrict__ cand,
                                                               uint32_t* __restrict__ ckeys, int Tc,
@@ -472,10 +650,11 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __res
   const int row = blockIdx.x / ns, s = blockIdx.x % ns;
   const int s0 = s * slen, n = min(slen, Tc - s0);
   const size_t o = ((size_t)row * ns + s) * kp;
-  topk_body<true, false>(S + (size_t)row * ldS + s0, nullptr, nullptr, n, kp, cand + o, ckeys + o, s0, 0, 0,
-                         vec, false, 0u, nullptr, 0);
+  topk_rows<KPT, false>(S + (size_t)row * ldS + s0, nullptr, nullptr, n, kp, cand + o, ckeys + o, s0, 0, 0, vec,
+                        false, 0u, nullptr, 0);
 }
 
+template <int KPT>
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const int32_t* __restrict__ cand,
                                                               const uint32_t* __restrict__ ckeys,
                                                               int32_t* __restrict__ sel, int Tc, int kp,
@@ -483,9 +662,12 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const int32_t* __r
                                                               uint32_t tkey, int32_t* __restrict__ cnt) {
   const int row = blockIdx.x;
   const size_t o = (size_t)row * ns * kp;
-  topk_body<true, true>(nullptr, cand + o, ckeys + o, ns * kp, kp, sel + (size_t)row * n_sel, nullptr, 0,
-                        ctx - Tc, Tc, false, thr, tkey, cnt ? cnt + row : nullptr, n_sel);
+  topk_rows<KPT, true>(nullptr, cand + o, ckeys + o, ns * kp, kp, sel + (size_t)row * n_sel, nullptr, 0, ctx - Tc,
+                       Tc, false, thr, tkey, cnt ? cnt + row : nullptr, n_sel);
 }
+
+// Keys per thread for a register-resident row of n keys (n <= kLdsKeys).
+int keys_per_thread(int n) { return n <= 4 * kThreads ? 4 : n <= 8 * kThreads ? 8 : n <= 16 * kThreads ? 16 : 32; }
 
 }  // namespace
 
@@ -518,15 +700,30 @@ hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, i
   const bool vec = (ldS & 3) == 0 && ((uintptr_t)S & 15) == 0;
   int slen = 0;
   const int ns = cand ? topk_slices(Tc, kp, &slen) : 0;
+#define SALS_KPT_SWITCH(N, CALL) \
+  switch (keys_per_thread(N)) {    \
+    case 4: CALL(4); break;        \
+    case 8: CALL(8); break;        \
+    case 16: CALL(16); break;      \
+    default: CALL(32); break;      \
+  }
   if (Tc <= kLdsKeys) {
-    topk_window_kernel<true><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt);
+#define SALS_ROWS(K) topk_window_kernel<K><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt)
+    SALS_KPT_SWITCH(Tc, SALS_ROWS)
+#undef SALS_ROWS
   } else if (ns > 0) {
     uint32_t* ckeys = (uint32_t*)(cand + (size_t)rows * ns * kp);
-    topk_slice_kernel<<<rows * ns, kThreads, 0, st>>>(S, cand, ckeys, Tc, ldS, kp, slen, ns, vec);
-    topk_merge_kernel<<<rows, kThreads, 0, st>>>(cand, ckeys, sel, Tc, kp, ns, ctx, n_sel, thr, tkey, cnt);
+#define SALS_SLICE(K) topk_slice_kernel<K><<<rows * ns, kThreads, 0, st>>>(S, cand, ckeys, Tc, ldS, kp, slen, ns, vec)
+    SALS_KPT_SWITCH(slen, SALS_SLICE)
+#undef SALS_SLICE
+#define SALS_MERGE(K) \
+  topk_merge_kernel<K><<<rows, kThreads, 0, st>>>(cand, ckeys, sel, Tc, kp, ns, ctx, n_sel, thr, tkey, cnt)
+    SALS_KPT_SWITCH(ns * kp, SALS_MERGE)
+#undef SALS_MERGE
   } else {
-    topk_window_kernel<false><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt);
+    topk_window_kernel<0><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt);
   }
+#undef SALS_KPT_SWITCH
   return hipGetLastError();
 }
 
