@@ -147,10 +147,13 @@ def algorithmic(cfg, ctx):
         stage_flops["select_attend"] = k_rebuild + logits
         stage_flops["value"] = value_side
     else:
-        stage_bytes["select_attend"] = sel_rows + p_bytes + sel_idx + q_in + o_out
-        stage_bytes["combine"] = 0
-        stage_flops["select_attend"] = k_rebuild + value_side + logits
-        stage_flops["combine"] = 0
+        # the gather kernel ends with latent sums z = p^T L_v,sel per split; the split merge
+        # applies P_v once per head and writes the output (the workloads here all have several
+        # splits; with one split both would run in the gather kernel)
+        stage_bytes["select_attend"] = sel_rows + D * r * s + sel_idx + q_in
+        stage_bytes["combine"] = D * r * s + o_out
+        stage_flops["select_attend"] = k_rebuild + 2 * B * Hq * n_sel * r + logits
+        stage_flops["combine"] = 2 * B * Hq * d * r
     return dict(
         lk_read=lk_read, sel_rows=sel_rows, p_bytes=p_bytes, compulsory=lk_read + sel_rows + p_bytes,
         k_rebuild_flops=k_rebuild, n_sel=n_sel, Tc=Tc, stage_bytes=stage_bytes, stage_flops=stage_flops,
@@ -688,8 +691,9 @@ def cpu_baseline(case, budget_s=10.0, tiny=None):
 def summary(cfg, r, label, hbm_measured=None):
     rl, alg = roofline_for(cfg, r["case"]["ctx"], r["stage_us"], label)
     gbps = alg["compulsory"] / (r["us"] * 1e-6) / 1e9
-    # scoring + attention: the latent scan and the rebuild/attention stage over their summed time
-    sa = ("latent_score", "select_attend") + (("value",) if "value" in r["stage_us"] else ())
+    # scoring + attention: the latent scan and the rebuild/attention stages (the value kernels, or
+    # the split merge that applies P_v) over their summed time
+    sa = ("latent_score", "select_attend") + (("value",) if "value" in r["stage_us"] else ("combine",))
     sa_bytes = sum(alg["stage_bytes"][k] for k in sa)
     sa_us = sum(r["stage_us"][k] for k in sa)
     return dict(
