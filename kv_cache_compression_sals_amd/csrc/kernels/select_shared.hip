@@ -39,6 +39,7 @@ constexpr int kAIW = (kAI + kWV - 1) / kWV;  // per wave, padded: 5
 constexpr int kBIW = kRows / 8 / kWV;        // B (P rows) per wave: 4
 constexpr int kMaxQH = 4;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
 // LDS layout (bytes)
 constexpr int kABytes = kTOK * 128;
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ Lk, const uint16_t* __restrict__ Pk,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, float* __restrict__ pbuf,
     float* __restrict__ pstat, int H_q, int H_kv, int G, int ctx_cap, int ctx, int n_sel, int n_splits,
-    float rope_base) {
+    double rope_r) {
   constexpr int NKC = R / kKC;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   int32_t* pos = (int32_t*)(smem + kOffPos);
@@ -108,33 +109,13 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
   }
   const size_t brow = (size_t)b * ctx_cap;
 
-  // ---- prologue: positions, RoPE frequencies, rotated and scaled queries ----
-  if (tid < kDH / 2) ftab[tid] = pow((double)rope_base, -2.0 * tid / kDH) / kTwoPi;
-  {
-    const int32_t* selrow = sel + ((size_t)b * G + s) * n_sel + j0;
-    for (int j = tid; j < kTOK; j += kNT) pos[j] = selrow[min(j, n_tok - 1)];
-  }
-  __syncthreads();
-  const float qscale = 1.0f / sqrtf((float)kDH);
-  for (int e = tid; e < kNH * nqh * (kDH / 2); e += kNT) {
-    const int i = e % (kDH / 2), hh = (e / (kDH / 2)) % nqh, h2 = e / (nqh * (kDH / 2));
-    const uint16_t* qp = q + ((size_t)b * H_q + (size_t)(g0 + h2) * nqh + hh) * kDH;
-    const float x1 = bf16_bits_to_f32(qp[i]), x2 = bf16_bits_to_f32(qp[i + kDH / 2]);
-    float sn, cs;
-    rope_sincos(ctx - 1, ftab[i], &sn, &cs);
-    float* dst = qs + (h2 * kMaxQH + hh) * kDH;
-    dst[i] = (x1 * cs - x2 * sn) * qscale;
-    dst[i + kDH / 2] = (x2 * cs + x1 * sn) * qscale;
-  }
-
   // ---- DMA of one chunk of both operands (rank elements kc*64 .. +64) into buffer bsel ----
   // A instruction j: tile rows 8j + lane/8, piece (lane%8) ^ row; instructions past the tile
   // (padding, so that every wave issues the same number) reload a valid row into a dummy area.
   // B instruction j: P_k rows g0*d + 8j + lane/8 (the two heads' rows are consecutive).
   const int drow = lane >> 3, dx = lane & 7;
-  auto issue_chunk = [&](int kc, int bsel) {
+  auto issue_a = [&](int kc, int bsel) {
     unsigned char* abuf = smem + kOffA + bsel * kABytes;
-    unsigned char* bbuf = smem + kOffB + bsel * kBBytes;
 #pragma unroll
     for (int u = 0; u < kAIW; ++u) {
       const int j = wave + kWV * u;
@@ -143,6 +124,9 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
       const uint16_t* g = Lk + (brow + pos[rr]) * R + kc * kKC + c * 8;
       dma16(g, j < kAI ? abuf + j * 1024 : smem + kOffDummy);
     }
+  };
+  auto issue_b = [&](int kc, int bsel) {
+    unsigned char* bbuf = smem + kOffB + bsel * kBBytes;
 #pragma unroll
     for (int u = 0; u < kBIW; ++u) {
       const int j = wave + kWV * u;
@@ -152,6 +136,48 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
       dma16(g, bbuf + j * 1024);
     }
   };
+  // ---- prologue: positions, RoPE frequencies, rotated and scaled queries ----
+  // The positions and this thread's query pair are loaded together, and every LDS write of the
+  // prologue happens before the first copy is issued (the compiler makes an LDS write wait for
+  // every global->LDS copy in flight). The first chunk's P_k rows (independent of the selection)
+  // are then requested, its token rows as soon as the positions are visible to every wave.
+  const int32_t* selrow = sel + ((size_t)b * G + s) * n_sel + j0;
+  static_assert(kTOK <= kNT && kNH * kMaxQH * (kDH / 2) <= kNT, "one position and one query pair per thread");
+  int pv = 0;
+  if (tid < kTOK) pv = selrow[min(tid, n_tok - 1)];
+  const int qi = lane, qhh = wave % nqh, qh2 = wave / nqh;  // this thread's query pair (i, i + d/2)
+  const bool qlive = tid < kNH * nqh * (kDH / 2);
+  float x1 = 0.f, x2 = 0.f;
+  if (qlive) {
+    const uint16_t* qp = q + ((size_t)b * H_q + (size_t)(g0 + qh2) * nqh + qhh) * kDH;
+    x1 = bf16_bits_to_f32(qp[qi]);
+    x2 = bf16_bits_to_f32(qp[qi + kDH / 2]);
+  }
+  // theta_i / (2 pi) = rope_r^i / (2 pi) with rope_r = base^(-2/d) from the host: six fp64
+  // squarings and products (relative error ~1e-15) instead of a pow per thread
+  double frq = 1.0;
+  {
+    double bb = rope_r;
+#pragma unroll
+    for (int t = 0; t < 6; ++t) {
+      if ((lane >> t) & 1) frq *= bb;
+      bb *= bb;
+    }
+    frq *= kInvTwoPi;
+  }
+  if (tid < kDH / 2) ftab[tid] = frq;
+  if (tid < kTOK) pos[tid] = pv;
+  if (qlive) {
+    const float qscale = 1.0f / sqrtf((float)kDH);
+    float sn, cs;
+    rope_sincos(ctx - 1, frq, &sn, &cs);
+    float* dst = qs + (qh2 * kMaxQH + qhh) * kDH;
+    dst[qi] = (x1 * cs - x2 * sn) * qscale;
+    dst[qi + kDH / 2] = (x2 * cs + x1 * sn) * qscale;
+  }
+  issue_b(0, 0);
+  lds_barrier();  // pos visible to every wave; the copies stay in flight
+  issue_a(0, 0);
 
   f32x4 acc[kTTW][4];
 #pragma unroll
@@ -163,15 +189,16 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
 #pragma unroll
   for (int lb = 0; lb < 4; ++lb) brw[lb] = (lb & 1) * kDH + (cg + (lb >> 1) * 4) * 16 + n16;
 
-  __syncthreads();  // pos visible to every wave before the first DMA addresses are formed
-  issue_chunk(0, 0);
   for (int kc = 0; kc < NKC; ++kc) {
     // this wave's copies of chunk kc have landed; after the barrier every wave's have, and every
     // wave has finished multiplying chunk kc - 1, whose buffer the next copies overwrite
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (kc + 1 < NKC) issue_chunk(kc + 1, (kc + 1) & 1);
+    if (kc + 1 < NKC) {
+      issue_a(kc + 1, (kc + 1) & 1);
+      issue_b(kc + 1, (kc + 1) & 1);
+    }
     const unsigned char* abuf = smem + kOffA + (kc & 1) * kABytes;
     const unsigned char* bbuf = smem + kOffB + (kc & 1) * kBBytes;
 #pragma unroll
@@ -295,16 +322,17 @@ hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, con
                               hipStream_t st, hipEvent_t t_start, hipEvent_t t_stop) {
   const dim3 grid(n_splits * (H_kv / kNH) * B);
   const int nqh = H_q / H_kv;
+  const double rope_r = pow((double)rope_base, -2.0 / kDH);  // theta_i = rope_r^i
   const auto* qq = (const uint16_t*)q;
   const auto* lk = (const uint16_t*)Lk;
   const auto* pk = (const uint16_t*)Pk;
 #define SALS_SK(RR, QQ)                                                                              \
   if (t_start)                                                                                       \
     hipExtLaunchKernelGGL(shared_keys_kernel<RR, QQ>, grid, dim3(kNT), 0, st, t_start, t_stop, 0, qq, lk, \
-                          pk, sel, cnt, pbuf, pstat, H_q, H_kv, G, ctx_cap, ctx, n_sel, n_splits, rope_base);  \
+                          pk, sel, cnt, pbuf, pstat, H_q, H_kv, G, ctx_cap, ctx, n_sel, n_splits, rope_r);  \
   else                                                                                               \
     shared_keys_kernel<RR, QQ><<<grid, kNT, 0, st>>>(qq, lk, pk, sel, cnt, pbuf, pstat, H_q, H_kv, G,       \
-                                                     ctx_cap, ctx, n_sel, n_splits, rope_base)
+                                                     ctx_cap, ctx, n_sel, n_splits, rope_r)
 #define SALS_SK_R(RR) \
   if (nqh <= 1) {     \
     SALS_SK(RR, 1);   \
