@@ -224,6 +224,51 @@ def test_compact_from_importance_matches_oracle(B, H_kv, d, ctx, cap, k_keep, dt
     assert np.array_equal(raw(Kc), ref["Kc"]) and np.array_equal(raw(Vc), ref["Vc"])
 
 
+def _importance_rows(kind, rows, ctx, rs):
+    """Importance rows shaped to drive each path of the per-row selection: spread values (a
+    small threshold bin), a range stretched by one huge value or by infinities (every key in a
+    few value bins: the key-bit fallback), a narrow positive range with ties, two far clusters,
+    subnormals and constant rows."""
+    x = rs.standard_normal((rows, ctx)).astype(np.float32)
+    if kind == "outlier":
+        x[:, rs.integers(0, ctx, rows)] = np.float32(1e30)
+    elif kind == "inf":
+        x[:, ::97] = np.inf
+        x[:, 5::89] = -np.inf
+    elif kind == "narrow":
+        x = (np.float32(1.0) + np.float32(2.0 ** -20) * np.round(x * 8)).astype(np.float32)
+    elif kind == "clusters":
+        x = np.where(rs.random((rows, ctx)) < 0.5, x * 1e-3, 1000 + x * 1e-3).astype(np.float32)
+    elif kind == "subnormal":
+        x = (x * np.float32(1e-39)).astype(np.float32)
+    elif kind == "constant":
+        x[:] = np.float32(-2.5)
+    return x
+
+
+IMP_KINDS = ["gauss", "outlier", "inf", "narrow", "clusters", "subnormal", "constant"]
+
+
+@pytest.mark.parametrize("ctx", [4000, 16384, 32768])
+@pytest.mark.parametrize("kind", IMP_KINDS)
+def test_compact_from_importance_value_distributions(kind, ctx):
+    """The kept sets are exact (ties to the lowest position) for every value distribution, at row
+    lengths of 4, 16 and 32 keys per thread, for several k."""
+    print(f"from_importance kind={kind} ctx={ctx}", flush=True)
+    rs = np.random.default_rng(ctx * 31 + IMP_KINDS.index(kind))
+    H_kv, d = 2, 64
+    imp = _importance_rows(kind, H_kv, ctx, rs).reshape(1, H_kv, ctx)
+    K = rs.standard_normal((1, H_kv, ctx, d)).astype(np.float32)
+    V = rs.standard_normal((1, H_kv, ctx, d)).astype(np.float32)
+    Kd, Vd, Id = torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), torch.from_numpy(imp).cuda()
+    for k_keep in (1, 37, ctx // 10, ctx // 2 + 3, ctx - 1):
+        Kc, Vc, kept = sals.kv_compact_from_importance(Kd, Vd, Id, k_keep=k_keep)
+        torch.cuda.synchronize()
+        ref = oracle.compact_from_importance(K, V, imp, k_keep=k_keep)
+        assert np.array_equal(kept.cpu().numpy(), ref["kept"]), (kind, ctx, k_keep)
+        assert np.array_equal(Kc.cpu().numpy(), ref["Kc"]), (kind, ctx, k_keep)
+
+
 def test_compact_higher_layer_from_lower_layer_importance():
     """The lower layer's kv_compact importance ranks a higher layer's cache (same selection rule)."""
     cfg = C4.with_(B=2, H_q=8, H_kv=4, ctx=3000, w=32, n_visual=2000, grid_h=40, grid_w=50, clusters_h=4,
