@@ -184,10 +184,17 @@ template <class T, int R, int TW>
 void launch_tw(dim3 grid, const float* qpart, int npart, const void* Lk, float* S, int ldS, int B,
                int G, int Tc, int ctx_cap, hipStream_t st) {
   using E = typename T::elem;
+  // parts per thread (as the kernel splits them): all of a thread's part loads in one round trip
+  constexpr int GPB = T::HILO ? 8 : 16;
+  const int nq = (G < GPB ? G : GPB) * (R / 4);
+  const int npg = nq >= 256 ? 1 : (256 / nq < npart ? 256 / nq : npart);
+  const int per = (npart + npg - 1) / npg;
   if (npart == 1)
     latent_score_kernel<T, R, TW, 1><<<grid, 256, 0, st>>>(qpart, npart, (const E*)Lk, S, B, G, Tc, ldS, ctx_cap);
-  else
+  else if (per <= 8)
     latent_score_kernel<T, R, TW, 8><<<grid, 256, 0, st>>>(qpart, npart, (const E*)Lk, S, B, G, Tc, ldS, ctx_cap);
+  else
+    latent_score_kernel<T, R, TW, 16><<<grid, 256, 0, st>>>(qpart, npart, (const E*)Lk, S, B, G, Tc, ldS, ctx_cap);
 }
 
 template <class T, int R>
