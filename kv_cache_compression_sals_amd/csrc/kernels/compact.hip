@@ -83,18 +83,13 @@ __device__ __forceinline__ void logit_tile(const u32x4 (&ch)[Seg<T, DH>::NCH], c
 
 // A wave's tiles t = t_begin, t_begin + stride, ... < t_end with the K rows of the next D - 1
 // tiles in flight while one is computed (D buffers, indexed by compile-time constants).
-// Tiles in flight per wave (bf16; fp32 rows are twice as long: 2). Measured on the compaction
-// workload (B=16, 32 heads, ctx 16384): the statistics pass gains from 6 (1254 -> 1135 us for
-// kv_compact together with the next choice), the accumulation pass from 2, whose smaller register
-// footprint lets more of its waves share a SIMD; 8 / 8 took 1470 us.
-template <class T>
-constexpr int kStatsDepth = sizeof(typename T::elem) == 2 ? 6 : 2;
-template <class T>
-constexpr int kAccumDepth = 2;
+template <class T, int DH>
+constexpr int kKDepth = sizeof(typename T::elem) == 2 ? 4 : 2;
 
-template <class T, int DH, int D, class StepF>
+template <class T, int DH, class StepF>
 __device__ __forceinline__ void for_k_tiles(const typename T::elem* __restrict__ Kh, int ctx, int lane,
                                             int t_begin, int t_end, int stride, StepF step) {
+  constexpr int D = kKDepth<T, DH>;
   u32x4 buf[D][Seg<T, DH>::NCH];
 #pragma unroll
   for (int j = 0; j < D; ++j)
@@ -136,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void imp_stats_kernel(const typename T::e
   const int cbeg = c * kChunk, cend = min(ctx, cbeg + kChunk);
   // online (max, sum) per lane over its 4 tokens of each tile: the tile's own maximum first, then
   // one rescale, so that every lane takes the same path
-  for_k_tiles<T, DH, kStatsDepth<T>>(Kh, ctx, lane, cbeg + wave * 16, cend, 64, [&](int t0, const u32x4 (&ch)[Seg<T, DH>::NCH]) {
+  for_k_tiles<T, DH>(Kh, ctx, lane, cbeg + wave * 16, cend, 64, [&](int t0, const u32x4 (&ch)[Seg<T, DH>::NCH]) {
     f32x4 acc[4];
     logit_tile<T, DH>(ch, f, acc);
     // the whole tile is visible to every query of the group (and they all exist)
@@ -251,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::e
           invS[nb] = 0.f;
         }
       }
-      for_k_tiles<T, DH, kAccumDepth<T>>(Kh, ctx, lane, cbeg + wave * 16, cend, 64, [&](int t0, const u32x4 (&ch)[Seg<T, DH>::NCH]) {
+      for_k_tiles<T, DH>(Kh, ctx, lane, cbeg + wave * 16, cend, 64, [&](int t0, const u32x4 (&ch)[Seg<T, DH>::NCH]) {
         f32x4 acc[4];
         logit_tile<T, DH>(ch, f, acc);
         float part[4] = {0.f, 0.f, 0.f, 0.f};
