@@ -38,7 +38,9 @@ The default run also measures, as extra objects of the same JSON line (--only pi
   c5  one decode step through 32 independent resident layers of the 128K-context GQA workload
       (one replay of K captured 32-layer steps), with per-stage times from a traced pass.
 Before the workloads, an in-tree streaming read (sals_hbm_read) measures the HBM read bandwidth
-that hbm_frac_measured is stated against. Each decode workload also reports the median, p10 and
+that hbm_frac_measured is stated against, and an in-tree register-only MFMA loop (sals_mfma_peak)
+the bf16 MFMA throughput; every roofline object also gives its fraction of the measured peak
+(peak_measured, frac_measured) beside the one of the specification. Each decode workload also reports the median, p10 and
 p90 of the per-step time over --replays further replays, a warm variant (every step on the same
 input copy), the scoring + attention HBM fraction, and threshold selection on the same layer.
 The cpu_baseline object adds the CPU model and one-thread oracle times.
@@ -627,6 +629,40 @@ def measure_hbm(gib=2):
     return round(best, 1)
 
 
+def measure_mfma():
+    """bf16 MFMA throughput of the in-tree register-only MFMA loop (sals_mfma_peak): 1024, 2048 and
+    4096 workgroups of 4 waves, each wave 4 independent 32x32x16 accumulators over 1500 steps; the
+    best of five timed launches each, in TFLOP/s."""
+    import torch
+
+    from kv_cache_compression_sals_amd._lib import lib
+
+    iters = 1500
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    best = 0.0
+    for blocks in (1024, 2048, 4096):
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            st = lib().sals_mfma_peak(blocks, iters, sink.data_ptr(), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if st:
+                raise RuntimeError(f"sals_mfma_peak returned {st}")
+            flops = blocks * 4 * iters * 4 * 32768
+            best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return round(best, 1)
+
+
+def with_measured(rl, hbm_measured=None, mfma_measured=None):
+    """The roofline object with its fraction of the peak measured on this machine (frac_measured)."""
+    peak = mfma_measured if rl["bound"] == "mfma" else hbm_measured
+    if peak:
+        rl = dict(rl, peak_measured=peak, frac_measured=round(rl["achieved"] / peak, 4))
+    return rl
+
+
 def roofline_for(cfg, ctx, stage_us, label):
     """Roofline of the kernel that takes the most time: bound by HBM or by bf16 MFMA, whichever
     peak gives the longer time for its algorithmic bytes / flops."""
@@ -709,8 +745,9 @@ def cpu_baseline(case, budget_s=10.0, tiny=None):
     return out
 
 
-def summary(cfg, r, label, hbm_measured=None):
+def summary(cfg, r, label, hbm_measured=None, mfma_measured=None):
     rl, alg = roofline_for(cfg, r["case"]["ctx"], r["stage_us"], label)
+    rl = with_measured(rl, hbm_measured, mfma_measured)
     gbps = alg["compulsory"] / (r["us"] * 1e-6) / 1e9
     # scoring + attention: the latent scan and the rebuild/attention stages (the value kernels, or
     # the split merge that applies P_v) over their summed time
@@ -770,10 +807,12 @@ def main():
         torch.cuda.synchronize()
         log(f"[calib] copied {args.calib_copy_mib} MiB")
         del a, b
-    hbm = None
+    hbm = mfma = None
     if not args.no_hbm_probe:
         hbm = measure_hbm()
         log(f"[hbm] streaming read {hbm:.0f} GB/s")
+        mfma = measure_mfma()
+        log(f"[mfma] bf16 MFMA loop {mfma:.0f} TFLOP/s")
 
     labels = {"c1": "ctx512_tiny", "c2": "ctx4k", "c3": "ctx32k", "c4": "compact_ctx16k", "c5": "ctx128k_32layers"}
     keys = [k for k in args.only.split(",") if k]
@@ -781,12 +820,13 @@ def main():
     for key in [k for k in keys if k in ("c4", "c5")]:
         fn = run_compact_workload if key == "c4" else run_layers_workload
         extra[labels[key]] = fn(CONFIGS[key], min(args.steps, 10), min(args.warmup, 2), labels[key])
+        extra[labels[key]]["roofline"] = with_measured(extra[labels[key]]["roofline"], hbm, mfma)
         log(f"[{labels[key]}] {extra[labels[key]]}")
     tiny = None
     if "c1" in keys:
         cfg = CONFIGS["c1"]
         r = run_workload(cfg, args.steps, args.warmup, labels["c1"], args.replays, comparators=False)
-        sm = summary(cfg, r, labels["c1"], hbm)
+        sm = summary(cfg, r, labels["c1"], hbm, mfma)
         extra[labels["c1"]] = dict(workload=f"{labels['c1']} decode, one layer: B={cfg.B} H_q={cfg.H_q} "
                                             f"H_kv={cfg.H_kv} d={cfg.d} ctx={cfg.ctx} r={cfg.r} k={cfg.k} w={cfg.w} "
                                             f"G={cfg.G}, fp32 (latency-bound)",
@@ -802,7 +842,7 @@ def main():
     for key in keys:
         cfg = CONFIGS[key]
         r = run_workload(cfg, args.steps, args.warmup, labels[key], args.replays)
-        res[key] = (cfg, r, summary(cfg, r, labels[key], hbm))
+        res[key] = (cfg, r, summary(cfg, r, labels[key], hbm, mfma))
         sm = res[key][2]
         log(f"[{labels[key]}] {sm['us_per_step']:.1f} us/step (eager traced {sm['eager_us_per_step']:.1f}), "
             f"{sm['kv_gbps']:.0f} GB/s effective, stages "
@@ -828,6 +868,7 @@ def main():
                         f"ctx={cfg.ctx} r={cfg.r} k={cfg.k} w={cfg.w} G={cfg.G}",
         },
         "hbm_measured_gbps": hbm,
+        "mfma_measured_tflops": mfma,
     }
     line.update({k: v for k, v in sm.items() if k != "us_per_step"})
     for key in keys[1:]:

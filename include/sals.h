@@ -260,6 +260,16 @@ sals_status kv_compact_traced(const kvc_shape* c, const void* K, const void* V, 
 sals_status sals_hbm_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, sals_stream_t stream);
 
 /*
+ * sals_mfma_peak - bf16 MFMA throughput probe: `blocks` workgroups of 256 threads (4 waves), each
+ * wave issuing iters x 4 independent bf16 32x32x16 MFMAs (32768 flops each) from registers, then
+ * writing one word per workgroup to sink[block] (so that no result is dead). Total flops:
+ * blocks * 4 * iters * 4 * 32768. The measured peak that the key rebuild is also stated against
+ * (next to the 2.5 PFLOP/s specification).
+ * Errors: NULL, RANGE (blocks outside [1, 2^20], iters outside [1, 2^24]), ALIGN, HIP.
+ */
+sals_status sals_mfma_peak(int32_t blocks, int32_t iters, uint32_t* sink, sals_stream_t stream);
+
+/*
  * kv_importance_sparsity_workspace_bytes - workspace size of kv_importance_sparsity.
  */
 sals_status kv_importance_sparsity_workspace_bytes(const kvc_shape* c, int32_t ctx, int32_t w,

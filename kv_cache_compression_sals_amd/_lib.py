@@ -69,6 +69,7 @@ PROTOTYPES = {
     "kv_compact_traced": (_I, [ctypes.POINTER(KvcShape), _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _S, _P,
                                ctypes.POINTER(ctypes.c_void_p), _I]),
     "sals_hbm_read": (_I, [_P, _S, _P, _I, _P]),
+    "sals_mfma_peak": (_I, [_I, _I, _P, _P]),
     "kv_layer_budgets": (_I, [_P, _I, ctypes.c_int64, _I, _P]),
     "kv_compact_from_importance": (_I, [ctypes.POINTER(KvcShape), _P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
     "sals_reconstruct_kv": (_I, [ctypes.POINTER(SalsShape), ctypes.c_float, _P, _P, _P, _P, _I, _I, _I,

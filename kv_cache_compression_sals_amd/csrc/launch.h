@@ -176,6 +176,9 @@ hipError_t launch_mass_budget(const float* imp, int rows, int ctx, float mass, i
 // Streaming read of bytes (a multiple of 16) with `blocks` workgroups of 256 threads; sink gets
 // one word per workgroup.
 hipError_t launch_hbm_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t st);
+// blocks workgroups of 256 threads, each wave issuing iters x 4 bf16 32x32x16 MFMAs (32768 flops
+// each) from registers; one word per workgroup to sink[block].
+hipError_t launch_mfma_peak(int blocks, int iters, uint32_t* sink, hipStream_t st);
 
 // Flash-decode over a contiguous cache: partials per split, or out directly (n_splits == 1).
 // Query heads of one KV head that a dense-decode workgroup serves together: 4, 2 or 1.

@@ -559,6 +559,16 @@ sals_status sals_hbm_read(const void* src, size_t bytes, uint32_t* sink, int32_t
   return e == hipSuccess ? SALS_OK : hip_fail(e);
 }
 
+sals_status sals_mfma_peak(int32_t blocks, int32_t iters, uint32_t* sink, sals_stream_t stream) {
+  if (!sink) return SALS_ERR_NULL;
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 24)) return SALS_ERR_RANGE;
+  if (misaligned(sink)) return SALS_ERR_ALIGN;
+  sals_status st = device_ready();
+  if (st != SALS_OK) return st;
+  hipError_t e = sals::launch_mfma_peak(blocks, iters, sink, (hipStream_t)stream);
+  return e == hipSuccess ? SALS_OK : hip_fail(e);
+}
+
 sals_status kv_importance_sparsity_workspace_bytes(const kvc_shape* c, int32_t ctx, int32_t w,
                                                  size_t* bytes) {
   if (!bytes) return SALS_ERR_NULL;

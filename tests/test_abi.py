@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     L = lib()
     for n in names:
         assert hasattr(L, n), n
@@ -238,6 +238,19 @@ def _gpu_present():
 
 
 @pytest.mark.skipif(_gpu_present(), reason="stand-in pointers must never reach a real GPU")
+def test_probe_argument_errors():
+    L = lib()
+    assert L.sals_hbm_read(None, 16, P, 1, None) == NULL
+    assert L.sals_hbm_read(P, 15, P, 1, None) == RANGE
+    assert L.sals_hbm_read(P, 16, P, 0, None) == RANGE
+    assert L.sals_hbm_read(P + 4, 16, P, 1, None) == ALIGN
+    assert L.sals_mfma_peak(1, 1, None, None) == NULL
+    assert L.sals_mfma_peak(0, 1, P, None) == RANGE
+    assert L.sals_mfma_peak(1, 0, P, None) == RANGE
+    assert L.sals_mfma_peak(1, 1 << 25, P, None) == RANGE
+    assert L.sals_mfma_peak(1, 1, P + 4, None) == ALIGN
+
+
 def test_valid_call_without_device_reports_hip_error():
     assert _step() == HIP
     assert lib().sals_last_hip_error() != 0
