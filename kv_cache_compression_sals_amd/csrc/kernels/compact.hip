@@ -130,7 +130,10 @@ __global__ __launch_bounds__(kThreads) void imp_stats_kernel(const typename T::e
   }
   const int cbeg = c * kChunk, cend = min(ctx, cbeg + kChunk);
   // online (max, sum) per lane over its 4 tokens of each tile: the tile's own maximum first, then
-  // one rescale, so that every lane takes the same path
+  // one rescale. Branch-free: the visibility masks are combined with bitwise operators and
+  // applied by selects (short-circuit conditions would compile to one divergent branch per
+  // element), and a lane that has seen nothing yet (mn = -inf) rescales against 0 instead, which
+  // leaves (m, s) = (-inf, 0) unchanged since every exponential is then of -inf.
   for_k_tiles<T, DH>(Kh, ctx, lane, cbeg + wave * 16, cend, 64, [&](int t0, const u32x4 (&ch)[Seg<T, DH>::NCH]) {
     f32x4 acc[4];
     logit_tile<T, DH>(ch, f, acc);
@@ -145,17 +148,18 @@ __global__ __launch_bounds__(kThreads) void imp_stats_kernel(const typename T::e
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + q4 * 4 + i;
-        x[i] = (full || (t < cend && t <= lim && qi < w)) ? acc[nb][i] * scale : -INFINITY;
+        const bool ok = full | ((t < cend) & (t <= lim) & (qi < w));
+        const float v = acc[nb][i] * scale;
+        x[i] = ok ? v : -INFINITY;
         tm = fmaxf(tm, x[i]);
       }
       const float mn = fmaxf(m[nb], tm);
-      if (mn != -INFINITY) {
-        float add = 0.f;
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      float add = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) add += __builtin_amdgcn_exp2f(x[i] - mn);
-        s[nb] = s[nb] * __builtin_amdgcn_exp2f(m[nb] - mn) + add;
-        m[nb] = mn;
-      }
+      for (int i = 0; i < 4; ++i) add += __builtin_amdgcn_exp2f(x[i] - mref);
+      s[nb] = s[nb] * __builtin_amdgcn_exp2f(m[nb] - mref) + add;
+      m[nb] = mn;
     }
   });
   // merge the 4 lane groups (same query), then the 4 waves
@@ -259,9 +263,9 @@ __global__ __launch_bounds__(kThreads) void imp_accum_kernel(const typename T::e
           for (int i = 0; i < 4; ++i) {
             const int t = t0 + q4 * 4 + i;
             const float e = __builtin_amdgcn_exp2f(acc[nb][i] * scale - M[nb]) * invS[nb];
-            const bool valid = full || (qi < w && t <= lim);
+            const bool valid = full | ((qi < w) & (t <= lim));  // bitwise: no branch per element
             part[i] += valid ? e : 0.f;
-            if (cnt) below += (valid && e < p_thresh) ? 1.f : 0.f;
+            if (cnt) below += (valid & (e < p_thresh)) ? 1.f : 0.f;
           }
         }
         // sum over the 16 queries of the row (DPP, no LDS crossbar)
