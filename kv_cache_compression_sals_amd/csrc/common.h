@@ -136,6 +136,18 @@ __device__ __forceinline__ float xor32_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Transposing pair sums (no LDS traffic). xor32_pair_sum(a, b): lanes 0-31 hold a[l] + a[l ^ 32],
+// lanes 32-63 hold b[l] + b[l ^ 32]. xor16_pair_sum(a, b): lane rows (16 lanes) 0 and 2 hold
+// a[l] + a[l ^ 16], rows 1 and 3 hold b[l] + b[l ^ 16].
+__device__ __forceinline__ float xor32_pair_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_pair_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum / max over the 16 lanes of a DPP row (lanes sharing lane/16), result in every lane of it.
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f32<0xB1>(v);

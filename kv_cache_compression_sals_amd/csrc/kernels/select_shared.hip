@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
         for (int i = 0; i < 3; ++i)
 #pragma unroll
           for (int lb = 0; lb < 4; ++lb)
-            acc[i0 + i][lb] = BF16::mma(chunk_frag<BF16>(af[i], 0), chunk_frag<BF16>(bf[lb], 0), acc[i0 + i][lb]);
+            acc[i0 + i][lb] = BF16::mma(chunk_frag<BF16>(bf[lb], 0), chunk_frag<BF16>(af[i], 0), acc[i0 + i][lb]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -226,41 +226,57 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
   __syncthreads();  // the chunk buffers are free: the first one holds the partial logits
 
   // ---- RoPE at the tokens' positions, partial logits over this wave's 64 columns ----
+  // acc[i][lb] holds K rows 4 q4 .. 4 q4 + 3 of column block lb for token tt * 16 + n16 (P_k is
+  // the MFMA's first operand), so the RoPE pairs (c, c + 64) and the query products are in-lane;
+  // only the sum over the four lane rows (q4) crosses lanes.
   float* lgp = (float*)(smem + kOffA);  // [cg][head][hh][token]
-  const double frev = ftab[cg * 16 + n16];
-  float qv[NQH][4];
+  const int c0 = cg * 16 + 4 * q4;      // first RoPE pair index of this lane (0..63)
+  double frev[4];
 #pragma unroll
-  for (int hh = 0; hh < NQH; ++hh)
+  for (int e = 0; e < 4; ++e) frev[e] = ftab[c0 + e];
+  constexpr int NV = kTTW * kNH * NQH;  // partial logits per lane: (tile, head, query head)
+  constexpr int NPT = kNH * NQH;        // per tile
+  float part[NV];
+  // this lane's token in tile i of the wave: tg * kTTW * 16 + i * 16 + n16
+  const int32_t* posw = pos + tg * kTTW * 16 + n16;
+  float* lgw = lgp + tg * kTTW * 16 + n16;
+  // sum of values 4j .. 4j + 3 over the four lane rows, by two transposing swaps: lane row 0 then
+  // holds the total of value 4j, row 1 of 4j + 2, row 2 of 4j + 1, row 3 of 4j + 3
+  auto flush = [&](int j) {
+    float v4[4];
 #pragma unroll
-    for (int lb = 0; lb < 4; ++lb)
-      qv[hh][lb] = qs[((lb & 1) * kMaxQH + min(hh, nqh - 1)) * kDH + (brw[lb] - (lb & 1) * kDH)];
+    for (int u = 0; u < 4; ++u) v4[u] = 4 * j + u < NV ? part[4 * j + u] : 0.f;
+    const float t = xor16_pair_sum(xor32_pair_sum(v4[0], v4[1]), xor32_pair_sum(v4[2], v4[3]));
+    const int vi = 4 * j + ((q4 & 1) << 1) + (q4 >> 1);
+    const int i = vi / NPT, h2 = (vi / NQH) % kNH, hh = vi % NQH;
+    if (vi < NV && hh < nqh) lgw[((cg * kNH + h2) * kMaxQH + hh) * kTOK + i * 16] = t;
+  };
 #pragma unroll
   for (int i = 0; i < kTTW; ++i) {
-    const int tt = tg * kTTW + i;
+    const double pd = (double)posw[i * 16];
+#pragma unroll
+    for (int v = 0; v < NPT; ++v) part[i * NPT + v] = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float sn, cs;
-      rope_sincos(pos[tt * 16 + q4 * 4 + e], frev, &sn, &cs);
+      double rv = pd * frev[e];
+      rv -= rint(rv);
+      const float sn = __builtin_amdgcn_sinf((float)rv), cs = __builtin_amdgcn_cosf((float)rv);
 #pragma unroll
-      for (int lb = 0; lb < 2; ++lb) {
-        const float x1 = acc[i][lb][e], x2 = acc[i][lb + 2][e];
-        acc[i][lb][e] = x1 * cs - x2 * sn;
-        acc[i][lb + 2][e] = x2 * cs + x1 * sn;
-      }
-    }
+      for (int h2 = 0; h2 < kNH; ++h2) {
+        const float x1 = acc[i][h2][e], x2 = acc[i][h2 + 2][e];
+        const float r1 = x1 * cs - x2 * sn, r2 = x2 * cs + x1 * sn;
 #pragma unroll
-    for (int h2 = 0; h2 < kNH; ++h2)
-#pragma unroll
-      for (int hh = 0; hh < NQH; ++hh) {
-        float pl[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pl[e] = row16_sum(fmaf(qv[hh][h2], acc[i][h2][e], qv[hh][h2 + 2] * acc[i][h2 + 2][e]));
-        if (n16 == 0 && hh < nqh) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) lgp[((cg * kNH + h2) * kMaxQH + hh) * kTOK + tt * 16 + q4 * 4 + e] = pl[e];
+        for (int hh = 0; hh < NQH; ++hh) {
+          const float* qh = qs + (h2 * kMaxQH + min(hh, nqh - 1)) * kDH + c0 + e;
+          float& pv = part[(i * kNH + h2) * NQH + hh];
+          pv = fmaf(qh[0], r1, fmaf(qh[kDH / 2], r2, pv));
         }
       }
+    }
+    // groups completed by this tile (the last, partial one after the last tile)
+#pragma unroll
+    for (int j = (i * NPT) / 4; j < ((i + 1) * NPT) / 4; ++j) flush(j);
+    if (i == kTTW - 1 && NV % 4) flush(NV / 4);
   }
   __syncthreads();
 
