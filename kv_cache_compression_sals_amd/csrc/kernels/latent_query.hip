@@ -67,50 +67,94 @@ __global__ __launch_bounds__(kThreads) void latent_query_kernel(const typename T
   const int group_rows = H_kv * d / G;
   const int s = row0 / group_rows, part = (row0 % group_rows) / RB;
 
-  // P_k rows of this thread, all in flight before the query staging starts
-  u32x4 pc[RPT][NC];
-#pragma unroll
-  for (int i = 0; i < RPT; ++i)
-#pragma unroll
-    for (int m = 0; m < NC; ++m) pc[i][m] = *(const u32x4*)(Pk + (size_t)(row0 + rp + 32 * i) * r + col + m * EPC);
-
-  for (int b0 = 0; b0 < B; b0 += kBC) {
+  // qsum[bb][i] = sum_h q[b0 + bb][g * nqh + h][c] for row row0 + i = g * d + c; a chunk of
+  // EPC rows never straddles a KV head (d is a multiple of EPC). Thread tid owns the chunks
+  // e = tid + kThreads * n of each pass.
+  auto qload = [&](int b0, int e, u32x4 (&v)[kQB], int h0) {
     const int nb = min(kBC, B - b0);
-    __syncthreads();  // the previous pass is done with qsum and red
-    // qsum[bb][i] = sum_h q[b0 + bb][g * nqh + h][c] for row row0 + i = g * d + c; a chunk of
-    // EPC rows never straddles a KV head (d is a multiple of EPC)
-    for (int e = tid; e < nb * QCH; e += kThreads) {
+    const int ee = min(e, nb * QCH - 1);
+    const int bb = ee / QCH, ch = ee % QCH;
+    const int row = row0 + ch * EPC;
+    const int g = row / d, c = row % d;
+    const elem* qp = q + ((size_t)(b0 + bb) * H_q + (size_t)g * nqh) * d + c;
+#pragma unroll
+    for (int u = 0; u < kQB; ++u) v[u] = *(const u32x4*)(qp + (size_t)min(h0 + u, nqh - 1) * d);
+  };
+  auto qadd = [&](const u32x4 (&v)[kQB], int h0, float (&acc)[EPC]) {
+    // branch-free: heads past nqh (clamped loads of the last head) add zero
+#pragma unroll
+    for (int u = 0; u < kQB; ++u) {
+      const uint32_t keep = h0 + u < nqh ? 0xffffffffu : 0u;
+      if constexpr (EPC == 8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] += __uint_as_float((v[u][j] << 16) & keep);
+          acc[2 * j + 1] += __uint_as_float(v[u][j] & 0xffff0000u & keep);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += __uint_as_float(v[u][j] & keep);
+      }
+    }
+  };
+  // stages qsum for chunks e0, e0 + kThreads, ... of the pass starting at sequence b0
+  auto stage_q = [&](int b0, int e0) {
+    const int nb = min(kBC, B - b0);
+    for (int e = e0; e < nb * QCH; e += kThreads) {
       const int bb = e / QCH, ch = e % QCH;
-      const int row = row0 + ch * EPC;
-      const int g = row / d, c = row % d;
-      const elem* qp = q + ((size_t)(b0 + bb) * H_q + (size_t)g * nqh) * d + c;
       float acc[EPC];
 #pragma unroll
       for (int x = 0; x < EPC; ++x) acc[x] = 0.f;
       for (int h0 = 0; h0 < nqh; h0 += kQB) {
         u32x4 v[kQB];
-#pragma unroll
-        for (int u = 0; u < kQB; ++u) v[u] = *(const u32x4*)(qp + (size_t)min(h0 + u, nqh - 1) * d);
-#pragma unroll
-        for (int u = 0; u < kQB; ++u) {
-          if (h0 + u < nqh) {
-            if constexpr (EPC == 8) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                acc[2 * j] += __uint_as_float(v[u][j] << 16);
-                acc[2 * j + 1] += __uint_as_float(v[u][j] & 0xffff0000u);
-              }
-            } else {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) acc[j] += __uint_as_float(v[u][j]);
-            }
-          }
-        }
+        qload(b0, e, v, h0);
+        qadd(v, h0, acc);
       }
 #pragma unroll
       for (int x = 0; x < EPC; ++x) qsum[bb][ch * EPC + x] = acc[x];
     }
-    __syncthreads();
+  };
+  // The first chunk of the first pass is straight-line code: its query loads go out first, then
+  // the P_k rows (loads complete in issue order, so the query sums wait for the queries alone),
+  // then its sums, written unconditionally (a thread past the last chunk repeats the last one
+  // and writes the same values), so that the compiler keeps the loads in this order.
+  u32x4 qv0[kQB];
+  qload(0, tid, qv0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 pc[RPT][NC];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+#pragma unroll
+    for (int m = 0; m < NC; ++m) pc[i][m] = *(const u32x4*)(Pk + (size_t)(row0 + rp + 32 * i) * r + col + m * EPC);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const int nb0 = min(kBC, B);
+    const int ee = min(tid, nb0 * QCH - 1);
+    float acc[EPC];
+#pragma unroll
+    for (int x = 0; x < EPC; ++x) acc[x] = 0.f;
+    qadd(qv0, 0, acc);
+    for (int h0 = kQB; h0 < nqh; h0 += kQB) {
+      u32x4 v[kQB];
+      qload(0, ee, v, h0);
+      qadd(v, h0, acc);
+    }
+#pragma unroll
+    for (int x = 0; x < EPC; ++x) qsum[ee / QCH][(ee % QCH) * EPC + x] = acc[x];
+  }
+  stage_q(0, tid + kThreads);
+  // nothing that uses P_k (the compiler hoists their unpacking out of the pass loop) moves above
+  // the query sums
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();  // qsum visible; the P_k loads stay in flight
+
+  for (int b0 = 0; b0 < B; b0 += kBC) {
+    const int nb = min(kBC, B - b0);
+    if (b0 > 0) {
+      __syncthreads();  // the previous pass is done with qsum and red
+      stage_q(b0, tid);
+      __syncthreads();
+    }
     float acc[kBC][8];
 #pragma unroll
     for (int bb = 0; bb < kBC; ++bb)
