@@ -105,49 +105,148 @@ __global__ __launch_bounds__(256) void latent_score_kernel(const float* __restri
   const int b = blockIdx.y, gb = blockIdx.z;
   const size_t brow = (size_t)b * ctx_cap;
   const int tile0 = blockIdx.x * (kWaves * TW) + wave;
-  // the first pair's rows (HBM) are requested first, then the latent-query parts (L2)
   u32x4 c0[NW], c1[NW];
-  load_tile<T, R>(Lk, brow, min(tile0 * 16 + n16, Tc - 1), q4, c0);
-  load_tile<T, R>(Lk, brow, min((tile0 + 4) * 16 + n16, Tc - 1), q4, c1);
-  // operand rows: q~ of group slot gs in row gs (bf16: high part; row 8 + gs the low part).
-  // Rows of slots past G are never written; the MFMA rows they feed are never stored. The parts
-  // of a column quad are split into npg contiguous ranges (npg = 256 / quads when there are
-  // fewer than 256 quads), each summed by one thread with all its loads in flight; the range
-  // sums are then added in range order.
-  {
+  if constexpr (PB == 1) {
+    // one part per group: the first pair's rows (HBM) are requested first, then the part (one
+    // L2 load per quad)
+    load_tile<T, R>(Lk, brow, min(tile0 * 16 + n16, Tc - 1), q4, c0);
+    load_tile<T, R>(Lk, brow, min((tile0 + 4) * 16 + n16, Tc - 1), q4, c1);
+    // operand rows: q~ of group slot gs in row gs (bf16: high part; row 8 + gs the low part).
+    // Rows of slots past G are never written; the MFMA rows they feed are never stored. The parts
+    // of a column quad are split into npg contiguous ranges (npg = 256 / quads when there are
+    // fewer than 256 quads), each summed by one thread with all its loads in flight; the range
+    // sums are then added in range order.
+    {
+      const int gv = min(GPB, G - gb * GPB);
+      const int nq = gv * (R / 4);  // column quads of the slice
+      const int npg = nq >= 256 ? 1 : min(256 / nq, npart);
+      const int per = (npart + npg - 1) / npg;
+      const size_t pstride = (size_t)B * G * R;
+      for (int e = tid; e < nq * npg; e += 256) {
+        const int quad = e % nq, pg = e / nq;
+        const int gs = quad / (R / 4), cq = quad % (R / 4);
+        const float* src = qpart + ((size_t)b * G + gb * GPB + gs) * R + cq * 4;
+        const int pa = pg * per, pe = min(npart, pa + per);
+        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int p0 = pa; p0 < pe; p0 += PB) {
+          float4 v[PB];
+#pragma unroll
+          for (int u = 0; u < PB; ++u) v[u] = *(const float4*)(src + (size_t)min(p0 + u, pe - 1) * pstride);
+#pragma unroll
+          for (int u = 0; u < PB; ++u) {
+            if (p0 + u < pe) {
+              sum.x += v[u].x;
+              sum.y += v[u].y;
+              sum.z += v[u].z;
+              sum.w += v[u].w;
+            }
+          }
+        }
+        if (npg == 1) {
+          store_operand_quad<T>(opnd, OST, gs, cq, sum);
+        } else {
+          rsum[pg * nq + quad] = sum;
+        }
+      }
+      if (npg > 1) {
+        __syncthreads();
+        for (int quad = tid; quad < nq; quad += 256) {
+          float4 sum = rsum[quad];
+          for (int pg = 1; pg < npg; ++pg) {
+            const float4 v = rsum[pg * nq + quad];
+            sum.x += v.x;
+            sum.y += v.y;
+            sum.z += v.z;
+            sum.w += v.w;
+          }
+          store_operand_quad<T>(opnd, OST, quad / (R / 4), quad % (R / 4), sum);
+        }
+      }
+    }
+    __syncthreads();
+  } else {
+    // several parts per group: their sums are the longer dependent chain before the MFMAs
+    // operand rows: q~ of group slot gs in row gs (bf16: high part; row 8 + gs the low part).
+    // Rows of slots past G are never written; the MFMA rows they feed are never stored. The parts
+    // of a column quad are split into npg contiguous ranges (npg = 256 / quads when there are
+    // fewer than 256 quads), each summed by one thread with all its loads in flight; the range
+    // sums are then added in range order.
     const int gv = min(GPB, G - gb * GPB);
     const int nq = gv * (R / 4);  // column quads of the slice
     const int npg = nq >= 256 ? 1 : min(256 / nq, npart);
     const int per = (npart + npg - 1) / npg;
     const size_t pstride = (size_t)B * G * R;
-    for (int e = tid; e < nq * npg; e += 256) {
-      const int quad = e % nq, pg = e / nq;
-      const int gs = quad / (R / 4), cq = quad % (R / 4);
-      const float* src = qpart + ((size_t)b * G + gb * GPB + gs) * R + cq * 4;
-      const int pa = pg * per, pe = min(npart, pa + per);
-      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int p0 = pa; p0 < pe; p0 += PB) {
-        float4 v[PB];
+    auto part_src = [&](int e, int& gs, int& cq, int& pg, int& pa, int& pe) {
+      const int quad = e % nq;
+      pg = e / nq;
+      gs = quad / (R / 4);
+      cq = quad % (R / 4);
+      pa = pg * per;
+      pe = min(npart, pa + per);
+      return qpart + ((size_t)b * G + gb * GPB + gs) * R + cq * 4;
+    };
+    auto add_parts = [&](const f32x4 (&v)[PB], int p0, int pe, float4& sum) {
 #pragma unroll
-        for (int u = 0; u < PB; ++u) v[u] = *(const float4*)(src + (size_t)min(p0 + u, pe - 1) * pstride);
-#pragma unroll
-        for (int u = 0; u < PB; ++u) {
-          if (p0 + u < pe) {
-            sum.x += v[u].x;
-            sum.y += v[u].y;
-            sum.z += v[u].z;
-            sum.w += v[u].w;
-          }
-        }
+      for (int u = 0; u < PB; ++u) {
+        const bool in = p0 + u < pe;  // branch-free: clamped loads past the range add 0
+        sum.x += in ? v[u][0] : 0.f;
+        sum.y += in ? v[u][1] : 0.f;
+        sum.z += in ? v[u][2] : 0.f;
+        sum.w += in ? v[u][3] : 0.f;
       }
+    };
+    auto put = [&](int e, int gs, int cq, int pg, const float4& sum) {
       if (npg == 1) {
         store_operand_quad<T>(opnd, OST, gs, cq, sum);
       } else {
-        rsum[pg * nq + quad] = sum;
+        rsum[pg * nq + e % nq] = sum;
       }
+    };
+    // Loads complete in issue order: this thread's first batch of part loads (L2) goes out first
+    // as straight-line code, then the first pair's rows (HBM), so that the part sums wait for the
+    // parts alone and the operand is built while the rows stream in. The first batch is summed and
+    // stored unconditionally (a thread past the last quad repeats it and writes the same values),
+    // so that the compiler keeps the loads in this order.
+    {
+      const int e = min(tid, nq * npg - 1);
+      int gs, cq, pg, pa, pe;
+      const float* src = part_src(e, gs, cq, pg, pa, pe);
+      f32x4 v[PB];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) v[u] = *(const f32x4*)(src + (size_t)min(pa + u, pe - 1) * pstride);
+      // compiler-only fences (no instruction): memory accesses keep their order across them
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile<T, R>(Lk, brow, min(tile0 * 16 + n16, Tc - 1), q4, c0);
+      load_tile<T, R>(Lk, brow, min((tile0 + 4) * 16 + n16, Tc - 1), q4, c1);
+      // the part registers pass through an empty asm here, so that no sum of them is placed above
+      // the row loads (the wait for the parts then follows the row loads' issue)
+#pragma unroll
+      for (int u = 0; u < PB; ++u) asm volatile("" : "+v"(v[u]) :: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+      add_parts(v, pa, pe, sum);
+      for (int p0 = pa + PB; p0 < pe; p0 += PB) {
+#pragma unroll
+        for (int u = 0; u < PB; ++u) v[u] = *(const f32x4*)(src + (size_t)min(p0 + u, pe - 1) * pstride);
+        add_parts(v, p0, pe, sum);
+      }
+      put(e, gs, cq, pg, sum);
+    }
+    for (int e = tid + 256; e < nq * npg; e += 256) {
+      int gs, cq, pg, pa, pe;
+      const float* src = part_src(e, gs, cq, pg, pa, pe);
+      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int p0 = pa; p0 < pe; p0 += PB) {
+        f32x4 v[PB];
+#pragma unroll
+        for (int u = 0; u < PB; ++u) v[u] = *(const f32x4*)(src + (size_t)min(p0 + u, pe - 1) * pstride);
+        add_parts(v, p0, pe, sum);
+      }
+      put(e, gs, cq, pg, sum);
     }
     if (npg > 1) {
-      __syncthreads();
+      lds_barrier();  // range sums visible; the row loads stay in flight
       for (int quad = tid; quad < nq; quad += 256) {
         float4 sum = rsum[quad];
         for (int pg = 1; pg < npg; ++pg) {
@@ -160,8 +259,10 @@ __global__ __launch_bounds__(256) void latent_score_kernel(const float* __restri
         store_operand_quad<T>(opnd, OST, quad / (R / 4), quad % (R / 4), sum);
       }
     }
+    // nothing that uses the rows moves above the operand
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
   }
-  __syncthreads();
   // MFMA A operand: row n16 of the operand, natural k layout
   u32x4 a[NW];
 #pragma unroll
