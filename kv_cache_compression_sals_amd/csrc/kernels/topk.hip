@@ -37,6 +37,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kShortThreads = 256;              // workgroup of the short-row kernel
+constexpr int kShortRow = 16 * kShortThreads;   // longest short row (16 keys per thread)
 constexpr int kLdsKeys = 32768;
 constexpr int kBins = 2048;
 constexpr int kIPT = 16;     // keys per lane per chunk when a wave ranks a run (16 slices of 64)
@@ -45,13 +47,22 @@ constexpr int kList = 16384; // short-list capacity of topk_global (positions)
 
 // Finds, in hist[0 .. kBins), the bin b holding the `remaining`-th largest item (bins ordered by
 // value, highest bin = largest): bcast[0] = b, bcast[1] = items in bins above b, bcast[2] =
-// items in b. Uses all threads; hist is no longer read once it returns.
+// items in b. Uses all NT threads (kBins / NT consecutive bins each); hist is no longer read once
+// it returns.
+template <int NT>
 __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remaining, uint32_t* scan,
                                          uint32_t* bcast) {
+  constexpr int NW = NT / 64, BPT = kBins / NT;
+  static_assert(BPT * NT == kBins && NW % 4 == 0, "bins per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b0 = 2 * tid;  // each thread owns bins [2*tid, 2*tid + 2)
-  const uint32_t c0 = hist[b0], c1 = hist[b0 + 1];
-  const uint32_t tot = c0 + c1;
+  const int b0 = BPT * tid;  // each thread owns bins [b0, b0 + BPT)
+  uint32_t c[BPT];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    c[j] = hist[b0 + j];
+    tot += c[j];
+  }
   // suffix sum over the bins: within the wave (total minus the exclusive prefix), then the
   // waves above
   const uint32_t incl = wave_incl_scan(tot, lane);
@@ -59,11 +70,11 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remainin
   const uint32_t v = wtot - incl + tot;
   if (lane == 0) scan[wave] = v;
   __syncthreads();
-  // the totals of all waves in four 16-byte reads, then the ones above this wave (no chain of
+  // the totals of all waves in 16-byte reads, then the ones above this wave (no chain of
   // dependent LDS reads)
-  uint32_t sv[kWaves];
+  uint32_t sv[NW];
 #pragma unroll
-  for (int q = 0; q < kWaves / 4; ++q) {
+  for (int q = 0; q < NW / 4; ++q) {
     const uint4 t = ((const uint4*)scan)[q];
     sv[4 * q] = t.x;
     sv[4 * q + 1] = t.y;
@@ -72,18 +83,22 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t remainin
   }
   uint32_t above_waves = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) above_waves += w > wave ? sv[w] : 0u;
+  for (int w = 0; w < NW; ++w) above_waves += w > wave ? sv[w] : 0u;
   const uint32_t suf = v + above_waves;  // items in this thread's bins and all higher bins
   const uint32_t above = suf - tot;
   if (above < remaining && remaining <= suf) {
-    if (above + c1 >= remaining) {
-      bcast[0] = (uint32_t)(b0 + 1);
-      bcast[1] = above;
-      bcast[2] = c1;
-    } else {
-      bcast[0] = (uint32_t)b0;
-      bcast[1] = above + c1;
-      bcast[2] = c0;
+    // this thread's bins from the highest down
+    uint32_t acc = above;
+    bool done = false;
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (!done && acc + c[j] >= remaining) {
+        bcast[0] = (uint32_t)(b0 + j);
+        bcast[1] = acc;
+        bcast[2] = c[j];
+        done = true;
+      }
+      acc += c[j];
     }
   }
   __syncthreads();
@@ -94,7 +109,8 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Exclusive prefix of a per-wave count over the waves of the workgroup, and the block total.
+// Exclusive prefix of a per-wave count over the NT / 64 waves of the workgroup, and the block total.
+template <int NT>
 __device__ __forceinline__ void block_prefix(uint32_t mine, uint32_t* scan, uint32_t& before, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (lane == 0) scan[wave] = mine;
@@ -102,7 +118,7 @@ __device__ __forceinline__ void block_prefix(uint32_t mine, uint32_t* scan, uint
   before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const uint32_t v = scan[w];
     before += (w < wave) ? v : 0u;
     total += v;
@@ -128,7 +144,7 @@ __device__ __forceinline__ int topk_prologue(KeyF key, MapF map, int Tc, int kp,
       uint32_t mine = 0;
       for (int i = tid; i < Tc; i += kThreads) mine += key(i) >= tkey ? 1u : 0u;
       uint32_t before, total;
-      block_prefix((uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(mine, lane), 63), scan, before, total);
+      block_prefix<kThreads>((uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(mine, lane), 63), scan, before, total);
       kp = (int)min((uint32_t)kp, total);
     }
     for (int j = kp + wcount + tid; j < pad_to; j += kThreads) out[j] = -1;
@@ -147,7 +163,6 @@ __device__ __forceinline__ int topk_prologue(KeyF key, MapF map, int Tc, int kp,
 // reading its 32 consecutive keys as 16-byte pieces and a wave writing consecutive 16-byte pieces
 // both spread over the banks.
 __device__ __forceinline__ int padded(int i) { return i + ((i >> 5) << 2); }
-constexpr int kStageWords = kLdsKeys / 32 * 36;
 
 // The selection of one workgroup over at most kThreads * KPT keys (thread t owns the KPT
 // consecutive keys from t * KPT and holds them in registers): the kp largest of n keys, ties to
@@ -159,26 +174,28 @@ constexpr int kStageWords = kLdsKeys / 32 * 36;
 // and *cnt_out receives kp + wcount. For GATHER the count runs over the candidates: a row with
 // fewer than kp passing keys has all of them among the candidates, otherwise at least kp pass
 // there too, so min(kp, count) is the row's.
-template <int KPT, bool GATHER>
+template <int NT, int KPT, bool GATHER>
 __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const int32_t* __restrict__ cand,
                                           const uint32_t* __restrict__ ckeys, int n, int kp,
                                           int32_t* __restrict__ out, uint32_t* __restrict__ okeys,
                                           int obase, int wcount, int wstart, bool vec, bool thr,
                                           uint32_t tkey, int32_t* __restrict__ cnt_out, int pad_to) {
-  static_assert(KPT % 4 == 0 && KPT <= 32 && kThreads * KPT <= kLdsKeys, "keys per thread");
+  static_assert(KPT % 4 == 0 && KPT <= 32 && NT * KPT <= kLdsKeys, "keys per thread");
+  constexpr int NW = NT / 64;
+  constexpr int kStage = NT * KPT / 32 * 36;  // staging words for NT * KPT keys
   // staged keys (padded layout); after the ranking, the selection's positions in output order
-  __shared__ __attribute__((aligned(16))) uint32_t stage[kStageWords];
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kStage];
   __shared__ __attribute__((aligned(16))) uint32_t hist[kBins + 4];  // [kBins]: keys past the row
-  __shared__ __attribute__((aligned(16))) uint32_t scan[kWaves];
+  __shared__ __attribute__((aligned(16))) uint32_t scan[NW];
   __shared__ uint32_t bcast[4];
-  __shared__ uint32_t mm[3 * kWaves];  // per-wave key minima, maxima and threshold counts
+  __shared__ uint32_t mm[3 * NW];  // per-wave key minima, maxima and threshold counts
   __shared__ uint32_t nsmall, tsel[2];  // small-bin gather count; (tau, take_eq)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Tc = n;
-  for (int i = tid; i < kBins + 4; i += kThreads) hist[i] = 0;
+  for (int i = tid; i < kBins + 4; i += NT) hist[i] = 0;
   if (tid == 0) nsmall = 0;
 
-  // ---- 1. coalesced loads: this thread's 16-byte pieces u = tid + kThreads * q hold positions
+  // ---- 1. coalesced loads: this thread's 16-byte pieces u = tid + NT * q hold positions
   //      4u .. 4u + 3. They are kept in registers (values for the histogram) and staged in LDS as
   //      keys; the row's range (and, in threshold mode, the count of keys >= tkey) follows ----
   using Reg = std::conditional_t<GATHER, uint32_t, float>;  // candidate keys, or scores
@@ -195,13 +212,13 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
     if constexpr (GATHER) {
       uint4 w[KPT / 4];
 #pragma unroll
-      for (int q = 0; q < KPT / 4; ++q) w[q] = *(const uint4*)(ckeys + min(4 * (tid + kThreads * q), last4));
+      for (int q = 0; q < KPT / 4; ++q) w[q] = *(const uint4*)(ckeys + min(4 * (tid + NT * q), last4));
 #pragma unroll
       for (int q = 0; q < KPT / 4; ++q) pr[4 * q] = w[q].x, pr[4 * q + 1] = w[q].y, pr[4 * q + 2] = w[q].z, pr[4 * q + 3] = w[q].w;
     } else {
       float4 w[KPT / 4];
 #pragma unroll
-      for (int q = 0; q < KPT / 4; ++q) w[q] = *(const float4*)(src + min(4 * (tid + kThreads * q), last4));
+      for (int q = 0; q < KPT / 4; ++q) w[q] = *(const float4*)(src + min(4 * (tid + NT * q), last4));
 #pragma unroll
       for (int q = 0; q < KPT / 4; ++q) pr[4 * q] = w[q].x, pr[4 * q + 1] = w[q].y, pr[4 * q + 2] = w[q].z, pr[4 * q + 3] = w[q].w;
     }
@@ -210,7 +227,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
     for (int q = 0; q < KPT / 4; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = min(4 * (tid + kThreads * q) + e, Tc - 1);
+        const int i = min(4 * (tid + NT * q) + e, Tc - 1);
         if constexpr (GATHER) pr[4 * q + e] = ckeys[i];
         else pr[4 * q + e] = src[i];
       }
@@ -221,7 +238,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
   };
 #pragma unroll
   for (int q = 0; q < KPT / 4; ++q) {
-    const int i = 4 * (tid + kThreads * q);
+    const int i = 4 * (tid + NT * q);
     uint32_t v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -241,32 +258,32 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
   if (thr) npass = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(npass, lane), 63);
   if (lane == 0) {
     mm[wave] = lmn;
-    mm[kWaves + wave] = lmx;
-    mm[2 * kWaves + wave] = npass;
+    mm[NW + wave] = lmx;
+    mm[2 * NW + wave] = npass;
   }
   __syncthreads();  // also orders the histogram zeroing before the atomics below
   uint32_t total_pass = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     lmn = min(lmn, mm[w]);
-    lmx = max(lmx, mm[kWaves + w]);
-    total_pass += mm[2 * kWaves + w];
+    lmx = max(lmx, mm[NW + w]);
+    total_pass += mm[2 * NW + w];
   }
 
   // ---- the parts that need no ranking ----
   if (thr) {
     if (kp > 0) kp = (int)min((uint32_t)kp, total_pass);
-    for (int j = kp + wcount + tid; j < pad_to; j += kThreads) out[j] = -1;
+    for (int j = kp + wcount + tid; j < pad_to; j += NT) out[j] = -1;
     if (tid == 0 && cnt_out) *cnt_out = kp + wcount;
   }
-  for (int j = tid; j < wcount; j += kThreads) out[kp + j] = wstart + j;
+  for (int j = tid; j < wcount; j += NT) out[kp + j] = wstart + j;
   auto map = [&](int i) -> int32_t {
     if constexpr (GATHER) return cand[i];
     else return obase + i;
   };
   if (kp <= 0) return;
   if (kp >= Tc) {
-    for (int j = tid; j < Tc; j += kThreads) {
+    for (int j = tid; j < Tc; j += NT) {
       out[j] = map(j);
       if (okeys) okeys[j] = stage[padded(j)];
     }
@@ -286,7 +303,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
   uint32_t kb[KPT];
 #pragma unroll
   for (int q = 0; q < KPT / 4; ++q) {
-    const int i = 4 * (tid + kThreads * q);
+    const int i = 4 * (tid + NT * q);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float x;
@@ -298,7 +315,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
     }
   }
   __syncthreads();
-  find_bin(hist, (uint32_t)kp, scan, bcast);
+  find_bin<NT>(hist, (uint32_t)kp, scan, bcast);
   const uint32_t bin1 = bcast[0];
   const uint32_t c1 = bcast[2];                  // keys in bin1
   uint32_t remaining = (uint32_t)kp - bcast[1];  // rank of tau inside bin1, >= 1
@@ -323,7 +340,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
       while (hm) {  // the keys are read back from the staging array by position
         const int e = __builtin_ctz(hm);
         hm &= hm - 1u;
-        small[at++] = stage[padded(4 * (tid + kThreads * (e >> 2)) + (e & 3))];
+        small[at++] = stage[padded(4 * (tid + NT * (e >> 2)) + (e & 3))];
       }
     }
     __syncthreads();
@@ -362,7 +379,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
       const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
       const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
       const uint32_t pmask = pass == 0 ? 0u : pass == 1 ? 0xffe00000u : 0xfffffc00u;
-      for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+      for (int i = tid; i < kBins; i += NT) hist[i] = 0;
       __syncthreads();
 #pragma unroll
       for (int e = 0; e < KPT; ++e) {
@@ -370,7 +387,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
         if (kb[e] < (uint32_t)kBins && (x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & dmask], 1u);
       }
       __syncthreads();
-      find_bin(hist, remaining, scan, bcast);
+      find_bin<NT>(hist, remaining, scan, bcast);
       prefix |= bcast[0] << shift;
       remaining -= bcast[1];
       __syncthreads();
@@ -403,7 +420,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
   const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);  // each <= 32768
   const uint32_t incl = wave_incl_scan(packed, lane);
   uint32_t before, total;
-  block_prefix((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), scan, before, total);
+  block_prefix<NT>((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), scan, before, total);
   const uint32_t excl = before + incl - packed;
   uint32_t ngt = excl & 0xffffu, neq = excl >> 16;
   int32_t* obuf = (int32_t*)stage;
@@ -420,7 +437,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
     }
   }
   __syncthreads();
-  batched_copy<4>(kp, tid, kThreads, [&](int j) { return obuf[j]; }, [&](int j, int32_t i) {
+  batched_copy<4>(kp, tid, NT, [&](int j) { return obuf[j]; }, [&](int j, int32_t i) {
     out[j] = map(i);
     if (okeys) okeys[j] = GATHER ? ckeys[i] : float_key(src[i]);
   });
@@ -462,7 +479,7 @@ __device__ __forceinline__ void topk_global(const float* __restrict__ src, int n
   batched_copy<16>(Tc, tid, kThreads, [&](int i) { return src[i]; },
                    [&](int, float v) { atomicAdd(&hist[float_key(v) >> 21], 1u); });
   __syncthreads();
-  find_bin(hist, (uint32_t)kp, scan, bcast);
+  find_bin<kThreads>(hist, (uint32_t)kp, scan, bcast);
   const uint32_t bin1 = bcast[0];
   const uint32_t above = bcast[1];            // keys in bins above bin1
   const uint32_t nl = above + bcast[2];       // keys in bin1 or above
@@ -481,7 +498,7 @@ __device__ __forceinline__ void topk_global(const float* __restrict__ src, int n
 #pragma unroll
       for (int j = 0; j < kIPT; ++j) cnt += (uint32_t)__popcll(__ballot(w0 + j * 64 + lane < Tc && kk[j] >= lo));
       uint32_t before, total;
-      block_prefix(cnt, scan, before, total);
+      block_prefix<kThreads>(cnt, scan, before, total);
       uint32_t at = run + before;
       // the same tests as the count pass, recomputed: keeping its 16 ballots live across the
       // barrier would spill scalar registers (the empty asm hides the equality from the
@@ -506,7 +523,7 @@ __device__ __forceinline__ void topk_global(const float* __restrict__ src, int n
       if ((k >> 21) == bin1) atomicAdd(&hist[(k >> 10) & 0x7ffu], 1u);
     }
     __syncthreads();
-    find_bin(hist, remaining, scan, bcast);
+    find_bin<kThreads>(hist, remaining, scan, bcast);
     uint32_t prefix = lo | (bcast[0] << 10);
     remaining -= bcast[1];
     for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
@@ -524,7 +541,7 @@ __device__ __forceinline__ void topk_global(const float* __restrict__ src, int n
         if (tid + u * kThreads < (int)nl && (lk[u] & 0xfffffc00u) == prefix) atomicAdd(&hist[lk[u] & 0x3ffu], 1u);
     }
     __syncthreads();
-    find_bin(hist, remaining, scan, bcast);
+    find_bin<kThreads>(hist, remaining, scan, bcast);
     tau = prefix | bcast[0];
     take_eq = remaining - bcast[1];
     // ---- 3. the selection is the list filtered, in list (index) order ----
@@ -546,7 +563,7 @@ __device__ __forceinline__ void topk_global(const float* __restrict__ src, int n
       const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);
       const uint32_t incl = wave_incl_scan(packed, lane);
       uint32_t before, total;
-      block_prefix((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), scan, before, total);
+      block_prefix<kThreads>((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), scan, before, total);
       const uint32_t excl = before + incl - packed;
       uint32_t ngt = run_gt + (excl & 0xffffu), neq = run_eq + (excl >> 16);
 #pragma unroll
@@ -578,7 +595,7 @@ __device__ __forceinline__ void topk_global(const float* __restrict__ src, int n
       if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
     });
     __syncthreads();
-    find_bin(hist, remaining, scan, bcast);
+    find_bin<kThreads>(hist, remaining, scan, bcast);
     prefix |= bcast[0] << shift;
     remaining -= bcast[1];
     __syncthreads();
@@ -599,7 +616,7 @@ __device__ __forceinline__ void topk_global(const float* __restrict__ src, int n
       weq += (uint32_t)__popcll(__ballot(valid && kk[j] == tau));
     }
     uint32_t before, total;
-    block_prefix(wgt | (weq << 16), scan, before, total);
+    block_prefix<kThreads>(wgt | (weq << 16), scan, before, total);
     uint32_t ngt = run_gt + (before & 0xffffu), neq = run_eq + (before >> 16);
 #pragma unroll
     for (int j = 0; j < kIPT; ++j) {
@@ -619,17 +636,17 @@ __device__ __forceinline__ void topk_global(const float* __restrict__ src, int n
   }
 }
 
-// One row per workgroup: rows of up to kThreads * KPT keys in registers (KPT > 0), longer rows
-// from global memory (KPT == 0).
-template <int KPT>
-__global__ __launch_bounds__(kThreads) void topk_window_kernel(const float* __restrict__ S,
+// One row per workgroup of NT threads: rows of up to NT * KPT keys in registers (KPT > 0), longer
+// rows from global memory (KPT == 0, NT = kThreads).
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_window_kernel(const float* __restrict__ S,
                                                                int32_t* __restrict__ sel, int Tc,
                                                                int ldS, int kp, int ctx, int n_sel,
                                                                bool vec, bool thr, uint32_t tkey,
                                                                int32_t* __restrict__ cnt) {
   const int row = blockIdx.x;
   if constexpr (KPT > 0)
-    topk_rows<KPT, false>(S + (size_t)row * ldS, nullptr, nullptr, Tc, kp, sel + (size_t)row * n_sel, nullptr, 0,
+    topk_rows<NT, KPT, false>(S + (size_t)row * ldS, nullptr, nullptr, Tc, kp, sel + (size_t)row * n_sel, nullptr, 0,
                           ctx - Tc, Tc, vec, thr, tkey, cnt ? cnt + row : nullptr, n_sel);
   else
     topk_global(S + (size_t)row * ldS, Tc, kp, sel + (size_t)row * n_sel, ctx - Tc, Tc, thr, tkey,
@@ -650,7 +667,7 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __res
   const int row = blockIdx.x / ns, s = blockIdx.x % ns;
   const int s0 = s * slen, n = min(slen, Tc - s0);
   const size_t o = ((size_t)row * ns + s) * kp;
-  topk_rows<KPT, false>(S + (size_t)row * ldS + s0, nullptr, nullptr, n, kp, cand + o, ckeys + o, s0, 0, 0, vec,
+  topk_rows<kThreads, KPT, false>(S + (size_t)row * ldS + s0, nullptr, nullptr, n, kp, cand + o, ckeys + o, s0, 0, 0, vec,
                         false, 0u, nullptr, 0);
 }
 
@@ -662,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const int32_t* __r
                                                               uint32_t tkey, int32_t* __restrict__ cnt) {
   const int row = blockIdx.x;
   const size_t o = (size_t)row * ns * kp;
-  topk_rows<KPT, true>(nullptr, cand + o, ckeys + o, ns * kp, kp, sel + (size_t)row * n_sel, nullptr, 0, ctx - Tc,
+  topk_rows<kThreads, KPT, true>(nullptr, cand + o, ckeys + o, ns * kp, kp, sel + (size_t)row * n_sel, nullptr, 0, ctx - Tc,
                        Tc, false, thr, tkey, cnt ? cnt + row : nullptr, n_sel);
 }
 
@@ -707,8 +724,18 @@ hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, i
     case 16: CALL(16); break;      \
     default: CALL(32); break;      \
   }
-  if (Tc <= kLdsKeys) {
-#define SALS_ROWS(K) topk_window_kernel<K><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt)
+  if (Tc <= kShortRow) {
+    // short rows: a 256-thread workgroup (up to 16 keys per thread), whose barriers and block
+    // scans span 4 waves instead of 16
+#define SALS_SHORT(K) \
+  topk_window_kernel<kShortThreads, K><<<rows, kShortThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt)
+    if (Tc <= 4 * kShortThreads) SALS_SHORT(4);
+    else if (Tc <= 8 * kShortThreads) SALS_SHORT(8);
+    else SALS_SHORT(16);
+#undef SALS_SHORT
+  } else if (Tc <= kLdsKeys) {
+#define SALS_ROWS(K) \
+  topk_window_kernel<kThreads, K><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt)
     SALS_KPT_SWITCH(Tc, SALS_ROWS)
 #undef SALS_ROWS
   } else if (ns > 0) {
@@ -721,7 +748,7 @@ hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, i
     SALS_KPT_SWITCH(ns * kp, SALS_MERGE)
 #undef SALS_MERGE
   } else {
-    topk_window_kernel<0><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt);
+    topk_window_kernel<kThreads, 0><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt);
   }
 #undef SALS_KPT_SWITCH
   return hipGetLastError();
