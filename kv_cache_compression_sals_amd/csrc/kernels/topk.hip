@@ -39,6 +39,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kShortThreads = 256;              // workgroup of the short-row kernel
 constexpr int kShortRow = 16 * kShortThreads;   // longest short row (16 keys per thread)
+constexpr int kMaxSlices = 64;                  // slices of a long row
 constexpr int kLdsKeys = 32768;
 constexpr int kBins = 2048;
 constexpr int kIPT = 16;     // keys per lane per chunk when a wave ranks a run (16 slices of 64)
@@ -173,26 +174,31 @@ __device__ __forceinline__ int padded(int i) { return i + ((i >> 5) << 2); }
 // selected, so kp becomes min(kp, #keys >= tkey); out[kp + wcount .. pad_to) is filled with -1
 // and *cnt_out receives kp + wcount. For GATHER the count runs over the candidates: a row with
 // fewer than kp passing keys has all of them among the candidates, otherwise at least kp pass
-// there too, so min(kp, count) is the row's.
+// there too, so min(kp, count) is the row's. With tcheck (GATHER, tcheck[0 .. ntcheck) the
+// threshold keys of the slices the candidates came from) the selection is exact only if its
+// threshold key exceeds their maximum T; otherwise topk_rows writes no selection and returns false
+// (the same in every thread). It returns true when the selection is written.
 template <int NT, int KPT, bool GATHER>
-__device__ __forceinline__ void topk_rows(const float* __restrict__ src, const int32_t* __restrict__ cand,
+__device__ __forceinline__ bool topk_rows(const float* __restrict__ src, const int32_t* __restrict__ cand,
                                           const uint32_t* __restrict__ ckeys, int n, int kp,
                                           int32_t* __restrict__ out, uint32_t* __restrict__ okeys,
                                           int obase, int wcount, int wstart, bool vec, bool thr,
-                                          uint32_t tkey, int32_t* __restrict__ cnt_out, int pad_to) {
+                                          uint32_t tkey, int32_t* __restrict__ cnt_out, int pad_to,
+                                          uint32_t* __restrict__ tau_out = nullptr,
+                                          const uint32_t* __restrict__ tcheck = nullptr, int ntcheck = 0) {
   static_assert(KPT % 4 == 0 && KPT <= 32 && NT * KPT <= kLdsKeys, "keys per thread");
   constexpr int NW = NT / 64;
   constexpr int kStage = NT * KPT / 32 * 36;  // staging words for NT * KPT keys
   // staged keys (padded layout); after the ranking, the selection's positions in output order
   __shared__ __attribute__((aligned(16))) uint32_t stage[kStage];
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins + 4];  // [kBins]: keys past the row
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
   __shared__ __attribute__((aligned(16))) uint32_t scan[NW];
   __shared__ uint32_t bcast[4];
-  __shared__ uint32_t mm[3 * NW];  // per-wave key minima, maxima and threshold counts
+  __shared__ uint32_t mm[4 * NW];  // per-wave key minima, maxima, threshold counts, tcheck maxima
   __shared__ uint32_t nsmall, tsel[2];  // small-bin gather count; (tau, take_eq)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Tc = n;
-  for (int i = tid; i < kBins + 4; i += NT) hist[i] = 0;
+  for (int i = tid; i < kBins; i += NT) hist[i] = 0;
   if (tid == 0) nsmall = 0;
 
   // ---- 1. coalesced loads: this thread's 16-byte pieces u = tid + NT * q hold positions
@@ -206,6 +212,8 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
   // element by element at clamped positions. Every load is unconditional so that all are in
   // flight together.
   const bool v4 = GATHER ? (((uintptr_t)ckeys & 15) == 0 && (Tc & 3) == 0) : vec;
+  uint32_t tmx = 0u;  // threads below ntcheck: that slice's threshold key
+  if (GATHER && tcheck) tmx = tcheck[min(tid, ntcheck - 1)];
   // (two separate loops: merged, the compiler would split the 16-byte loads into single words)
   if (Tc > 0 && v4) {
     const int last4 = ((Tc + 3) & ~3) - 4;
@@ -254,12 +262,14 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
   for (int o = 1; o < 64; o <<= 1) {
     lmn = min(lmn, (uint32_t)__shfl_xor((int)lmn, o));
     lmx = max(lmx, (uint32_t)__shfl_xor((int)lmx, o));
+    if (GATHER && tcheck) tmx = max(tmx, (uint32_t)__shfl_xor((int)tmx, o));
   }
   if (thr) npass = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(npass, lane), 63);
   if (lane == 0) {
     mm[wave] = lmn;
     mm[NW + wave] = lmx;
     mm[2 * NW + wave] = npass;
+    if constexpr (GATHER) mm[3 * NW + wave] = tmx;
   }
   __syncthreads();  // also orders the histogram zeroing before the atomics below
   uint32_t total_pass = 0;
@@ -268,6 +278,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
     lmn = min(lmn, mm[w]);
     lmx = max(lmx, mm[NW + w]);
     total_pass += mm[2 * NW + w];
+    if constexpr (GATHER) tmx = max(tmx, mm[3 * NW + w]);
   }
 
   // ---- the parts that need no ranking ----
@@ -281,20 +292,25 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
     if constexpr (GATHER) return cand[i];
     else return obase + i;
   };
-  if (kp <= 0) return;
+  // tau_out: the selection's threshold key (0, the smallest key, when every key is selected)
+  if (kp <= 0 || kp >= Tc) {
+    if (tau_out && tid == 0) *tau_out = 0u;
+  }
+  if (kp <= 0) return true;
   if (kp >= Tc) {
     for (int j = tid; j < Tc; j += NT) {
       out[j] = map(j);
       if (okeys) okeys[j] = stage[padded(j)];
     }
-    return;
+    return true;
   }
 
   // ---- 2. histogram of equal-width value bins over the range ----
   // bin(k) = clamp(floor(value(k) * s + o), 0, kBins - 1) with s = kBins / (max - min) and
   // o = -min * s: one fused multiply-add is monotone in the value, so a larger key never lands
   // in a lower bin, and equal keys share a bin. A range that is empty or not finite
-  // (infinities, NaN) puts every key in bin 0. Positions past the row count in hist[kBins].
+  // (infinities, NaN) puts every key in bin 0. Positions past the row get bin kBins and are not
+  // counted (all of them on one counter would serialise the atomics of whole waves).
   const float vmin = key_value(lmn), vmax = key_value(lmx);
   const float span = __fsub_rn(vmax, vmin);
   float scale = __fdiv_rn((float)kBins, span);
@@ -311,7 +327,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
       else x = pr[4 * q + e];
       const float t = fminf(fmaxf(__fmaf_rn(x, scale, off), 0.f), (float)(kBins - 1));
       kb[4 * q + e] = i + e < Tc ? (uint32_t)t : (uint32_t)kBins;
-      atomicAdd(&hist[kb[4 * q + e]], 1u);
+      if (i + e < Tc) atomicAdd(&hist[kb[4 * q + e]], 1u);
     }
   }
   __syncthreads();
@@ -396,6 +412,9 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
     take_eq = remaining;  // >= 1
   }
 
+  if (tau_out && tid == 0) *tau_out = tau;
+  if (GATHER && tcheck && tau <= tmx) return false;  // tau and tmx are the same in every thread
+
   // ---- 4. ordered compaction over this thread's KPT consecutive keys (from t * KPT): its output
   //      slots start at the number of selected keys before its first key (a block prefix sum of
   //      its counts); the positions go to LDS in output order (over the staged keys, read for the
@@ -441,6 +460,7 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ src, const i
     out[j] = map(i);
     if (okeys) okeys[j] = GATHER ? ckeys[i] : float_key(src[i]);
   });
+  return true;
 }
 
 // The selection of a row read from global memory (rows beyond the LDS staging array that are not
@@ -654,33 +674,51 @@ __global__ __launch_bounds__(NT) void topk_window_kernel(const float* __restrict
 }
 
 // Rows longer than the register-resident limit: one workgroup per (row, slice of slen keys) keeps
-// the kp largest of its slice (ties to the lowest position) as candidates, in ascending position
-// order, with their keys. Every element of the row's top kp is among its slice's top kp, with the
-// lowest-index ties of the row's threshold key included, so the row's selection over the
-// candidates (which are in ascending position order across slices) is exact.
-template <int KPT>
-__global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __restrict__ S,
-                                                              int32_t* __restrict__ cand,
-                                                              uint32_t* __restrict__ ckeys, int Tc,
-                                                              int ldS, int kp, int slen, int ns,
-                                                              bool vec) {
+// the m largest of its slice (ties to the lowest position) as candidates, in ascending position
+// order, with their keys, and writes its threshold key (the m-th largest) to taus. With m = kp
+// every element of the row's top kp is among its slice's top kp, with the lowest-index ties of the
+// row's threshold key included, so the row's selection over the candidates (in ascending position
+// order across slices) is exact. With m < kp (about twice a slice's expected share of the row's
+// top kp) the merge checks that this still holds.
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_slice_kernel(const float* __restrict__ S,
+                                                        int32_t* __restrict__ cand,
+                                                        uint32_t* __restrict__ ckeys,
+                                                        uint32_t* __restrict__ taus, int Tc, int ldS,
+                                                        int m, int slen, int ns, bool vec) {
   const int row = blockIdx.x / ns, s = blockIdx.x % ns;
   const int s0 = s * slen, n = min(slen, Tc - s0);
-  const size_t o = ((size_t)row * ns + s) * kp;
-  topk_rows<kThreads, KPT, false>(S + (size_t)row * ldS + s0, nullptr, nullptr, n, kp, cand + o, ckeys + o, s0, 0, 0, vec,
-                        false, 0u, nullptr, 0);
+  const size_t o = ((size_t)row * ns + s) * m;
+  topk_rows<NT, KPT, false>(S + (size_t)row * ldS + s0, nullptr, nullptr, n, m, cand + o, ckeys + o, s0, 0, 0, vec,
+                            false, 0u, nullptr, 0, taus + (size_t)row * ns + s);
 }
 
+// The row's selection over its slices' candidates. With m < kp the candidates may miss part of
+// the row's top kp: a key a slice dropped is at most that slice's threshold key, so with T the
+// largest slice threshold, a selection whose threshold key exceeds T contains no dropped key and
+// misses none. That holds exactly when at least kp candidates exceed T (the kp-th largest
+// candidate then exceeds T). Otherwise the row is selected from the scores themselves
+// (topk_global): exact either way.
 template <int KPT>
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const int32_t* __restrict__ cand,
                                                               const uint32_t* __restrict__ ckeys,
+                                                              const uint32_t* __restrict__ taus,
                                                               int32_t* __restrict__ sel, int Tc, int kp,
-                                                              int ns, int ctx, int n_sel, bool thr,
-                                                              uint32_t tkey, int32_t* __restrict__ cnt) {
+                                                              int ns, int m, int ctx, int n_sel, bool thr,
+                                                              uint32_t tkey, int32_t* __restrict__ cnt,
+                                                              const float* __restrict__ S, int ldS) {
   const int row = blockIdx.x;
-  const size_t o = (size_t)row * ns * kp;
-  topk_rows<kThreads, KPT, true>(nullptr, cand + o, ckeys + o, ns * kp, kp, sel + (size_t)row * n_sel, nullptr, 0, ctx - Tc,
-                       Tc, false, thr, tkey, cnt ? cnt + row : nullptr, n_sel);
+  const size_t o = (size_t)row * ns * m;
+  // (the reduced plan keeps at most kLdsKeys / 2 candidates: merges of more keys per thread are
+  // only used with m = kp, whose selection needs no check, and leave no LDS for the fallback)
+  const bool check = KPT <= 16 && m < kp;
+  if (!topk_rows<kThreads, KPT, true>(nullptr, cand + o, ckeys + o, ns * m, kp, sel + (size_t)row * n_sel, nullptr, 0,
+                                      ctx - Tc, Tc, false, thr, tkey, cnt ? cnt + row : nullptr, n_sel, nullptr,
+                                      check ? taus + (size_t)row * ns : nullptr, ns)) {
+    if constexpr (KPT <= 16)
+      topk_global(S + (size_t)row * ldS, Tc, kp, sel + (size_t)row * n_sel, ctx - Tc, Tc, thr, tkey,
+                  cnt ? cnt + row : nullptr, n_sel);
+  }
 }
 
 // Keys per thread for a register-resident row of n keys (n <= kLdsKeys).
@@ -688,19 +726,49 @@ int keys_per_thread(int n) { return n <= 4 * kThreads ? 4 : n <= 8 * kThreads ? 
 
 }  // namespace
 
-int topk_slices(int Tc, int kp, int* slen) {
+// Slices of a row of Tc candidates, rows rows: ns slices of *slen keys, each keeping its top *m
+// (0: the row is not split). Rows up to the register-resident limit are not split. Otherwise
+// (reduce, i.e. not in threshold mode) the row is cut into about one slice per CU over all rows,
+// each keeping twice its expected share of the top kp (plus 32), when that fits; else into the
+// fewest slices that fit, each keeping kp.
+int topk_slices(int rows, int Tc, int kp, bool reduce, int* slen, int* m) {
   if (Tc <= kLdsKeys || kp <= 0) return 0;
+  auto fits = [&](int ns, int mm, int* len_out) {
+    const int len = (ceil_div(Tc, ns) + 3) / 4 * 4;
+    const int last = Tc - (ns - 1) * len;
+    if (len > kLdsKeys || last <= mm || (long)ns * mm > kLdsKeys) return false;
+    *len_out = len;
+    return true;
+  };
+  int len = 0;
+  if (reduce) {
+    int ns = ceil_div(256, rows > 0 ? rows : 1);
+    if (ns < ceil_div(Tc, kLdsKeys)) ns = ceil_div(Tc, kLdsKeys);
+    if (ns > kMaxSlices) ns = kMaxSlices;
+    const int mm = (2 * ceil_div(kp, ns) + 32 + 31) / 32 * 32;
+    if (mm < kp && (long)ns * mm <= kLdsKeys / 2 && fits(ns, mm, &len)) {
+      if (slen) *slen = len;
+      if (m) *m = mm;
+      return ns;
+    }
+  }
   const int ns = ceil_div(Tc, kLdsKeys);
-  const int len = (ceil_div(Tc, ns) + 3) / 4 * 4;
-  const int last = Tc - (ns - 1) * len;
-  if (len > kLdsKeys || last <= kp || (long)ns * kp > kLdsKeys) return 0;
+  if (!fits(ns, kp, &len)) return 0;
   if (slen) *slen = len;
+  if (m) *m = kp;
   return ns;
 }
 
 size_t topk_candidate_bytes(int rows, int Tc, int kp) {
-  const int ns = topk_slices(Tc, kp, nullptr);
-  return ns ? (size_t)rows * ns * kp * 8 : 0;  // positions, then keys
+  size_t best = 0;
+  for (int reduce = 0; reduce < 2; ++reduce) {
+    int m = 0;
+    const int ns = topk_slices(rows, Tc, kp, reduce != 0, nullptr, &m);
+    // positions, then keys, then the slices' threshold keys
+    const size_t b = ns ? (size_t)rows * ns * m * 8 + (size_t)rows * ns * 4 : 0;
+    if (b > best) best = b;
+  }
+  return best;
 }
 
 uint32_t threshold_key(float tau) {
@@ -715,8 +783,8 @@ hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, i
                               int32_t* cnt) {
   if (rows <= 0) return hipSuccess;
   const bool vec = (ldS & 3) == 0 && ((uintptr_t)S & 15) == 0;
-  int slen = 0;
-  const int ns = cand ? topk_slices(Tc, kp, &slen) : 0;
+  int slen = 0, m = 0;
+  const int ns = cand ? topk_slices(rows, Tc, kp, !thr, &slen, &m) : 0;
 #define SALS_KPT_SWITCH(N, CALL) \
   switch (keys_per_thread(N)) {    \
     case 4: CALL(4); break;        \
@@ -739,13 +807,25 @@ hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, i
     SALS_KPT_SWITCH(Tc, SALS_ROWS)
 #undef SALS_ROWS
   } else if (ns > 0) {
-    uint32_t* ckeys = (uint32_t*)(cand + (size_t)rows * ns * kp);
-#define SALS_SLICE(K) topk_slice_kernel<K><<<rows * ns, kThreads, 0, st>>>(S, cand, ckeys, Tc, ldS, kp, slen, ns, vec)
-    SALS_KPT_SWITCH(slen, SALS_SLICE)
+    uint32_t* ckeys = (uint32_t*)(cand + (size_t)rows * ns * m);
+    uint32_t* taus = ckeys + (size_t)rows * ns * m;
+    if (slen <= kShortRow) {
+#define SALS_SHORT_SLICE(K) \
+  topk_slice_kernel<kShortThreads, K><<<rows * ns, kShortThreads, 0, st>>>(S, cand, ckeys, taus, Tc, ldS, m, slen, ns, vec)
+      if (slen <= 4 * kShortThreads) SALS_SHORT_SLICE(4);
+      else if (slen <= 8 * kShortThreads) SALS_SHORT_SLICE(8);
+      else SALS_SHORT_SLICE(16);
+#undef SALS_SHORT_SLICE
+    } else {
+#define SALS_SLICE(K) \
+  topk_slice_kernel<kThreads, K><<<rows * ns, kThreads, 0, st>>>(S, cand, ckeys, taus, Tc, ldS, m, slen, ns, vec)
+      SALS_KPT_SWITCH(slen, SALS_SLICE)
 #undef SALS_SLICE
-#define SALS_MERGE(K) \
-  topk_merge_kernel<K><<<rows, kThreads, 0, st>>>(cand, ckeys, sel, Tc, kp, ns, ctx, n_sel, thr, tkey, cnt)
-    SALS_KPT_SWITCH(ns * kp, SALS_MERGE)
+    }
+#define SALS_MERGE(K)                                                                                  \
+  topk_merge_kernel<K><<<rows, kThreads, 0, st>>>(cand, ckeys, taus, sel, Tc, kp, ns, m, ctx, n_sel, thr, tkey, \
+                                                  cnt, S, ldS)
+    SALS_KPT_SWITCH(ns * m, SALS_MERGE)
 #undef SALS_MERGE
   } else {
     topk_window_kernel<kThreads, 0><<<rows, kThreads, 0, st>>>(S, sel, Tc, ldS, kp, ctx, n_sel, vec, thr, tkey, cnt);

@@ -29,14 +29,14 @@ hipError_t launch_latent_score(int dtype, const float* qpart, int npart, const v
 
 // sel[row][0 .. kp) = top-kp of S[row][0 .. Tc) (ties to the lowest index), ascending;
 // sel[row][kp .. n_sel) = Tc .. ctx-1. Rows of S are ldS floats apart. Rows longer than 32768
-// candidates are split into topk_slices(...) slices whose candidates (positions, then their
-// keys: topk_candidate_bytes(...) bytes) go to `cand`; with cand null, or no valid split, one
-// workgroup per row reads the row from memory in every pass instead.
+// candidates are split into topk_slices(...) slices whose candidates (positions, their keys and
+// the slices' threshold keys: at most topk_candidate_bytes(...) bytes) go to `cand`; with cand
+// null, or no valid split, one workgroup per row reads the row from memory in every pass instead.
 // Threshold mode (thr): a row keeps only the candidates whose key is at least tkey
 // (float_key of the threshold), at most kp of them, so its top-k count is min(kp, #passing);
 // the window follows them, the rest of the row (up to n_sel) is filled with -1, and cnt[row]
 // receives the row's length (count + window).
-int topk_slices(int Tc, int kp, int* slen);
+int topk_slices(int rows, int Tc, int kp, bool reduce, int* slen, int* m);
 size_t topk_candidate_bytes(int rows, int Tc, int kp);
 hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, int Tc, int kp,
                               int ctx, int n_sel, int32_t* cand, hipStream_t st, bool thr = false,

@@ -59,6 +59,14 @@ def _split_scores(name, T):
         return s
     if name == "ascending":
         return np.linspace(-3.0, 3.0, T).astype(np.float32)
+    if name == "gaussian":
+        return rs.standard_normal(T).astype(np.float32)
+    if name == "gaussian_hot_region":
+        # one region of 4000 tokens scores far above the rest: the slices that hold it would
+        # drop part of the row's top k if each kept only its share
+        s = rs.standard_normal(T).astype(np.float32)
+        s[T // 3: T // 3 + 4000] += 4.0
+        return s
     raise ValueError(name)
 
 
@@ -68,6 +76,9 @@ SPLIT = [("ties_across_slices", 8000, 1000, 16), ("two_values", 6000, 2500, 8),
          # rows past 32768 candidates: per-slice candidates, then one selection over them
          ("ties_across_slices", 70000, 4000, 16), ("two_values", 50000, 9000, 8),
          ("list_overflow", 100000, 6000, 64), ("ascending", 90000, 5000, 0),
+         # untied scores: each slice keeps about twice its share of the top k, checked at the merge;
+         # with a hot region the check fails and the row is selected from its scores
+         ("gaussian", 100000, 3000, 32), ("gaussian_hot_region", 100000, 3000, 32),
          # too many candidates for the slice path: one workgroup reads the row in every pass
          ("two_values", 40000, 20000, 0)]
 
