@@ -168,8 +168,8 @@ __device__ __forceinline__ int padded(int i) { return i + ((i >> 5) << 2); }
 // The selection of one workgroup over at most kThreads * KPT keys (thread t owns the KPT
 // consecutive keys from t * KPT and holds them in registers): the kp largest of n keys, ties to
 // the lowest position, written to out[0 .. kp) in ascending position order as map(position)
-// (and, with okeys, their keys to okeys[0 .. kp)), followed by the window out[kp + j] =
-// wstart + j, j < wcount. Keys are float_key(src[i]) with map(i) = obase + i, or (GATHER) the
+// (and, with okeys, for rows of scores only, their keys to okeys[0 .. kp)), followed by the
+// window out[kp + j] = wstart + j, j < wcount. Keys are float_key(src[i]) with map(i) = obase + i, or (GATHER) the
 // given keys ckeys[i] with map(i) = cand[i]. Threshold mode (thr): only keys >= tkey may be
 // selected, so kp becomes min(kp, #keys >= tkey); out[kp + wcount .. pad_to) is filled with -1
 // and *cnt_out receives kp + wcount. For GATHER the count runs over the candidates: a row with
@@ -240,6 +240,23 @@ __device__ __forceinline__ bool topk_rows(const float* __restrict__ src, const i
         else pr[4 * q + e] = src[i];
       }
   }
+  // GATHER: the positions of this thread's KPT consecutive candidates (from t * KPT, the keys its
+  // compaction walks), loaded with the keys so that the output needs no dependent gather
+  int32_t cp[GATHER ? KPT : 1];
+  if constexpr (GATHER) {
+    const int c0 = tid * KPT;
+    if (Tc > 0 && v4 && ((uintptr_t)cand & 15) == 0) {
+      const int last4 = ((Tc + 3) & ~3) - 4;
+#pragma unroll
+      for (int q = 0; q < KPT / 4; ++q) {
+        const int4 w = *(const int4*)(cand + min(c0 + 4 * q, last4));
+        cp[4 * q] = w.x, cp[4 * q + 1] = w.y, cp[4 * q + 2] = w.z, cp[4 * q + 3] = w.w;
+      }
+    } else if (Tc > 0) {
+#pragma unroll
+      for (int e = 0; e < KPT; ++e) cp[e] = cand[min(c0 + e, Tc - 1)];
+    }
+  }
   auto key_of = [&](int e) -> uint32_t {
     if constexpr (GATHER) return pr[e];
     else return float_key(pr[e]);
@@ -271,7 +288,9 @@ __device__ __forceinline__ bool topk_rows(const float* __restrict__ src, const i
     mm[2 * NW + wave] = npass;
     if constexpr (GATHER) mm[3 * NW + wave] = tmx;
   }
-  __syncthreads();  // also orders the histogram zeroing before the atomics below
+  // (LDS only: also orders the histogram zeroing before the atomics below; GATHER's position loads
+  // stay in flight)
+  lds_barrier();
   uint32_t total_pass = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -442,23 +461,40 @@ __device__ __forceinline__ bool topk_rows(const float* __restrict__ src, const i
   block_prefix<NT>((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), scan, before, total);
   const uint32_t excl = before + incl - packed;
   uint32_t ngt = excl & 0xffffu, neq = excl >> 16;
-  int32_t* obuf = (int32_t*)stage;
-  uint32_t m = fgt | feq;
-  while (m) {
-    const int e = __builtin_ctz(m);
-    m &= m - 1u;
-    if ((fgt >> e) & 1u) {
-      obuf[ngt + min(neq, take_eq)] = b0 + e;
-      ++ngt;
-    } else {
-      if (neq < take_eq) obuf[ngt + neq] = b0 + e;
-      ++neq;
+  int32_t* obuf = (int32_t*)stage;  // GATHER: the candidates' positions; else indices into the row
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {  // static register indices
+      if ((fgt >> e) & 1u) {
+        obuf[ngt + min(neq, take_eq)] = cp[e];
+        ++ngt;
+      } else if ((feq >> e) & 1u) {
+        if (neq < take_eq) obuf[ngt + neq] = cp[e];
+        ++neq;
+      }
+    }
+  } else {
+    uint32_t m = fgt | feq;
+    while (m) {
+      const int e = __builtin_ctz(m);
+      m &= m - 1u;
+      if ((fgt >> e) & 1u) {
+        obuf[ngt + min(neq, take_eq)] = b0 + e;
+        ++ngt;
+      } else {
+        if (neq < take_eq) obuf[ngt + neq] = b0 + e;
+        ++neq;
+      }
     }
   }
   __syncthreads();
   batched_copy<4>(kp, tid, NT, [&](int j) { return obuf[j]; }, [&](int j, int32_t i) {
-    out[j] = map(i);
-    if (okeys) okeys[j] = GATHER ? ckeys[i] : float_key(src[i]);
+    if constexpr (GATHER) {
+      out[j] = i;
+    } else {
+      out[j] = obase + i;
+      if (okeys) okeys[j] = float_key(src[i]);
+    }
   });
   return true;
 }
