@@ -35,14 +35,13 @@ constexpr int kMinChunk = 32;   // shortest chunk made by subdividing a split
 // 16-byte chunk (row starts then fall on different banks):
 //   rowsT[CB][ts]        gathered row pieces, transposed (column-major: tokens contiguous)
 //   pA[NP][hs16][ts]     probabilities of the chunk (bf16: high and low parts, NP = 2)
-//   pos[cl]              int32 positions of the chunk
 template <class T>
 struct VSLayout {
   static constexpr int ESZ = (int)sizeof(typename T::elem);
   static constexpr int NP = T::HILO ? 2 : 1;
   __host__ __device__ static int ts(int cl) { return cl + 16 / ESZ; }
   static size_t bytes(int cb, int hs16, int cl) {
-    return (size_t)(cb + NP * hs16) * ts(cl) * ESZ + (size_t)cl * 4;
+    return (size_t)(cb + NP * hs16) * ts(cl) * ESZ;
   }
 };
 
@@ -77,109 +76,152 @@ __global__ __launch_bounds__(kThreads) void value_sum_kernel(
   const int ts = LY::ts(cl);
   elem* rowsT = (elem*)vs_smem;
   elem* pA = rowsT + (size_t)CB * ts;
-  int32_t* pos = (int32_t*)(pA + (size_t)LY::NP * hs16 * ts);
   const int h0 = s * HS;
   const int nsp = (n_sel + 3) & ~3;  // row stride of pbuf
 
-  // ---- 1. positions, probabilities and split stats, all requested before the first wait ----
-  int32_t sv[kCLMax / kThreads];
-  if (nt > 0) {
-    const int32_t* selrow = sel + (size_t)bs * n_sel + t0;
+  // ---- 1-2. probabilities (unit: 4 tokens of one head; zero past the chunk and for padding
+  //      heads) and row pieces (unit: token pair i, 16-byte chunk cc; tokens past the chunk repeat
+  //      its last row, whose probabilities are zero), both staged in LDS, the pieces transposed.
+  //      The first batch of every load is issued before any is consumed: the positions of this
+  //      thread's pieces straight from the selection (no LDS round trip), the probabilities, then
+  //      the gathered pieces; the probabilities and the split statistics are written while the
+  //      pieces are in flight. ----
+  const int nq = ntp / 4, npu = hs16 * nq;   // probability units
+  const int np2 = ntp / 2, nru = np2 * CPR;  // row-piece units
+  const int32_t* selrow = sel + (size_t)bs * n_sel + t0;
+  const float* prow0 = pbuf + ((size_t)b * H_q + h0) * nsp + t0;
+  const elem* vbase = Lv + (size_t)b * ctx_cap * r + cb * CB;
+  auto row_pos = [&](int e0, int32_t (&pp)[4][2]) {
 #pragma unroll
-    for (int k = 0; k < kCLMax / kThreads; ++k) sv[k] = selrow[min(tid + k * kThreads, nt - 1)];
-  }
-  {
-    // 4 tokens per unit; zero past the chunk and for padding heads
-    const int nq = ntp / 4;
-    const float* prow0 = pbuf + ((size_t)b * H_q + h0) * nsp + t0;
-    for (int e0 = tid; e0 < hs16 * nq; e0 += 4 * kThreads) {
-      u32x4 v[4];
+    for (int k = 0; k < 4; ++k) {
+      const int i = min(e0 + k * kThreads, nru - 1) % np2;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e = min(e0 + k * kThreads, hs16 * nq - 1);
-        const int hl = min(e / nq, HS - 1), q = min(e % nq, (nt - 1) / 4);
-        v[k] = *(const u32x4*)(prow0 + (size_t)hl * nsp + 4 * q);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e = e0 + k * kThreads;
-        if (e < hs16 * nq) {
-          const int hl = e / nq, q = e % nq;
-          float x[4];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) x[m] = (hl < HS && 4 * q + m < nt) ? __uint_as_float(v[k][m]) : 0.f;
-          elem* dst = pA + (size_t)hl * ts + 4 * q;
-          if constexpr (T::HILO) {
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              hi[m] = f32_to_bf16_bits(x[m]);
-              lo[m] = f32_to_bf16_bits(x[m] - bf16_bits_to_f32(hi[m]));
-            }
-            *(uint2*)dst = make_uint2(hi[0] | hi[1] << 16, hi[2] | hi[3] << 16);
-            *(uint2*)(dst + (size_t)hs16 * ts) = make_uint2(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16);
-          } else {
-            *(u32x4*)dst = u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
-                                 __float_as_uint(x[3])};
-          }
-        }
-      }
+      for (int h = 0; h < 2; ++h) pp[k][h] = selrow[min(2 * i + h, nt - 1)];
     }
-  }
-  if (nt > 0) {
+  };
+  auto row_load = [&](int e0, const int32_t (&pp)[4][2], u32x4 (&v)[4][2]) {
 #pragma unroll
-    for (int k = 0; k < kCLMax / kThreads; ++k)
-      if (tid + k * kThreads < nt) pos[tid + k * kThreads] = sv[k];
-  }
-  // merge weight of this chunk's split per head: e^{m_split - M} / L over all splits
-  if (tid < HS) {
-    const float* st = pstat + ((size_t)b * H_q + h0 + tid) * n_splits * 2;
-    float M = -INFINITY;
-    for (int k = 0; k < n_splits; ++k) M = fmaxf(M, st[2 * k]);
-    float L = 0.f;
-    for (int k = 0; k < n_splits; ++k) L += st[2 * k + 1] * expf(st[2 * k] - M);
-    wsh[tid] = expf(st[2 * sp] - M) / L;
-  }
-  __syncthreads();
-
-  // ---- 2. row pieces, transposed: unit = (token pair i, chunk cc); tokens past the chunk
-  // repeat its last row (their probabilities are zero) ----
-  if (nt > 0) {
-    const int np2 = ntp / 2;
-    const elem* vbase = Lv + (size_t)b * ctx_cap * r + cb * CB;
-    for (int e0 = tid; e0 < np2 * CPR; e0 += 4 * kThreads) {
-      u32x4 v[4][2];
+    for (int k = 0; k < 4; ++k) {
+      const int cc = min(e0 + k * kThreads, nru - 1) / np2;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e = min(e0 + k * kThreads, np2 * CPR - 1);
+      for (int h = 0; h < 2; ++h) v[k][h] = *(const u32x4*)(vbase + (size_t)pp[k][h] * r + cc * EPC);
+    }
+  };
+  auto row_store = [&](int e0, const u32x4 (&v)[4][2]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = e0 + k * kThreads;
+      if (e < nru) {
         const int i = e % np2, cc = e / np2;
+        elem* dst = rowsT + (size_t)cc * EPC * ts + 2 * i;
+        if constexpr (sizeof(elem) == 2) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          v[k][h] = *(const u32x4*)(vbase + (size_t)pos[min(2 * i + h, nt - 1)] * r + cc * EPC);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int e = e0 + k * kThreads;
-        if (e < np2 * CPR) {
-          const int i = e % np2, cc = e / np2;
-          elem* dst = rowsT + (size_t)cc * EPC * ts + 2 * i;
-          if constexpr (sizeof(elem) == 2) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              // columns 2j and 2j+1 of tokens 2i and 2i+1
-              const uint32_t a = v[k][0][j], bb = v[k][1][j];
-              *(uint32_t*)(dst + (size_t)(2 * j) * ts) = (a & 0xffffu) | (bb << 16);
-              *(uint32_t*)(dst + (size_t)(2 * j + 1) * ts) = (a >> 16) | (bb & 0xffff0000u);
-            }
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) *(uint2*)(dst + (size_t)j * ts) = make_uint2(v[k][0][j], v[k][1][j]);
+          for (int j = 0; j < 4; ++j) {
+            // columns 2j and 2j+1 of tokens 2i and 2i+1
+            const uint32_t a = v[k][0][j], bb = v[k][1][j];
+            *(uint32_t*)(dst + (size_t)(2 * j) * ts) = (a & 0xffffu) | (bb << 16);
+            *(uint32_t*)(dst + (size_t)(2 * j + 1) * ts) = (a >> 16) | (bb & 0xffff0000u);
           }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) *(uint2*)(dst + (size_t)j * ts) = make_uint2(v[k][0][j], v[k][1][j]);
         }
       }
     }
+  };
+  auto p_load = [&](int e0, u32x4 (&v)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = min(e0 + k * kThreads, npu - 1);
+      const int hl = min(e / nq, HS - 1), q = min(e % nq, (nt - 1) / 4);
+      v[k] = *(const u32x4*)(prow0 + (size_t)hl * nsp + 4 * q);
+    }
+  };
+  auto p_store = [&](int e0, const u32x4 (&v)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = e0 + k * kThreads;
+      if (e < npu) {
+        const int hl = e / nq, q = e % nq;
+        float x[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) x[m] = (hl < HS && 4 * q + m < nt) ? __uint_as_float(v[k][m]) : 0.f;
+        elem* dst = pA + (size_t)hl * ts + 4 * q;
+        if constexpr (T::HILO) {
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            hi[m] = f32_to_bf16_bits(x[m]);
+            lo[m] = f32_to_bf16_bits(x[m] - bf16_bits_to_f32(hi[m]));
+          }
+          *(uint2*)dst = make_uint2(hi[0] | hi[1] << 16, hi[2] | hi[3] << 16);
+          *(uint2*)(dst + (size_t)hs16 * ts) = make_uint2(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16);
+        } else {
+          *(u32x4*)dst = u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                               __float_as_uint(x[3])};
+        }
+      }
+    }
+  };
+  // merge weight of this chunk's split per head (tid < HS): e^{m_split - M} / L over all splits,
+  // from the split statistics held in registers (a loop over them beyond kStReg splits)
+  constexpr int kStReg = 8;
+  const float* st = pstat + ((size_t)b * H_q + h0 + min(tid, HS - 1)) * n_splits * 2;
+  float stm[kStReg], stl[kStReg], stmine = 0.f;
+  auto stats_load = [&]() {
+    if (tid < HS && n_splits <= kStReg) {
+#pragma unroll
+      for (int k = 0; k < kStReg; ++k) {
+        const int kk = min(k, n_splits - 1);
+        stm[k] = st[2 * kk];
+        stl[k] = st[2 * kk + 1];
+      }
+      stmine = st[2 * sp];
+    }
+  };
+  auto stats_weight = [&]() {
+    if (tid >= HS) return;
+    float M = -INFINITY, L = 0.f;
+    if (n_splits <= kStReg) {
+#pragma unroll
+      for (int k = 0; k < kStReg; ++k) M = k < n_splits ? fmaxf(M, stm[k]) : M;
+#pragma unroll
+      for (int k = 0; k < kStReg; ++k) L = k < n_splits ? L + stl[k] * expf(stm[k] - M) : L;
+      wsh[tid] = expf(stmine - M) / L;
+    } else {
+      for (int k = 0; k < n_splits; ++k) M = fmaxf(M, st[2 * k]);
+      for (int k = 0; k < n_splits; ++k) L += st[2 * k + 1] * expf(st[2 * k] - M);
+      wsh[tid] = expf(st[2 * sp] - M) / L;
+    }
+  };
+  if (nt > 0) {  // (nt = 0: no units, and the tiles below sum no window)
+    int32_t pp[4][2];
+    u32x4 pv[4], rv[4][2];
+    row_pos(tid, pp);
+    p_load(tid, pv);
+    row_load(tid, pp, rv);
+    stats_load();
+    // every first-batch load is issued before the first LDS write (the empty asm keeps the
+    // compiler from sinking the loads towards their uses)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    p_store(tid, pv);
+    for (int e0 = tid + 4 * kThreads; e0 < npu; e0 += 4 * kThreads) {
+      p_load(e0, pv);
+      __builtin_amdgcn_sched_barrier(0);
+      p_store(e0, pv);
+    }
+    stats_weight();
+    row_store(tid, rv);
+    for (int e0 = tid + 4 * kThreads; e0 < nru; e0 += 4 * kThreads) {
+      row_pos(e0, pp);
+      row_load(e0, pp, rv);
+      __builtin_amdgcn_sched_barrier(0);
+      row_store(e0, rv);
+    }
+  } else {
+    stats_load();
+    stats_weight();
   }
   __syncthreads();
 
