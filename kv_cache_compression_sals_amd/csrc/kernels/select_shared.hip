@@ -72,8 +72,8 @@ __device__ __forceinline__ void rope_sincos(int pos, double frev, float* s, floa
   *c = __builtin_amdgcn_cosf(r);
 }
 
-// grid: n_splits x (H_kv / 2) x B workgroups (XCD-aware order: the head pairs and splits of one
-// sequence, which read the same rows, share an XCD).
+// grid: n_splits x (H_kv / 2) x B workgroups (XCD-aware order: each XCD takes a block of
+// (sequence, split) pairs x head pairs, whose token rows and P_k rows it reads several times).
 template <int R, int NQH>
 __global__ __launch_bounds__(kNT) void shared_keys_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ Lk, const uint16_t* __restrict__ Pk,
@@ -89,8 +89,18 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
   const int n16 = lane & 15, q4 = lane >> 4;
   const int tg = wave >> 2, cg = wave & 3;  // token group, column group (RoPE pair of blocks)
   const int npairs = H_kv / kNH;
+  // logical order: groups of up to 8 head pairs, (sequence, split) pairs within a group, head
+  // pairs fastest; XCD-aware, so an XCD takes a block of a few (sequence, split) pairs x up to 8
+  // head pairs and its L2 serves both the token rows (shared by the head pairs) and the P_k rows
+  // (shared by the sequences and splits)
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int sp = wg % n_splits, hp = (wg / n_splits) % npairs, b = wg / (n_splits * npairs);
+  const int nbs = (int)(gridDim.x / npairs);  // (sequence, split) pairs
+  const int GH = npairs < 8 ? npairs : 8;
+  const int grp = wg / (GH * nbs);
+  const int gh = min(GH, npairs - grp * GH);  // head pairs of this group
+  const int within = wg - grp * GH * nbs;
+  const int hp = grp * GH + within % gh, bsp = within / gh;
+  const int sp = bsp % n_splits, b = bsp / n_splits;
   const int g0 = hp * kNH;
   const int s = (g0 * G) / H_kv;
   const int nqh = H_q / H_kv;
