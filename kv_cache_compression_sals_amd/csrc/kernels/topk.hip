@@ -714,7 +714,7 @@ __global__ __launch_bounds__(NT) void topk_window_kernel(const float* __restrict
 // order, with their keys, and writes its threshold key (the m-th largest) to taus. With m = kp
 // every element of the row's top kp is among its slice's top kp, with the lowest-index ties of the
 // row's threshold key included, so the row's selection over the candidates (in ascending position
-// order across slices) is exact. With m < kp (about twice a slice's expected share of the row's
+// order across slices) is exact. With m < kp (about 1.5 times a slice's expected share of the row's
 // top kp) the merge checks that this still holds.
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void topk_slice_kernel(const float* __restrict__ S,
@@ -765,7 +765,7 @@ int keys_per_thread(int n) { return n <= 4 * kThreads ? 4 : n <= 8 * kThreads ? 
 // Slices of a row of Tc candidates, rows rows: ns slices of *slen keys, each keeping its top *m
 // (0: the row is not split). Rows up to the register-resident limit are not split. Otherwise
 // (reduce, i.e. not in threshold mode) the row is cut into about one slice per CU over all rows,
-// each keeping twice its expected share of the top kp (plus 32), when that fits; else into the
+// each keeping 1.5 times its expected share of the top kp (plus 32), when that fits; else into the
 // fewest slices that fit, each keeping kp.
 int topk_slices(int rows, int Tc, int kp, bool reduce, int* slen, int* m) {
   if (Tc <= kLdsKeys || kp <= 0) return 0;
@@ -781,7 +781,7 @@ int topk_slices(int rows, int Tc, int kp, bool reduce, int* slen, int* m) {
     int ns = ceil_div(256, rows > 0 ? rows : 1);
     if (ns < ceil_div(Tc, kLdsKeys)) ns = ceil_div(Tc, kLdsKeys);
     if (ns > kMaxSlices) ns = kMaxSlices;
-    const int mm = (2 * ceil_div(kp, ns) + 32 + 31) / 32 * 32;
+    const int mm = (3 * ceil_div(kp, ns) / 2 + 32 + 31) / 32 * 32;
     if (mm < kp && (long)ns * mm <= kLdsKeys / 2 && fits(ns, mm, &len)) {
       if (slen) *slen = len;
       if (m) *m = mm;
