@@ -21,7 +21,9 @@ the launch stream at every stage boundary; the events give each stage's average 
 (stage_us), and the host clock around that pass gives eager_us_per_step. The attention stage
 (select_attend, the dominant kernel) is bounded by events that the runtime records at its
 kernel's own start and end, so its figure (the roofline's avg_launch_us) is the kernel's duration
-without the launch gap before it; the other stages include that gap. Each step is also followed,
+without the launch gap before it; the other stages include that gap. At ctx4k the two-head key
+tile kernel ranks the score rows itself (no top-k launch): there the topk_window stage is only the
+gap before that kernel, and the attention stage includes the ranking. Each step is also followed,
 outside the timed replay, by the dense baselines (comparators): flash-decode over the whole KV
 cache, and the full rebuild of the cache followed by it. One JSON line goes to stdout; progress
 goes to stderr.
@@ -76,13 +78,24 @@ def stages_of(cfg):
 
 def shared_value(cfg):
     return cfg.H_kv // cfg.G >= 4
+
+
+# rows of at most this many candidates are ranked inside the two-head key tile kernel (512
+# threads, 8 keys each) when it serves the layer: that kernel then also does the top-k stage
+RANK_IN_KEYS_MAX = 4096
+
+
+def ranks_in_keys(cfg, ctx):
+    return (shared_value(cfg) and cfg.dtype == "bf16" and cfg.d == 128 and (cfg.H_kv // cfg.G) % 2 == 0
+            and cfg.H_q // cfg.H_kv <= 4 and cfg.r in (128, 256, 384, 512)
+            and max(0, ctx - cfg.w) <= RANK_IN_KEYS_MAX)
 KDIR = os.path.join(ROOT, "kv_cache_compression_sals_amd", "csrc")
 # sources whose change invalidates a kernel's stored traffic counters
 KERNEL_SOURCES = {
     "select_attend": ["kernels/select_attend.inc", "kernels/select_attend_bf16_d128.hip",
-                      "kernels/select_shared.hip", "common.h"],
+                      "kernels/select_shared.hip", "topk_rows.h", "common.h"],
     "latent_score": ["kernels/latent_score.hip", "common.h"],
-    "topk_window": ["kernels/topk.hip", "common.h"],
+    "topk_window": ["kernels/topk.hip", "topk_rows.h", "common.h"],
     "latent_query": ["kernels/latent_query.hip", "common.h"],
     "combine": ["kernels/select_attend.hip", "common.h"],
     "value": ["kernels/value.hip", "common.h"],
@@ -162,6 +175,10 @@ def algorithmic(cfg, ctx):
         # attention up to the softmax, probabilities out; then the value kernels read them back
         probs = B * Hq * n_sel * 4
         stage_bytes["select_attend"] = half_rows + D * r * s + sel_idx + q_in + probs
+        if ranks_in_keys(cfg, ctx):
+            # the key tile kernel ranks the score rows itself: the top-k stage is its launch gap
+            stage_bytes["select_attend"] += scores
+            stage_bytes["topk_window"] = 0
         stage_bytes["value"] = half_rows + D * r * s + sel_idx + probs + o_out
         stage_flops["select_attend"] = k_rebuild + logits
         stage_flops["value"] = value_side

@@ -21,6 +21,7 @@
 // split, for the shared-selection value kernels, as in select_attend's shared-selection mode.
 #include "../common.h"
 #include "../launch.h"
+#include "../topk_rows.h"
 
 namespace sals {
 namespace {
@@ -38,6 +39,8 @@ constexpr int kAI = kTOK / 8;        // A (token rows) DMA instructions per chun
 constexpr int kAIW = (kAI + kWV - 1) / kWV;  // per wave, padded: 5
 constexpr int kBIW = kRows / 8 / kWV;        // B (P rows) per wave: 4
 constexpr int kMaxQH = 4;
+constexpr int kRankKPT = 8;          // keys per thread when the kernel ranks its own row
+constexpr int kRankMax = kNT * kRankKPT;  // longest row it ranks
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
@@ -53,6 +56,7 @@ constexpr int kOffRed = kOffQs + kNH * kMaxQH * kDH * 4;  // double ftab[kDH / 2
 constexpr int kLds = kOffRed + kDH / 2 * 8;
 static_assert(kLds <= 160 * 1024, "LDS");
 static_assert(4 * kNH * kMaxQH * kTOK * 4 <= kABytes, "partial logits reuse the first A buffer");
+static_assert(tk::topk_ext_words(kNT, kRankKPT) * 4 <= 2 * kABytes, "the row ranking uses the A buffers");
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -74,12 +78,16 @@ __device__ __forceinline__ void rope_sincos(int pos, double frev, float* s, floa
 
 // grid: n_splits x (H_kv / 2) x B workgroups (XCD-aware order: each XCD takes a block of
 // (sequence, split) pairs x head pairs, whose token rows and P_k rows it reads several times).
-template <int R, int NQH>
+// RANK: the selection is not given; every workgroup ranks its sequence's score row itself (the
+// top kp of Tc scores, ties to the lowest position, then the window [Tc, ctx)), with no other
+// workgroup to wait for, and the first workgroup of each (sequence, selection group) writes the
+// whole selection to sel for the value kernels and the caller.
+template <int R, int NQH, bool RANK>
 __global__ __launch_bounds__(kNT) void shared_keys_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ Lk, const uint16_t* __restrict__ Pk,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, float* __restrict__ pbuf,
+    int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, float* __restrict__ pbuf,
     float* __restrict__ pstat, int H_q, int H_kv, int G, int ctx_cap, int ctx, int n_sel, int n_splits,
-    double rope_r) {
+    double rope_r, const float* __restrict__ S, int ldS, int Tc, int kp) {
   constexpr int NKC = R / kKC;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   int32_t* pos = (int32_t*)(smem + kOffPos);
@@ -154,7 +162,9 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
   const int32_t* selrow = sel + ((size_t)b * G + s) * n_sel + j0;
   static_assert(kTOK <= kNT && kNH * kMaxQH * (kDH / 2) <= kNT, "one position and one query pair per thread");
   int pv = 0;
-  if (tid < kTOK) pv = selrow[min(tid, n_tok - 1)];
+  if constexpr (!RANK) {
+    if (tid < kTOK) pv = selrow[min(tid, n_tok - 1)];
+  }
   const int qi = lane, qhh = wave % nqh, qh2 = wave / nqh;  // this thread's query pair (i, i + d/2)
   const bool qlive = tid < kNH * nqh * (kDH / 2);
   float x1 = 0.f, x2 = 0.f;
@@ -175,6 +185,26 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
     }
     frq *= kInvTwoPi;
   }
+  if constexpr (RANK) {
+    // the first chunk's P_k rows do not depend on the selection: requested before the ranking,
+    // which stages its keys in the A buffers (free until the first token rows are copied)
+    issue_b(0, 0);
+    uint32_t* ext = (uint32_t*)(smem + kOffA);
+    const bool ranked = kp > 0 && kp < Tc;
+    if (ranked) {
+      const float* srow = S + ((size_t)b * G + s) * ldS;
+      const bool vec = (ldS & 3) == 0 && ((uintptr_t)S & 15) == 0;
+      tk::topk_rows<kNT, kRankKPT, false, true>(srow, nullptr, nullptr, Tc, kp, nullptr, nullptr, 0, 0, 0, vec,
+                                                false, 0u, nullptr, 0, nullptr, nullptr, 0, ext);
+    }
+    const int32_t* ranks = (const int32_t*)ext;  // ascending positions of the top kp
+    auto position = [&](int j) { return j < kp ? (ranked ? ranks[j] : j) : Tc + (j - kp); };
+    if (tid < kTOK) pv = position(j0 + min(tid, n_tok - 1));
+    if (sp == 0 && g0 * G == s * H_kv) {
+      int32_t* srow_out = sel + ((size_t)b * G + s) * n_sel;
+      for (int j = tid; j < n_sel; j += kNT) srow_out[j] = position(j);
+    }
+  }
   if (tid < kDH / 2) ftab[tid] = frq;
   if (tid < kTOK) pos[tid] = pv;
   if (qlive) {
@@ -185,8 +215,8 @@ __global__ __launch_bounds__(kNT) void shared_keys_kernel(
     dst[qi] = (x1 * cs - x2 * sn) * qscale;
     dst[qi + kDH / 2] = (x2 * cs + x1 * sn) * qscale;
   }
-  issue_b(0, 0);
-  lds_barrier();  // pos visible to every wave; the copies stay in flight
+  if constexpr (!RANK) issue_b(0, 0);
+  lds_barrier();  // pos visible to every wave, the ranking's LDS reads done; the copies stay in flight
   issue_a(0, 0);
 
   f32x4 acc[kTTW][4];
@@ -342,28 +372,41 @@ bool shared_keys_supported(int dtype, int H_q, int H_kv, int G, int d, int r) {
 
 int shared_keys_split() { return kTOK; }
 
-hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, const int32_t* sel,
+int shared_keys_rank_max() { return kRankMax; }
+
+hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, int32_t* sel,
                               const int32_t* cnt, float* pbuf, float* pstat, int B, int H_q, int H_kv, int G, int r,
                               int ctx_cap, int ctx, int n_sel, int n_splits, float rope_base,
-                              hipStream_t st, hipEvent_t t_start, hipEvent_t t_stop) {
+                              hipStream_t st, hipEvent_t t_start, hipEvent_t t_stop, const float* S,
+                              int ldS, int Tc, int kp) {
   const dim3 grid(n_splits * (H_kv / kNH) * B);
   const int nqh = H_q / H_kv;
   const double rope_r = pow((double)rope_base, -2.0 / kDH);  // theta_i = rope_r^i
   const auto* qq = (const uint16_t*)q;
   const auto* lk = (const uint16_t*)Lk;
   const auto* pk = (const uint16_t*)Pk;
-#define SALS_SK(RR, QQ)                                                                              \
-  if (t_start)                                                                                       \
-    hipExtLaunchKernelGGL(shared_keys_kernel<RR, QQ>, grid, dim3(kNT), 0, st, t_start, t_stop, 0, qq, lk, \
-                          pk, sel, cnt, pbuf, pstat, H_q, H_kv, G, ctx_cap, ctx, n_sel, n_splits, rope_r);  \
-  else                                                                                               \
-    shared_keys_kernel<RR, QQ><<<grid, kNT, 0, st>>>(qq, lk, pk, sel, cnt, pbuf, pstat, H_q, H_kv, G,       \
-                                                     ctx_cap, ctx, n_sel, n_splits, rope_r)
-#define SALS_SK_R(RR) \
-  if (nqh <= 1) {     \
-    SALS_SK(RR, 1);   \
-  } else {            \
-    SALS_SK(RR, 4);   \
+  const bool rank = S != nullptr;
+  if (rank && (cnt || Tc > kRankMax || Tc < 0 || kp < 0 || n_sel != min(kp, Tc) + (ctx - Tc)))
+    return hipErrorInvalidValue;
+#define SALS_SK(RR, QQ, RK)                                                                             \
+  if (t_start)                                                                                          \
+    hipExtLaunchKernelGGL(shared_keys_kernel<RR, QQ, RK>, grid, dim3(kNT), 0, st, t_start, t_stop, 0, qq, lk, \
+                          pk, sel, cnt, pbuf, pstat, H_q, H_kv, G, ctx_cap, ctx, n_sel, n_splits, rope_r, S,  \
+                          ldS, Tc, kp);                                                                 \
+  else                                                                                                  \
+    shared_keys_kernel<RR, QQ, RK><<<grid, kNT, 0, st>>>(qq, lk, pk, sel, cnt, pbuf, pstat, H_q, H_kv, G,     \
+                                                         ctx_cap, ctx, n_sel, n_splits, rope_r, S, ldS, Tc, kp)
+#define SALS_SK_Q(RR, QQ) \
+  if (rank) {             \
+    SALS_SK(RR, QQ, true); \
+  } else {                \
+    SALS_SK(RR, QQ, false); \
+  }
+#define SALS_SK_R(RR)  \
+  if (nqh <= 1) {      \
+    SALS_SK_Q(RR, 1);  \
+  } else {             \
+    SALS_SK_Q(RR, 4);  \
   }
   switch (r) {
     case 128: SALS_SK_R(128) break;
@@ -373,6 +416,7 @@ hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, con
     default: return hipErrorInvalidValue;
   }
 #undef SALS_SK_R
+#undef SALS_SK_Q
 #undef SALS_SK
   return hipGetLastError();
 }

@@ -64,12 +64,18 @@ hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const 
 // KV heads over one split of shared_keys_split() selected tokens per workgroup, then RoPE,
 // logits and the softmax over the split, written as pbuf / pstat (as select_attend's
 // shared-selection mode) for the value kernels below.
+// With S non-null (score rows of ldS floats, one per (sequence, selection group); Tc candidates,
+// kp = min(k, Tc); a fixed n_sel = kp + ctx - Tc, no cnt; Tc <= shared_keys_rank_max()) the kernel
+// also makes the selection: every workgroup ranks its own row (no top-k launch before it) and the
+// selection is written to sel, which is then an output.
 bool shared_keys_supported(int dtype, int H_q, int H_kv, int G, int d, int r);
 int shared_keys_split();
-hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, const int32_t* sel,
+int shared_keys_rank_max();
+hipError_t launch_shared_keys(const void* q, const void* Lk, const void* Pk, int32_t* sel,
                               const int32_t* cnt, float* pbuf, float* pstat, int B, int H_q, int H_kv, int G, int r,
                               int ctx_cap, int ctx, int n_sel, int n_splits, float rope_base,
-                              hipStream_t st, hipEvent_t t_start = nullptr, hipEvent_t t_stop = nullptr);
+                              hipStream_t st, hipEvent_t t_start = nullptr, hipEvent_t t_stop = nullptr,
+                              const float* S = nullptr, int ldS = 0, int Tc = 0, int kp = 0);
 
 // Full reconstruction of cache rows [t0, t0 + T) into a post-RoPE KV cache [B, H_kv,
 // stride_tokens, d] (bf16, d = 128, an even H_kv, r in {128, 256, 384, 512}); V (and Lv, Pv)

@@ -239,7 +239,10 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
     e = sals::launch_latent_score(s->dtype, qpart, p.npart, Lk, S, p.ldS, s->B, G, s->r, p.Tc,
                                   ctx_cap, hs);
   mark(2);
-  if (e == hipSuccess)
+  // with one selection shared by the key tile kernel's workgroups and rows short enough, each of
+  // them ranks its own row instead of waiting for a top-k launch
+  const bool rank_in_keys = p.skeys && !thr && p.Tc <= sals::shared_keys_rank_max();
+  if (e == hipSuccess && !rank_in_keys)
     e = sals::launch_topk_window(S, p.ldS, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel,
                                  (int32_t*)(w + p.off_cand), hs, thr, thr ? sals::threshold_key(tau) : 0u,
                                  cnt);
@@ -248,7 +251,8 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   hipEvent_t k0 = events ? (hipEvent_t)events[3] : nullptr, k1 = events ? (hipEvent_t)events[4] : nullptr;
   if (e == hipSuccess && p.skeys)
     e = sals::launch_shared_keys(q, Lk, Pk, selb, cnt, pbuf, pstat, s->B, s->H_q, s->H_kv, G, s->r,
-                                 ctx_cap, ctx, p.n_sel, p.n_splits, rope_base, hs, k0, k1);
+                                 ctx_cap, ctx, p.n_sel, p.n_splits, rope_base, hs, k0, k1,
+                                 rank_in_keys ? S : nullptr, p.ldS, p.Tc, p.kp);
   else if (e == hipSuccess)
     e = sals::launch_select_attend(s->dtype, q, Lk, Lv, Pk, Pv, selb, cnt, out, part, pbuf, pstat,
                                    s->B, s->H_q, s->H_kv, s->d, s->r, G, ctx_cap, ctx, p.n_sel,

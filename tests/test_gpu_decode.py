@@ -83,6 +83,27 @@ def test_edge_cases(name, ov, ctx, dtype):
     check(decode_case(base.with_(**ov), B=2, ctx=ctx, ctx_cap=ctx + 5))
 
 
+# the two-head key tile kernel ranking its own rows (bf16, d = 128, one selection for 4 KV heads):
+# the same edges, where the selection needs no ranking (k = 0, k + w >= ctx, w >= ctx) or has
+# massive ties (q = 0)
+KEY_TILE = C3.with_(H_q=8, H_kv=4, d=128, r=128, G=1, rank=64, calib_tokens=256)
+
+
+@pytest.mark.parametrize("name,ov,ctx", EDGES, ids=[e[0] for e in EDGES])
+def test_edge_cases_key_tile_ranking(name, ov, ctx):
+    check(decode_case(KEY_TILE.with_(**ov), B=2, ctx=ctx, ctx_cap=ctx + 5))
+
+
+@pytest.mark.parametrize("ctx", [250, 3000])
+def test_zero_query_key_tile_ranking(ctx):
+    case = decode_case(KEY_TILE.with_(k=20, w=6), B=2, ctx=ctx)
+    case["q"] = np.zeros_like(case["q"])
+    out, sel = run_gpu(case)
+    want = np.concatenate([np.arange(20), np.arange(ctx - 6, ctx)])
+    assert all(np.array_equal(sel[b, 0], want) for b in range(2))
+    decode_parity(case, out, sel)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_exact_ties_lowest_index(dtype):
     """Latent rows drawn from 4 prototypes: scores take 4 values with massive exact ties; the
