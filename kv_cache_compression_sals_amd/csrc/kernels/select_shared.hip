@@ -19,6 +19,12 @@
 // of each, and the four column groups are added in a fixed order. The softmax over the tile's
 // tokens (one split) ends the kernel: exp(logit - m) per query head and token, and (m, l) per
 // split, for the shared-selection value kernels, as in select_attend's shared-selection mode.
+//
+// For rows of at most 4096 candidates the kernel also makes the selection (SALS 关键设计 items 2
+// and 4): every workgroup ranks its own sequence's score row with the register-resident row
+// routine (topk_rows.h), its keys staged in the token buffers before their first use, while the
+// first chunk's P_k rows are already being copied. All workgroups of a sequence rank the same
+// row, so none waits for another and the top-k needs no launch of its own.
 #include "../common.h"
 #include "../launch.h"
 #include "../topk_rows.h"
