@@ -94,6 +94,14 @@ def test_edge_cases_key_tile_ranking(name, ov, ctx):
     check(decode_case(KEY_TILE.with_(**ov), B=2, ctx=ctx, ctx_cap=ctx + 5))
 
 
+@pytest.mark.parametrize("Tc", [4095, 4096, 4097])
+def test_key_tile_ranking_row_limit(Tc):
+    """Rows of up to 4096 candidates are ranked inside the key tile kernel, longer ones by the
+    top-k kernel; two selection groups of 4 KV heads, so two workgroups write selection rows."""
+    case = decode_case(KEY_TILE.with_(H_q=16, H_kv=8, G=2, k=700, w=20), B=1, ctx=Tc + 20)
+    check(case)
+
+
 @pytest.mark.parametrize("ctx", [250, 3000])
 def test_zero_query_key_tile_ranking(ctx):
     case = decode_case(KEY_TILE.with_(k=20, w=6), B=2, ctx=ctx)
