@@ -89,6 +89,8 @@ def ranks_in_keys(cfg, ctx):
     return (shared_value(cfg) and cfg.dtype == "bf16" and cfg.d == 128 and (cfg.H_kv // cfg.G) % 2 == 0
             and cfg.H_q // cfg.H_kv <= 4 and cfg.r in (128, 256, 384, 512)
             and max(0, ctx - cfg.w) <= RANK_IN_KEYS_MAX)
+
+
 KDIR = os.path.join(ROOT, "kv_cache_compression_sals_amd", "csrc")
 # sources whose change invalidates a kernel's stored traffic counters
 KERNEL_SOURCES = {
