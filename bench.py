@@ -23,7 +23,9 @@ the launch stream at every stage boundary; the events give each stage's average 
 kernel's own start and end, so its figure (the roofline's avg_launch_us) is the kernel's duration
 without the launch gap before it; the other stages include that gap. At ctx4k the two-head key
 tile kernel ranks the score rows itself (no top-k launch): there the topk_window stage is only the
-gap before that kernel, and the attention stage includes the ranking. Each step is also followed,
+gap before that kernel, and the attention stage includes the ranking; at 128K the top-k stage is
+the slice kernel alone and the attention stage includes the merge of the slices' candidates.
+Each step is also followed,
 outside the timed replay, by the dense baselines (comparators): flash-decode over the whole KV
 cache, and the full rebuild of the cache followed by it. One JSON line goes to stdout; progress
 goes to stderr.

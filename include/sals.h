@@ -201,7 +201,9 @@ sals_status sals_decode_step_noalloc(const sals_shape* s, const sals_select* sel
  *   events[5] after the last kernel. A stage that does not run for a shape leaves its two
  *   events back to back; when the rebuild kernel ranks the rows itself (one selection shared by
  *   at least 4 KV heads, bf16, d = 128, at most 4096 candidates, no threshold) the top-k stage
- *   is the gap before that kernel and the ranking falls in the rebuild stage.
+ *   is the gap before that kernel and the ranking falls in the rebuild stage; for rows past
+ *   32768 candidates (bf16, d = 128, no threshold) the top-k stage holds the slice kernel and the
+ *   merge of its candidates falls in the rebuild stage.
  * events: at least 6 hipEvent_t handles from hipEventCreate (owned by the caller);
  * SALS_ERR_NULL if events is NULL, SALS_ERR_RANGE if n_events < 6.
  */

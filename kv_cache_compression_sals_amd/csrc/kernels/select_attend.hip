@@ -15,15 +15,29 @@ int select_attend_max_split(int dtype, int d, int r, int nqh) {
   return 0;
 }
 
+bool select_attend_rank_fits(int dtype, int d, int r, int nqh, int split_len, int nc, int kp) {
+  return dtype == 1 && d == 128 && sa::bf16_d128_rank_fits(r, nqh, split_len, nc, kp);
+}
+
 hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const void* Lv,
                                 const void* Pk, const void* Pv, const int32_t* sel, const int32_t* cnt,
                                 float* out, float* part, float* pbuf, float* pstat, int B, int H_q,
                                 int H_kv, int d, int r, int G, int ctx_cap, int ctx, int n_sel,
                                 int split_len, int n_splits, float rope_base, hipStream_t st,
-                                hipEvent_t t_start, hipEvent_t t_stop) {
+                                hipEvent_t t_start, hipEvent_t t_stop, const int32_t* cand, int ns, int m,
+                                const float* S, int ldS, int Tc, int kp, int32_t* selw) {
+  sa::RankArgs rk{};
+  if (cand) {
+    if (cnt || !selw || !S || ns < 1 || m < 1 || kp < 1 || n_sel != kp + (ctx - Tc) ||
+        !select_attend_rank_fits(dtype, d, r, H_q / H_kv, split_len, ns * m, kp))
+      return hipErrorInvalidValue;
+    const size_t per = (size_t)B * G * ns * m;
+    rk = sa::RankArgs{cand, (const uint32_t*)(cand + per), (const uint32_t*)(cand + 2 * per), S, selw,
+                      ns, m, ldS, Tc, kp};
+  }
   const sa::SAArgs a{q,     Lk,   Lv, Pk,      Pv,  sel,   cnt,   out,       part,     pbuf,     pstat,
                      B,     H_q,  H_kv, G,     ctx_cap, ctx, n_sel, split_len, n_splits, rope_base,
-                     t_start, t_stop};
+                     t_start, t_stop, rk};
   bool ok = false;
   if (dtype == 1 && d == 128) ok = sa::bf16_d128_launch(r, a, st);
   else if (dtype == 1 && d == 64) ok = sa::bf16_d64_launch(r, a, st);

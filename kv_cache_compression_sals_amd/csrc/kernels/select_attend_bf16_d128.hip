@@ -25,5 +25,14 @@ int bf16_d128_max_split(int r, int nqh) {
 }
 #undef SALS_CASE
 
+#define SALS_CASE(RR) \
+  case RR:            \
+    return rank_fits_t<BF16, RR, 128>(nqh, split_len, nc, kp);
+bool bf16_d128_rank_fits(int r, int nqh, int split_len, int nc, int kp) {
+  switch (r) { SALS_CASE(32) SALS_CASE(64) SALS_CASE(128) SALS_CASE(256) SALS_CASE(384) SALS_CASE(512) }
+  return false;
+}
+#undef SALS_CASE
+
 }  // namespace sa
 }  // namespace sals

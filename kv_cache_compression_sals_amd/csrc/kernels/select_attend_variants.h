@@ -17,6 +17,7 @@ int bf16_d128_max_split(int r, int nqh);
 int bf16_d64_max_split(int r, int nqh);
 int f32_d128_max_split(int r, int nqh);
 int f32_d64_max_split(int r, int nqh);
+bool bf16_d128_rank_fits(int r, int nqh, int split_len, int nc, int kp);
 
 }  // namespace sa
 }  // namespace sals

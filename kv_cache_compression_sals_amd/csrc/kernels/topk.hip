@@ -396,6 +396,37 @@ size_t topk_candidate_bytes(int rows, int Tc, int kp) {
   return best;
 }
 
+int topk_rank_plan(int rows, int Tc, int kp, int* m) {
+  int slen = 0, mm = 0;
+  const int ns = topk_slices(rows, Tc, kp, true, &slen, &mm);
+  if (ns <= 0 || mm >= kp) return 0;
+  if (m) *m = mm;
+  return ns;
+}
+
+hipError_t launch_topk_slices(const float* S, int ldS, int rows, int Tc, int kp, int32_t* cand, hipStream_t st) {
+  int slen = 0, m = 0;
+  const int ns = rows > 0 ? topk_slices(rows, Tc, kp, true, &slen, &m) : 0;
+  if (ns <= 0 || m >= kp || !cand) return hipErrorInvalidValue;
+  const bool vec = (ldS & 3) == 0 && ((uintptr_t)S & 15) == 0;
+  uint32_t* ckeys = (uint32_t*)(cand + (size_t)rows * ns * m);
+  uint32_t* taus = ckeys + (size_t)rows * ns * m;
+  if (slen <= 4 * kShortThreads)
+    topk_slice_kernel<kShortThreads, 4><<<rows * ns, kShortThreads, 0, st>>>(S, cand, ckeys, taus, Tc, ldS, m, slen, ns, vec);
+  else if (slen <= 8 * kShortThreads)
+    topk_slice_kernel<kShortThreads, 8><<<rows * ns, kShortThreads, 0, st>>>(S, cand, ckeys, taus, Tc, ldS, m, slen, ns, vec);
+  else if (slen <= kShortRow)
+    topk_slice_kernel<kShortThreads, 16><<<rows * ns, kShortThreads, 0, st>>>(S, cand, ckeys, taus, Tc, ldS, m, slen, ns, vec);
+  else
+    switch (keys_per_thread(slen)) {
+      case 4: topk_slice_kernel<kThreads, 4><<<rows * ns, kThreads, 0, st>>>(S, cand, ckeys, taus, Tc, ldS, m, slen, ns, vec); break;
+      case 8: topk_slice_kernel<kThreads, 8><<<rows * ns, kThreads, 0, st>>>(S, cand, ckeys, taus, Tc, ldS, m, slen, ns, vec); break;
+      case 16: topk_slice_kernel<kThreads, 16><<<rows * ns, kThreads, 0, st>>>(S, cand, ckeys, taus, Tc, ldS, m, slen, ns, vec); break;
+      default: topk_slice_kernel<kThreads, 32><<<rows * ns, kThreads, 0, st>>>(S, cand, ckeys, taus, Tc, ldS, m, slen, ns, vec); break;
+    }
+  return hipGetLastError();
+}
+
 uint32_t threshold_key(float tau) {
   uint32_t u;
   const float z = tau == 0.0f ? 0.0f : tau;  // -0.0 ranks as +0.0

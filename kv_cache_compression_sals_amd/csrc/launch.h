@@ -42,6 +42,12 @@ hipError_t launch_topk_window(const float* S, int ldS, int32_t* sel, int rows, i
                               int ctx, int n_sel, int32_t* cand, hipStream_t st, bool thr = false,
                               uint32_t tkey = 0, int32_t* cnt = nullptr);
 uint32_t threshold_key(float tau);
+// The checked candidate plan of a long row (topk_slices with reduce, each slice keeping m < kp
+// candidates): ns slices, or 0 when the row is not split that way. launch_topk_slices runs only
+// its slice kernel (candidates, their keys and the slices' threshold keys to cand, laid out as in
+// launch_topk_window), for a consumer that ranks the candidates itself.
+int topk_rank_plan(int rows, int Tc, int kp, int* m);
+hipError_t launch_topk_slices(const float* S, int ldS, int rows, int Tc, int kp, int32_t* cand, hipStream_t st);
 
 // Gather + rebuild + RoPE + attention over the selected rows, split along the selected set.
 // With n_splits == 1 the normalised result goes to out; otherwise latent partials
@@ -57,7 +63,14 @@ hipError_t launch_select_attend(int dtype, const void* q, const void* Lk, const 
                                 float* out, float* part, float* pbuf, float* pstat, int B, int H_q,
                                 int H_kv, int d, int r, int G, int ctx_cap, int ctx, int n_sel,
                                 int split_len, int n_splits, float rope_base, hipStream_t st,
-                                hipEvent_t t_start = nullptr, hipEvent_t t_stop = nullptr);
+                                hipEvent_t t_start = nullptr, hipEvent_t t_stop = nullptr,
+                                const int32_t* cand = nullptr, int ns = 0, int m = 0, const float* S = nullptr,
+                                int ldS = 0, int Tc = 0, int kp = 0, int32_t* selw = nullptr);
+// With cand non-null the kernel also makes the selection from launch_topk_slices' candidates
+// (ns slices of m per row; the exact selection from the score rows S when they cannot decide it),
+// every workgroup for its own row, and writes it to selw; select_attend_rank_fits tells whether a
+// shape has that variant and room for it.
+bool select_attend_rank_fits(int dtype, int d, int r, int nqh, int split_len, int nc, int kp);
 
 // Key side when one selection serves several KV heads (bf16, d = 128, an even number of KV heads
 // per group, at most 4 query heads per KV head, r in {128, 256, 384, 512}): the K rebuild of two

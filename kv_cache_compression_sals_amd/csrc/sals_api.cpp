@@ -242,10 +242,18 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   // with one selection shared by the key tile kernel's workgroups and rows short enough, each of
   // them ranks its own row instead of waiting for a top-k launch
   const bool rank_in_keys = p.skeys && !thr && p.Tc <= sals::shared_keys_rank_max();
-  if (e == hipSuccess && !rank_in_keys)
-    e = sals::launch_topk_window(S, p.ldS, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel,
-                                 (int32_t*)(w + p.off_cand), hs, thr, thr ? sals::threshold_key(tau) : 0u,
-                                 cnt);
+  // rows long enough to be cut into checked slices: the slice kernel runs here and the attention
+  // kernel's workgroups merge their own row's candidates (no merge launch)
+  int rk_m = 0;
+  const int rk_ns = (!p.skeys && !thr && p.kp > 0 && p.kp < p.Tc) ? sals::topk_rank_plan(s->B * G, p.Tc, p.kp, &rk_m) : 0;
+  const bool rank_in_attend =
+      rk_ns > 0 && sals::select_attend_rank_fits(s->dtype, s->d, s->r, p.nqh, p.split_len, rk_ns * rk_m, p.kp);
+  int32_t* cand = (int32_t*)(w + p.off_cand);
+  if (e == hipSuccess && rank_in_attend)
+    e = sals::launch_topk_slices(S, p.ldS, s->B * G, p.Tc, p.kp, cand, hs);
+  else if (e == hipSuccess && !rank_in_keys)
+    e = sals::launch_topk_window(S, p.ldS, selb, s->B * G, p.Tc, p.kp, ctx, p.n_sel, cand, hs, thr,
+                                 thr ? sals::threshold_key(tau) : 0u, cnt);
   // the attention kernel's own start and end (recorded by the runtime around the kernel) bound
   // its stage, so that the traced time of the dominant kernel excludes the launch gap
   hipEvent_t k0 = events ? (hipEvent_t)events[3] : nullptr, k1 = events ? (hipEvent_t)events[4] : nullptr;
@@ -256,7 +264,9 @@ sals_status decode_impl(const sals_shape* s, const sals_select* sel, float rope_
   else if (e == hipSuccess)
     e = sals::launch_select_attend(s->dtype, q, Lk, Lv, Pk, Pv, selb, cnt, out, part, pbuf, pstat,
                                    s->B, s->H_q, s->H_kv, s->d, s->r, G, ctx_cap, ctx, p.n_sel,
-                                   p.split_len, p.n_splits, rope_base, hs, k0, k1);
+                                   p.split_len, p.n_splits, rope_base, hs, k0, k1,
+                                   rank_in_attend ? cand : nullptr, rk_ns, rk_m, S, p.ldS, p.Tc, p.kp,
+                                   selb);
   if (p.shared) {
     if (e == hipSuccess)
       e = sals::launch_value_sum(s->dtype, p.vp, pbuf, pstat, selb, cnt, Lv, zpart, s->B, s->H_q, G,

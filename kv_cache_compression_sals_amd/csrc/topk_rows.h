@@ -135,7 +135,6 @@ __device__ __forceinline__ bool topk_rows(const float* __restrict__ src, const i
   // 16-byte aligned; the selection is then left in LDS, below)
   uint32_t *stage, *hist, *scan, *bcast, *mm, *nsp, *tsel;
   if constexpr (EXT) {
-    static_assert(!GATHER, "external LDS: rows of scores only");
     stage = ext;
     hist = stage + kStage;
     scan = hist + kBins;
@@ -451,7 +450,8 @@ __device__ __forceinline__ bool topk_rows(const float* __restrict__ src, const i
     }
   }
   __syncthreads();
-  // EXT: the kp positions stay in LDS, ext[0 .. kp) in ascending order, for the caller
+  // EXT: the kp positions (row indices, or the candidates' positions) stay in LDS, ext[0 .. kp) in
+  // ascending order, for the caller
   if constexpr (EXT) return true;
   batched_copy<4>(kp, tid, NT, [&](int j) { return obuf[j]; }, [&](int j, int32_t i) {
     if constexpr (GATHER) {
@@ -462,6 +462,78 @@ __device__ __forceinline__ bool topk_rows(const float* __restrict__ src, const i
     }
   });
   return true;
+}
+
+// The exact top kp of a row of n scores read from global memory by NT threads, ties to the lowest
+// position: three key-bit digit passes (bits [31:21], [20:10], [9:0]) give the threshold key tau and
+// how many keys equal to it are taken, then an ordered compaction over the row writes the selected
+// positions to out[0 .. kp) (LDS) in ascending order. scratch: kBins + NT / 64 + 4 LDS words.
+// 0 < kp < n. For rows whose candidates could not decide the selection; every thread returns
+// after a barrier, with out complete.
+template <int NT>
+__device__ __forceinline__ void topk_row_digits(const float* __restrict__ src, int n, int kp, int32_t* out,
+                                                uint32_t* scratch) {
+  constexpr int NW = NT / 64, IPT = 16;
+  uint32_t* hist = scratch;
+  uint32_t* scan = hist + kBins;
+  uint32_t* bcast = scan + NW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  auto key_at = [&](int i) -> uint32_t { return float_key(src[i]); };
+  uint32_t prefix = 0, remaining = (uint32_t)kp;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+    const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
+    const uint32_t pmask = pass == 0 ? 0u : pass == 1 ? 0xffe00000u : 0xfffffc00u;
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    __syncthreads();
+    batched_copy<8>(n, tid, NT, key_at, [&](int, uint32_t k) {
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+    });
+    __syncthreads();
+    find_bin<NT>(hist, remaining, scan, bcast);
+    prefix |= bcast[0] << shift;
+    remaining -= bcast[1];
+    __syncthreads();
+  }
+  const uint32_t tau = prefix, take_eq = remaining;  // take_eq >= 1
+  // ordered compaction: wave w owns [base + w * 64 * IPT, + 64 * IPT) of each chunk, lane l the
+  // l-th key of each of its IPT runs of 64; ranks inside a run come from ballots, the waves' packed
+  // (gt, eq) counts (each at most NT * IPT) from a block prefix
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  uint32_t run_gt = 0, run_eq = 0;
+  for (int base = 0; base < n; base += NT * IPT) {
+    const int w0 = base + wave * 64 * IPT;
+    uint32_t kk[IPT];
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) kk[j] = key_at(min(w0 + j * 64 + lane, n - 1));
+    uint32_t wgt = 0, weq = 0;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const bool valid = w0 + j * 64 + lane < n;
+      wgt += (uint32_t)__popcll(__ballot(valid && kk[j] > tau));
+      weq += (uint32_t)__popcll(__ballot(valid && kk[j] == tau));
+    }
+    uint32_t before, total;
+    block_prefix<NT>(wgt | (weq << 16), scan, before, total);
+    uint32_t ngt = run_gt + (before & 0xffffu), neq = run_eq + (before >> 16);
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int i = w0 + j * 64 + lane;
+      const bool valid = i < n;
+      const bool gt = valid && kk[j] > tau, eq = valid && kk[j] == tau;
+      const unsigned long long mg = __ballot(gt), me = __ballot(eq);
+      const uint32_t bg = ngt + (uint32_t)__popcll(mg & lt_mask);  // gt keys before i
+      const uint32_t be = neq + (uint32_t)__popcll(me & lt_mask);  // eq keys before i
+      if (gt) out[bg + min(be, take_eq)] = i;
+      else if (eq && be < take_eq) out[bg + be] = i;
+      ngt += (uint32_t)__popcll(mg);
+      neq += (uint32_t)__popcll(me);
+    }
+    run_gt += total & 0xffffu;
+    run_eq += total >> 16;
+  }
+  __syncthreads();
 }
 
 }  // namespace tk

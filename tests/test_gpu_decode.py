@@ -102,6 +102,41 @@ def test_key_tile_ranking_row_limit(Tc):
     check(case)
 
 
+def _bf16_bits(x):
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kind", ["gaussian", "hot_region", "two_values"])
+def test_long_row_ranked_in_attention_kernel(kind):
+    """Rows past 32768 candidates with bf16 d = 128: the slice kernel keeps each slice's share and
+    the attention kernel's workgroups merge their own row; with a hot region the slices' share
+    cannot decide the selection and the exact digit selection over the scores takes over. The
+    scores are planted: q = e_0 and P_k = I make S[t] = L_k[t][0] (bf16, so many exact ties)."""
+    T, k, w = 40032, 3000, 32
+    case = decode_case(C3.with_(H_q=1, H_kv=1, d=128, r=128, G=1, k=k, w=w, rank=64, calib_tokens=256), B=1,
+                       ctx=T)
+    rs = np.random.default_rng(11)
+    sc = rs.standard_normal(T - w).astype(np.float32)
+    if kind == "hot_region":
+        sc[T // 3: T // 3 + 4000] += 4.0
+    if kind == "two_values":
+        sc = np.where(rs.random(T - w) < 0.05, 2.0, 1.0).astype(np.float32)
+    case["Lk"][0, : T - w, 0] = _bf16_bits(sc)
+    case["Pk"] = _bf16_bits(np.eye(128, 128, dtype=np.float32))
+    q = np.zeros((1, 1, 128), dtype=np.float32)
+    q[0, 0, 0] = 1.0
+    case["q"] = _bf16_bits(q)
+    print(f"long row ranked in the attention kernel: {kind} T={T} k={k} w={w}", flush=True)
+    out, sel = run_gpu(case)
+    scores = np.asarray(case["Lk"][0, : T - w, 0], dtype=np.uint32) << 16
+    scores = scores.view(np.float32).astype(np.float64)
+    order = np.lexsort((np.arange(T - w), -scores))  # score desc, index asc
+    want = np.concatenate([np.sort(order[:k]), np.arange(T - w, T)])
+    assert np.array_equal(sel[0, 0], want)
+    decode_parity(case, out, sel)
+
+
 @pytest.mark.parametrize("ctx", [250, 3000])
 def test_zero_query_key_tile_ranking(ctx):
     case = decode_case(KEY_TILE.with_(k=20, w=6), B=2, ctx=ctx)
