@@ -47,7 +47,6 @@ constexpr int kBIW = kRows / 8 / kWV;        // B (P rows) per wave: 4
 constexpr int kMaxQH = 4;
 constexpr int kRankKPT = 8;          // keys per thread when the kernel ranks its own row
 constexpr int kRankMax = kNT * kRankKPT;  // longest row it ranks
-constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
 // LDS layout (bytes)
